@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark: query x candidate distance pairs per second on one MI355X.
+
+Default workload: the dense best-matching-unit search of a 128x128 SOM map --
+65,536 queries N(0,1) x 16,384 neurons N(0, 0.5), d = 256, squared-L2
+argmin -- with inputs resident in HBM.  One step = one vs_bmu_search call:
+candidate (and query) norms, the fused MFMA scan with its arg-reduction and
+merge, and the finalize kernel.
+
+Output: one JSON line (rank 0) with the throughput, the roofline of the
+dominant kernel (its algorithmic FLOPs per launch over its average launch
+time, taken with HIP events on the launch stream by the library's timing
+hook) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
+same workload on the host's cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+                    [--no-cpu-baseline] [--traffic-json FILE]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query×candidate distance pairs/sec (BMU search) + % of fp32 MFMA/HBM roof"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def load_traffic(path, kernel, workload):
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t.get(f"{workload}:{kernel}")
+        if e and e.get("kernel_source_hash") == kernel_source_hash():
+            return e.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "farthest_vector_search_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ workloads --
+
+def setup(k, torch, vs):
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.workload(k)
+    if w["kind"] == "dense":
+        Q = torch.from_numpy(w["Q"]).to(dev)
+        C = torch.from_numpy(w["C"]).to(dev)
+        idx = torch.empty(w["nq"], dtype=torch.int32, device=dev)
+        score = torch.empty(w["nq"], dtype=torch.float32, device=dev)
+        ws = torch.empty(vs.lib().vs_bmu_search_workspace(w["nq"], w["nc"], w["d"], 0),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            vs.vs_bmu_search(Q, C, 0, idx_out=idx, score_out=score, workspace=ws)
+        pairs = w["nq"] * w["nc"]
+        flops = 2.0 * w["d"] * pairs
+        cfg = dict(workload=w["name"], nq=w["nq"], nc=w["nc"], d=w["d"], metric="l2sq_min")
+        return w, step, pairs, flops, 1, cfg
+    if w["kind"] == "diversity":
+        n, d, nseq, steps = w["n"], w["d"], w["nseq"], w["steps"]
+        C = torch.from_numpy(w["C"]).to(dev)
+        seeds = torch.from_numpy(w["seeds"]).to(dev)
+        W = (n + 31) // 32
+        m0 = np.zeros((nseq, W), np.uint32)
+        m0[np.arange(nseq), w["seeds"] // 32] |= (np.uint32(1) << (w["seeds"] % 32).astype(np.uint32))
+        mask0 = torch.from_numpy(m0.view(np.int32)).to(dev)
+        mask = mask0.clone()
+        picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+        ws = torch.empty(vs.lib().vs_diversity_step_workspace(n, d, nseq), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            mask.copy_(mask0)
+            last = seeds
+            for t in range(steps):
+                vs.vs_diversity_step(C, last, mask, idx_out=picks[t], workspace=ws,
+                                     want_score=False)
+                last = picks[t]
+        pairs = nseq * n * steps
+        flops = 2.0 * d * pairs
+        cfg = dict(workload=w["name"], n=n, d=d, nseq=nseq, steps_per_run=steps,
+                   metric="cos_min_masked")
+        return w, step, pairs, flops, steps, cfg
+    # sparse
+    indptr = torch.from_numpy(w["indptr"]).to(dev)
+    indices = torch.from_numpy(w["indices"]).to(dev)
+    values = torch.from_numpy(w["values"]).to(dev)
+    CT = torch.from_numpy(w["CT"]).to(dev)
+    nq, nc = w["nq"], w["nc"]
+    idx = torch.empty(nq, dtype=torch.int32, device=dev)
+    score = torch.empty(nq, dtype=torch.float32, device=dev)
+    ws = torch.empty(vs.lib().vs_bmu_search_csr_workspace(nq, nc, w["d"], 0), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        vs.vs_bmu_search_csr(indptr, indices, values, CT, 0, idx_out=idx, score_out=score,
+                             workspace=ws)
+    pairs = nq * nc
+    w["nnz"] = int(w["indices"].shape[0])
+    flops = 2.0 * w["nnz"] * nc
+    cfg = dict(workload=w["name"], nq=nq, nc=nc, d=w["d"], nnz=w["nnz"], metric="l2sq_min")
+    return w, step, pairs, flops, 1, cfg
+
+
+# ------------------------------------------------------------ cpu leg --
+
+def cpu_baseline(k, w, target_s):
+    """Oracle (fp64, plain loops, untuned) on a bounded sample, all host
+    threads, each running the single-threaded scan on its own shard."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    if w["kind"] == "dense":
+        nc = w["nc"]
+        t0 = time.perf_counter()
+        oracle.dense(w["Q"][:4], w["C"], 0, threads=1)
+        per_q = (time.perf_counter() - t0) / 4
+        nsample = int(max(threads, min(w["nq"], target_s * threads / max(per_q, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.dense(w["Q"][:nsample], w["C"], 0, threads=threads)
+        dt = time.perf_counter() - t0
+        return dict(value=nsample * nc / dt, unit="pairs/s", cores=threads, kind="oracle",
+                    sample=f"first {nsample} of {w['nq']} queries x all {nc} candidates",
+                    seconds=round(dt, 2))
+    if w["kind"] == "diversity":
+        n = w["n"]
+        # one diversity step straight from the rows (no Gram cache): a sample
+        # of sequences, each scanning all n rows against its reference
+        t0 = time.perf_counter()
+        oracle.div_run(w["C"], w["seeds"][:2], 1)
+        per_seq = (time.perf_counter() - t0) / 2
+        nsample = int(max(threads, min(w["nseq"], target_s * threads / max(per_seq, 1e-9))))
+        seeds = w["seeds"][:nsample]
+        from concurrent.futures import ThreadPoolExecutor
+        parts = np.array_split(seeds, threads)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda s: oracle.div_run(w["C"], s, 1), [p for p in parts if len(p)]))
+        dt = time.perf_counter() - t0
+        return dict(value=nsample * n / dt, unit="pairs/s", cores=threads, kind="oracle",
+                    sample=f"one step of {nsample} of {w['nseq']} sequences x all {n} rows",
+                    seconds=round(dt, 2))
+    # sparse
+    ptr = w["indptr"]
+    col_sq = oracle.sqnorms(w["CT"], feature_major=True, threads=threads)
+    t0 = time.perf_counter()
+    oracle.csr(ptr[:3], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq, threads=1)
+    per_q = (time.perf_counter() - t0) / 2
+    nsample = int(max(threads, min(w["nq"], target_s * threads / max(per_q, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.csr(ptr[:nsample + 1], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq,
+               threads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=nsample * w["nc"] / dt, unit="pairs/s", cores=threads, kind="oracle",
+                sample=f"first {nsample} of {w['nq']} CSR rows x all {w['nc']} neurons",
+                seconds=round(dt, 2))
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import farthest_vector_search_amd as vs
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"workload {a.workload}: generating inputs")
+    w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs)
+    torch.cuda.synchronize()
+    log(f"warmup {a.warmup} steps")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {a.steps} steps")
+    with vs.KernelTimer(max_launches=a.steps * launches_per_step + 8) as kt:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / a.steps
+    value = pairs * a.steps / dt
+    kernel_ms = kt.ms / max(kt.launches, 1)
+    flops_per_launch = flops / launches_per_step
+    roof = None
+    if w["kind"] in ("dense", "diversity"):
+        achieved = flops_per_launch / (kernel_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4))
+    else:
+        # sparse: algorithmic codebook bytes (4 B per non-zero x neuron) per
+        # launch against the HBM peak; the measured on-chip roof is reported
+        # separately in the design doc
+        bytes_per_launch = 4.0 * w["nnz"] * w["nc"]
+        achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    roof["kernel"] = kt.name
+    roof["kernel_ms"] = round(kernel_ms, 5)
+    roof["traffic"] = load_traffic(a.traffic_json, kt.name, cfg["workload"])
+    out = {
+        "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": cfg, "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(a.workload, w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+"""Python binding of libvs (masked arg-reduction scans on MI355X / gfx950).
+
+Argument marshalling only: every step of every search runs in the HIP
+kernels of ``libvs.so``, called through its C ABI (``include/vs.h``) on the
+current torch stream.  PyTorch supplies device memory and streams.  There is
+no CPU fallback: if the library is missing or no gfx950 GPU is present the
+calls raise.
+
+Functions (same names as the C entry points):
+    vs_bmu_search(Q, C, metric)                        -> (idx, score)
+    vs_bmu_search_csr(indptr, indices, values, CT, metric) -> (idx, score)
+    vs_diversity_step(C, last_pick, mask_bits)         -> (idx, score)
+    vs_candidate_norms(C, feature_major=False)         -> norms
+    vs_tile_rows(cache_bytes, d, bytes_per_value)      -> int (host only)
+Metrics: VS_L2SQ_MIN, VS_L2SQ_MAX, VS_COS_MAX, VS_COS_MIN.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvs.so")
+
+VS_L2SQ_MIN, VS_L2SQ_MAX, VS_COS_MAX, VS_COS_MIN = 0, 1, 2, 3
+METRICS = {"l2sq_min": 0, "l2sq_max": 1, "cos_max": 2, "cos_min": 3}
+
+STATUS = {0: "VS_OK", 1: "VS_ERR_NULL", 2: "VS_ERR_SHAPE", 3: "VS_ERR_METRIC",
+          4: "VS_ERR_WORKSPACE", 5: "VS_ERR_ALIGN", 6: "VS_ERR_INDEX",
+          7: "VS_ERR_UNSUPPORTED", 8: "VS_ERR_HIP"}
+
+EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_csr_workspace",
+           "vs_bmu_search_csr", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
+           "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
+
+
+class VsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == 8 and _lib is not None:
+            msg += f" (hip error {_lib.vs_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m farthest_vector_search_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.vs_bmu_search_workspace.argtypes = [I64, I64, I32, I32]
+    L.vs_bmu_search_workspace.restype = SZ
+    L.vs_bmu_search.argtypes = [P, P, I64, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_bmu_search_csr_workspace.argtypes = [I64, I64, I32, I32]
+    L.vs_bmu_search_csr_workspace.restype = SZ
+    L.vs_bmu_search_csr.argtypes = [P, P, P, I64, I64, P, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
+    L.vs_diversity_step_workspace.restype = SZ
+    L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
+    L.vs_candidate_norms.argtypes = [P, I64, I32, I32, P, P]
+    L.vs_tile_rows.argtypes = [I64, I32, I32]
+    L.vs_tile_rows.restype = I64
+    L.vs_timing_enable.argtypes = [I32]
+    L.vs_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
+    L.vs_timing_kernel_name.restype = ctypes.c_char_p
+    L.vs_status_str.argtypes = [ctypes.c_int]
+    L.vs_status_str.restype = ctypes.c_char_p
+    L.vs_version.restype = ctypes.c_char_p
+    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_diversity_step",
+                 "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
+                 "vs_last_hip_error"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- helpers --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _metric(m) -> int:
+    return METRICS[m] if isinstance(m, str) else int(m)
+
+
+def _dev(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise VsError(rc, where)
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    return workspace
+
+
+# ------------------------------------------------------------ entry points --
+
+def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, workspace=None,
+                  want_score: bool = True):
+    """Best candidate row of C for every row of Q (see include/vs.h)."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(Q, "Q", torch.float32, 2)
+    _dev(C, "C", torch.float32, 2)
+    nq, d = Q.shape
+    nc = C.shape[0]
+    if C.shape[1] != d:
+        raise ValueError("Q and C must have the same number of columns")
+    dev = Q.device
+    if idx_out is None:
+        idx_out = torch.empty(nq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nq, dtype=torch.float32, device=dev)
+    need = L.vs_bmu_search_workspace(nq, nc, d, m)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out), _ptr(score_out),
+                             _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_bmu_search")
+    return idx_out, score_out
+
+
+def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=None,
+                      score_out=None, workspace=None, want_score: bool = True):
+    """Best codebook column of CT (d x nc, feature-major) for every CSR row."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(indptr, "indptr", torch.int32, 1)
+    _dev(indices, "indices", torch.int32, 1)
+    _dev(values, "values", torch.float32, 1)
+    _dev(CT, "CT", torch.float32, 2)
+    nq = indptr.numel() - 1
+    nnz = indices.numel()
+    if values.numel() != nnz:
+        raise ValueError("indices and values differ in length")
+    d, nc = CT.shape
+    dev = CT.device
+    if idx_out is None:
+        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search_csr(_ptr(indptr), _ptr(indices) if nnz else None,
+                                 _ptr(values) if nnz else None, nq, nnz, _ptr(CT), nc, d, m,
+                                 _ptr(idx_out), _ptr(score_out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_bmu_search_csr")
+    return idx_out, score_out
+
+
+def vs_diversity_step(C, last_pick, mask_bits, idx_out=None, score_out=None, workspace=None,
+                      want_score: bool = True):
+    """One greedy diversity step for every sequence; updates mask_bits in place."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    _dev(last_pick, "last_pick", torch.int32, 1)
+    n, d = C.shape
+    nseq = last_pick.numel()
+    W = (n + 31) // 32
+    if mask_bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask_bits must be int32 or uint32 words")
+    _dev(mask_bits, "mask_bits", mask_bits.dtype, 2)
+    if tuple(mask_bits.shape) != (nseq, W):
+        raise ValueError(f"mask_bits must be [{nseq}, {W}]")
+    dev = C.device
+    if idx_out is None:
+        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    need = L.vs_diversity_step_workspace(n, d, nseq)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_step(_ptr(C), n, d, _ptr(last_pick), _ptr(mask_bits), nseq,
+                                 _ptr(idx_out), _ptr(score_out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_diversity_step")
+    return idx_out, score_out
+
+
+def vs_candidate_norms(C, feature_major: bool = False, out=None):
+    """Squared L2 norms (float32) of the rows of C, or of its columns."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    if feature_major:
+        d, nc = C.shape
+    else:
+        nc, d = C.shape
+    if out is None:
+        out = torch.empty(nc, dtype=torch.float32, device=C.device)
+    with torch.cuda.device(C.device):
+        rc = L.vs_candidate_norms(_ptr(C), nc, d, int(bool(feature_major)), _ptr(out),
+                                  _stream(C.device))
+    _check(rc, "vs_candidate_norms")
+    return out
+
+
+def vs_tile_rows(cache_bytes: int, d: int, bytes_per_value: int = 4) -> int:
+    return int(lib().vs_tile_rows(cache_bytes, d, bytes_per_value))
+
+
+def mask_words(n: int) -> int:
+    return (n + 31) // 32
+
+
+class KernelTimer:
+    """Sum of the dominant kernel's durations (HIP events on the call's stream)."""
+
+    def __init__(self, max_launches: int = 4096):
+        self.max = max_launches
+        self.ms = None
+        self.launches = None
+
+    def __enter__(self):
+        _check(lib().vs_timing_enable(self.max), "vs_timing_enable")
+        return self
+
+    def __exit__(self, *exc):
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        _check(lib().vs_timing_read(ctypes.byref(ms), ctypes.byref(n)), "vs_timing_read")
+        self.ms, self.launches = ms.value, n.value
+        self.name = lib().vs_timing_kernel_name().decode()
+        return False

@@ -1,0 +1,341 @@
+// api.hip -- the C ABI of libvs (declared in include/vs.h).
+//
+// Host side only: argument checks (before anything is enqueued), workspace
+// layout, the per-device architecture check and the kernel sequence of each
+// entry point on the caller's stream.  The library allocates no device
+// memory: every buffer is the caller's.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "vs.h"
+#include "vs_internal.h"
+
+#define VS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+int g_last_hip = 0;
+
+struct DevInfo {
+    bool probed = false, ok = false;
+    int n_cu = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+int device_ready(int *n_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip = (int)e;
+        return VS_ERR_HIP;
+    }
+    if (dev < 0 || dev >= 64) return VS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo &di = g_dev[dev];
+    if (!di.probed) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess) {
+            g_last_hip = (int)e;
+            return VS_ERR_HIP;
+        }
+        di.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        di.n_cu = p.multiProcessorCount;
+        di.probed = true;
+    }
+    if (!di.ok) return VS_ERR_UNSUPPORTED;
+    *n_cu = di.n_cu;
+    return VS_OK;
+}
+
+inline size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+inline bool al256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+constexpr int64_t kMaxIndex = 2147483647;  // indices are int32
+constexpr int32_t kMaxDim = 1 << 20;
+
+// Workspace of the dense and CSR searches: keys[nq] u64 | qn[nq] f32 | cn[nc] f32.
+struct Layout {
+    size_t keys = 0, qn = 0, cn = 0, total = 0;
+};
+Layout search_layout(int64_t nq, int64_t nc, int32_t metric) {
+    Layout L;
+    L.keys = 0;
+    L.total = up256((size_t)nq * 8);
+    if (vs::metric_is_l2(metric)) {
+        L.qn = L.total;
+        L.total += up256((size_t)nq * 4);
+        L.cn = L.total;
+        L.total += up256((size_t)nc * 4);
+    }
+    return L;
+}
+
+#define VS_TRY_HIP(expr)                   \
+    do {                                   \
+        const hipError_t e_ = (expr);      \
+        if (e_ != hipSuccess) {            \
+            g_last_hip = (int)e_;          \
+            return VS_ERR_HIP;             \
+        }                                  \
+    } while (0)
+
+// ---- timing hook -------------------------------------------------------
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    int max = 0, count = 0;
+    std::vector<hipEvent_t> start, stop;
+    const char *name = "";
+} g_timing;
+
+}  // namespace
+
+namespace vs {
+
+void timing_before(hipStream_t st, const char *name) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on || g_timing.count >= g_timing.max) return;
+    g_timing.name = name;
+    (void)hipEventRecord(g_timing.start[g_timing.count], st);
+}
+
+void timing_after(hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on || g_timing.count >= g_timing.max) return;
+    (void)hipEventRecord(g_timing.stop[g_timing.count], st);
+    ++g_timing.count;
+}
+
+}  // namespace vs
+
+VS_API int vs_timing_enable(int32_t max_launches) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.on = false;
+    g_timing.count = 0;
+    if (max_launches <= 0) return VS_OK;
+    while ((int)g_timing.start.size() < max_launches) {
+        hipEvent_t a, b;
+        VS_TRY_HIP(hipEventCreate(&a));
+        VS_TRY_HIP(hipEventCreate(&b));
+        g_timing.start.push_back(a);
+        g_timing.stop.push_back(b);
+    }
+    g_timing.max = max_launches;
+    g_timing.on = true;
+    return VS_OK;
+}
+
+VS_API int vs_timing_read(double *total_ms, int64_t *launches) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double sum = 0.0;
+    for (int i = 0; i < g_timing.count; ++i) {
+        VS_TRY_HIP(hipEventSynchronize(g_timing.stop[i]));
+        float ms = 0.0f;
+        VS_TRY_HIP(hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]));
+        sum += ms;
+    }
+    if (total_ms) *total_ms = sum;
+    if (launches) *launches = g_timing.count;
+    g_timing.on = false;
+    g_timing.count = 0;
+    return VS_OK;
+}
+
+VS_API const char *vs_timing_kernel_name(void) { return g_timing.name; }
+
+// ---- dense search --------------------------------------------------------
+
+VS_API size_t vs_bmu_search_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric) {
+    (void)d;
+    if (nq < 0 || nc < 0 || metric < 0 || metric > 3) return 0;
+    return search_layout(nq, nc, metric).total;
+}
+
+VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                         int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (nq < 0 || nq > kMaxIndex || nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxDim)
+        return VS_ERR_SHAPE;
+    if (nq == 0) return VS_OK;
+    if (!Q || !C || !idx_out || !workspace) return VS_ERR_NULL;
+    if (!al4(Q) || !al4(C) || !al4(idx_out) || !al4(score_out) || !al256(workspace))
+        return VS_ERR_ALIGN;
+    const Layout L = search_layout(nq, nc, metric);
+    if (workspace_bytes < L.total) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(ws + L.keys);
+    float *qn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.qn) : nullptr;
+    float *cn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.cn) : nullptr;
+
+    VS_TRY_HIP(vs::launch_fill_keys(keys, nq, st));
+    if (cn) VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, cn, st));
+    if (qn && score_out) VS_TRY_HIP(vs::launch_row_sqnorms(Q, nq, d, qn, st));
+
+    vs::DenseArgs a{};
+    a.Q = Q;
+    a.C = C;
+    a.cn = cn;
+    a.keys = keys;
+    a.nq = nq;
+    a.nc = nc;
+    a.d = d;
+    VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu));
+    VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
+    return VS_OK;
+}
+
+// ---- sparse-query search ---------------------------------------------------
+
+VS_API size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric) {
+    (void)d;
+    if (nq < 0 || nc < 0 || metric < 0 || metric > 3) return 0;
+    Layout L;
+    L.total = up256((size_t)nq * 8);
+    L.total += up256((size_t)nq * 4);  // query norms (also used by the cosine metrics)
+    L.total += up256((size_t)nc * 4);
+    return L.total;
+}
+
+VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                             int64_t nq, int64_t nnz, const float *CT, int64_t nc, int32_t d,
+                             int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (nq < 0 || nq > kMaxIndex || nnz < 0 || nnz > kMaxIndex || nc < 1 || nc > kMaxIndex ||
+        d < 1 || d > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nq == 0) return VS_OK;
+    if (!indptr || !CT || !idx_out || !workspace || (nnz > 0 && (!indices || !values)))
+        return VS_ERR_NULL;
+    if (!al4(indptr) || !al4(indices) || !al4(values) || !al4(CT) || !al4(idx_out) ||
+        !al4(score_out) || !al256(workspace))
+        return VS_ERR_ALIGN;
+    const size_t need = vs_bmu_search_csr_workspace(nq, nc, d, metric);
+    if (workspace_bytes < need) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(ws);
+    float *qn = reinterpret_cast<float *>(ws + up256((size_t)nq * 8));
+    float *cn = reinterpret_cast<float *>(ws + up256((size_t)nq * 8) + up256((size_t)nq * 4));
+
+    VS_TRY_HIP(vs::launch_fill_keys(keys, nq, st));
+    if (vs::metric_is_l2(metric)) VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, d, cn, st));
+    if (vs::metric_is_l2(metric) && score_out)
+        VS_TRY_HIP(vs::launch_csr_row_sqnorms(indptr, values, nq, nnz, qn, st));
+
+    vs::CsrArgs a{};
+    a.indptr = indptr;
+    a.indices = indices;
+    a.values = values;
+    a.CT = CT;
+    a.cn = cn;
+    a.keys = keys;
+    a.nq = nq;
+    a.nnz = nnz;
+    a.nc = nc;
+    a.d = d;
+    VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu));
+    VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
+    return VS_OK;
+}
+
+// ---- diversity step ------------------------------------------------------
+
+VS_API size_t vs_diversity_step_workspace(int64_t n, int32_t d, int64_t nseq) {
+    (void)n;
+    (void)d;
+    if (nseq < 0) return 0;
+    return up256((size_t)nseq * 8);
+}
+
+VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_pick,
+                             uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
+                             float *score_out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || d > kMaxDim || nseq < 0 || nseq > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nseq == 0) return VS_OK;
+    if (!C || !last_pick || !mask_bits || !idx_out || !workspace) return VS_ERR_NULL;
+    if (!al4(C) || !al4(last_pick) || !al4(mask_bits) || !al4(idx_out) || !al4(score_out) ||
+        !al256(workspace))
+        return VS_ERR_ALIGN;
+    if (workspace_bytes < vs_diversity_step_workspace(n, d, nseq)) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    uint64_t *keys = static_cast<uint64_t *>(workspace);
+    const int64_t W = (n + 31) / 32;
+    VS_TRY_HIP(vs::launch_fill_keys(keys, nseq, st));
+    vs::DenseArgs a{};
+    a.C = C;
+    a.pick = last_pick;
+    a.mask = mask_bits;
+    a.keys = keys;
+    a.nq = nseq;
+    a.nc = n;
+    a.d = d;
+    a.mask_words = W;
+    VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, true, st, n_cu));
+    VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
+    return VS_OK;
+}
+
+// ---- norms, tile rule, status ---------------------------------------------
+
+VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t feature_major,
+                              float *norms_out, void *stream) {
+    if (nc < 0 || nc > kMaxIndex || d < 1 || d > kMaxIndex) return VS_ERR_SHAPE;
+    if (nc == 0) return VS_OK;
+    if (!C || !norms_out) return VS_ERR_NULL;
+    if (!al4(C) || !al4(norms_out)) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (feature_major) VS_TRY_HIP(vs::launch_col_sqnorms(C, nc, d, norms_out, st));
+    else VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, norms_out, st));
+    return VS_OK;
+}
+
+VS_API int64_t vs_tile_rows(int64_t cache_bytes, int32_t d, int32_t bytes_per_value) {
+    if (cache_bytes <= 0 || d < 1 || bytes_per_value < 1) return 0;
+    // floor(cache * 0.85 / (d * b)) in exact integer arithmetic: 0.85 = 17/20
+    const __int128 num = (__int128)cache_bytes * 17;
+    const __int128 den = (__int128)20 * d * bytes_per_value;
+    const int64_t rows = (int64_t)(num / den);
+    return rows > 0 ? rows : 1;
+}
+
+VS_API const char *vs_status_str(int status) {
+    switch (status) {
+    case VS_OK: return "ok";
+    case VS_ERR_NULL: return "required pointer is NULL";
+    case VS_ERR_SHAPE: return "invalid size";
+    case VS_ERR_METRIC: return "unknown metric";
+    case VS_ERR_WORKSPACE: return "workspace too small";
+    case VS_ERR_ALIGN: return "misaligned pointer";
+    case VS_ERR_INDEX: return "index out of range";
+    case VS_ERR_UNSUPPORTED: return "no supported (gfx950) GPU";
+    case VS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+VS_API int vs_last_hip_error(void) { return g_last_hip; }
+
+VS_API const char *vs_version(void) { return "libvs 0.1 gfx950"; }

@@ -1,0 +1,163 @@
+// prep.hip -- squared-norm precompute and key initialisation (gfx950).
+//
+// The squared-L2 ranking uses |q|^2 + |c|^2 - 2 q.c; |c|^2 is the same for
+// every query, so it is computed once per call here instead of inside the
+// scan (the diversity shader of "Issue 9-014: Tile Diversity Shader Inner
+// Loop For L2 Cache Locality", "FP16 storage path", keeps norm accumulators
+// inside its inner loop).  Every norm is summed in one fixed order that does
+// not depend on alignment, table size or launch shape, so a candidate's
+// norm -- and with it every ranking value -- is identical on every call.
+#include "vs_internal.h"
+
+namespace vs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_fill_keys(uint64_t *keys, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) keys[i] = kNoKey;
+}
+
+// One wave per row.  Lane l owns the 4-element groups starting at 4l + 256i
+// and accumulates them in index order; the 64 lane sums are then combined by
+// a fixed butterfly.  The vector and scalar variants read the same elements
+// in the same order.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X, int64_t rows,
+                                                    int32_t d, float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *x = X + row * (int64_t)d;
+    float acc = 0.0f;
+    for (int32_t k = 4 * lane; k < d; k += 256) {
+        if constexpr (VEC) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(x + k);
+            acc = __builtin_fmaf(v.x, v.x, acc);
+            acc = __builtin_fmaf(v.y, v.y, acc);
+            acc = __builtin_fmaf(v.z, v.z, acc);
+            acc = __builtin_fmaf(v.w, v.w, acc);
+        } else {
+            for (int e = 0; e < 4; ++e) {
+                if (k + e < d) {
+                    const float v = x[k + e];
+                    acc = __builtin_fmaf(v, v, acc);
+                }
+            }
+        }
+    }
+    for (int s = 32; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
+    if (lane == 0) out[row] = acc;
+}
+
+// Feature-major X (d x cols): column j's squared norm.  A workgroup owns 64
+// columns (VEC: 256, four per lane); its 16 waves each sum one contiguous
+// range of features in order, then wave 0 adds the 16 partial sums in wave
+// order.  Vector width does not change any column's order of summation.
+constexpr int kColWaves = 16;
+
+template <bool VEC>
+__global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__restrict__ X,
+                                                               int64_t cols, int32_t d,
+                                                               float *__restrict__ out) {
+    constexpr int W = VEC ? 4 : 1;
+    __shared__ f32x4 part[kColWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * W;
+    const int32_t k0 = (int32_t)((int64_t)d * wave / kColWaves);
+    const int32_t k1 = (int32_t)((int64_t)d * (wave + 1) / kColWaves);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c0 < cols) {
+        const float *x = X + c0;
+        if constexpr (VEC) {
+#pragma unroll 8
+            for (int32_t k = k0; k < k1; ++k) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(x + (int64_t)k * cols);
+                acc.x = __builtin_fmaf(v.x, v.x, acc.x);
+                acc.y = __builtin_fmaf(v.y, v.y, acc.y);
+                acc.z = __builtin_fmaf(v.z, v.z, acc.z);
+                acc.w = __builtin_fmaf(v.w, v.w, acc.w);
+            }
+        } else {
+#pragma unroll 8
+            for (int32_t k = k0; k < k1; ++k) {
+                const float v = x[(int64_t)k * cols];
+                acc.x = __builtin_fmaf(v, v, acc.x);
+            }
+        }
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && c0 < cols) {
+        f32x4 s = part[0][lane];
+        for (int w = 1; w < kColWaves; ++w) s += part[w][lane];
+        if constexpr (VEC) {
+            *reinterpret_cast<f32x4 *>(out + c0) = s;
+        } else {
+            out[c0] = s.x;
+        }
+    }
+}
+
+// Squared norm of each CSR row, summed in storage order.  Rows whose range
+// is not inside [0, nnz] get NaN (they are not scanned either).
+__global__ __launch_bounds__(256) void k_csr_row_sqnorms(const int32_t *__restrict__ indptr,
+                                                        const float *__restrict__ values,
+                                                        int64_t nq, int64_t nnz,
+                                                        float *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nq) return;
+    const int64_t b = indptr[i], e = indptr[i + 1];
+    if (b < 0 || e < b || e > nnz) {
+        out[i] = __builtin_nanf("");
+        return;
+    }
+    float acc = 0.0f;
+    for (int64_t p = b; p < e; ++p) acc = __builtin_fmaf(values[p], values[p], acc);
+    out[i] = acc;
+}
+
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_fill_keys(uint64_t *keys, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_keys, dim3(blocks_for(n, 256)), dim3(256), 0, st, keys, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *out,
+                              hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const bool vec = (d % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    if (vec)
+        hipLaunchKernelGGL(k_row_sqnorms<true>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, X,
+                           rows, d, out);
+    else
+        hipLaunchKernelGGL(k_row_sqnorms<false>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, X,
+                           rows, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int32_t d, float *out,
+                              hipStream_t st) {
+    if (cols <= 0) return hipSuccess;
+    const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    if (vec)
+        hipLaunchKernelGGL(k_col_sqnorms<true>, dim3(blocks_for(cols, 256)), dim3(64 * kColWaves),
+                           0, st, X, cols, d, out);
+    else
+        hipLaunchKernelGGL(k_col_sqnorms<false>, dim3(blocks_for(cols, 64)), dim3(64 * kColWaves),
+                           0, st, X, cols, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
+                                  int64_t nnz, float *out, hipStream_t st) {
+    if (nq <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_csr_row_sqnorms, dim3(blocks_for(nq, 256)), dim3(256), 0, st, indptr,
+                       values, nq, nnz, out);
+    return hipGetLastError();
+}
+
+}  // namespace vs

@@ -1,0 +1,104 @@
+// vs_internal.h -- declarations shared by the HIP sources of libvs (gfx950).
+//
+// Packed arg-reduction keys.  A candidate's ranking value e (float, smaller
+// is better after the metric's sign is applied) and its index j are packed
+// into one uint64 so that the unsigned minimum of packed keys is the
+// lexicographic minimum of (e, j): the best value, lowest index on ties.
+// That makes the merge of partial winners exact and order-independent, which
+// is the associativity argument of "Issue 9-014: Tile Diversity Shader Inner
+// Loop For L2 Cache Locality", "Intended Behavior", applied to (value, index)
+// pairs.  0xFFFF...F means "no candidate".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vs {
+
+constexpr uint64_t kNoKey = ~0ull;
+
+enum Metric : int { L2SQ_MIN = 0, L2SQ_MAX = 1, COS_MAX = 2, COS_MIN = 3 };
+
+__host__ __device__ constexpr bool metric_is_l2(int m) { return m == L2SQ_MIN || m == L2SQ_MAX; }
+__host__ __device__ constexpr bool metric_is_max(int m) { return m == L2SQ_MAX || m == COS_MAX; }
+
+// Order-preserving float -> uint32 map (-0 folded onto +0 first).
+__device__ __forceinline__ uint32_t ord_of(float x) {
+    x = (x == 0.0f) ? 0.0f : x;
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float float_of_ord(uint32_t o) {
+    const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t pack_key(float e, uint32_t j) {
+    return (static_cast<uint64_t>(ord_of(e)) << 32) | j;
+}
+
+// Ranking value of one pair from its dot product s (and the candidate's
+// squared norm cn for squared L2).  The query's own squared norm is the same
+// for every candidate, so it is added back only when the score is reported.
+template <int M>
+__device__ __forceinline__ float rank_value(float s, float cn) {
+    if constexpr (M == L2SQ_MIN) return __builtin_fmaf(-2.0f, s, cn);
+    else if constexpr (M == L2SQ_MAX) return __builtin_fmaf(2.0f, s, -cn);
+    else if constexpr (M == COS_MAX) return -s;
+    else return s;
+}
+
+// ---------------------------------------------------------------- kernels --
+
+struct DenseArgs {
+    const float *Q;         // nq x d (unused when gathering)
+    const float *C;         // nc x d
+    const int32_t *pick;    // gather: query i is row pick[i] of C
+    const uint32_t *mask;   // nq x W words, or null
+    const float *cn;        // nc squared norms (L2 metrics)
+    uint64_t *keys;         // nq packed keys (pre-filled with kNoKey)
+    int64_t nq, nc;
+    int32_t d;
+    int64_t mask_words;     // W
+    int64_t n_items;        // query tiles x candidate tiles
+    int64_t n_ctiles;
+    int32_t grid;           // launched workgroups (for the item split)
+};
+
+struct CsrArgs {
+    const int32_t *indptr, *indices;
+    const float *values;
+    const float *CT;        // d x nc
+    const float *cn;        // nc
+    uint64_t *keys;         // nq
+    int64_t nq, nnz, nc;
+    int32_t d;
+    int64_t n_chunks;       // candidate chunks
+    int64_t n_items;        // n_chunks * n_qgroups
+    int32_t qgroup;         // queries per wave item
+};
+
+// Launchers (return hipError_t of the launch).  `timed` brackets the launch
+// with the library's timing events when recording is on.
+hipError_t launch_fill_keys(uint64_t *keys, int64_t n, hipStream_t st);
+hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *out,
+                              hipStream_t st);
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int32_t d, float *out,
+                              hipStream_t st);
+hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
+                                  int64_t nnz, float *out, hipStream_t st);
+hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t st,
+                        int n_cu);
+hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu);
+hipError_t launch_finalize(const uint64_t *keys, const float *qn, int64_t nq, int metric,
+                           int32_t *idx_out, float *score_out, hipStream_t st);
+hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mask,
+                               int64_t mask_words, int32_t *idx_out, float *score_out,
+                               hipStream_t st);
+
+// Timing hook (api.hip).
+void timing_before(hipStream_t st, const char *name);
+void timing_after(hipStream_t st);
+
+}  // namespace vs

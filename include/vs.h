@@ -1,0 +1,168 @@
+/*
+ * vs.h -- C ABI of libvs: masked arg-reduction scans on AMD MI355X (gfx950).
+ *
+ * For every query vector the library finds the best row of a candidate
+ * table -- nearest or farthest by squared Euclidean distance, or most/least
+ * similar by cosine on unit-norm rows -- optionally skipping candidates a
+ * per-query bit mask excludes, with the lowest candidate index winning ties.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [BMU] "From 80x to 385x: A Best-Matching-Unit Search at the L2 Roof,
+ *        Measured Against a Symmetrically Tuned Baseline" (summary),
+ *        section 3 "Background: the design being tuned": the best-matching
+ *        unit of each article is its closest neuron; sparse articles against
+ *        a feature-major codebook, the arg-reduction fused into the product
+ *        so the score block never reaches memory.
+ *  [DIV] "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache
+ *        Locality", "Current Behavior" and "Intended Behavior": per sequence,
+ *        the unmasked candidate most different from the reference vector,
+ *        which is then masked; a tiled scan must give the same winner as
+ *        the untiled one.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device pointers owned by the caller.  The
+ *    library never allocates, frees or retains them after the call's work
+ *    has completed on `stream`.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every call is asynchronous: it validates its arguments on the host,
+ *    enqueues kernels on `stream` and returns.  Outputs are valid once the
+ *    stream reaches the call.  Calls on one stream are ordered, so results
+ *    of one call may feed the next without a host synchronisation.
+ *  - Matrices are row-major and contiguous (row stride = number of columns).
+ *    Any d >= 1 works; 16-byte vector loads are used when d % 4 == 0 and the
+ *    matrix pointers are 16-byte aligned, 4-byte loads otherwise.
+ *  - Inputs are assumed finite; NaN/Inf inputs give unspecified winners.
+ *  - `workspace` is caller-provided device memory of at least the size the
+ *    matching *_workspace() query returns, 256-byte aligned.  Its contents
+ *    need no initialisation and are clobbered.  Two calls in flight at the
+ *    same time must not share a workspace.
+ *  - Return value: a vs_status.  The library never aborts, prints or throws.
+ *    Arguments are checked before anything is enqueued; a failed check
+ *    enqueues nothing.  A HIP launch failure returns VS_ERR_HIP and the HIP
+ *    error code is kept for vs_last_hip_error().
+ *  - A query whose every candidate is masked gets index -1 and score NaN;
+ *    this is not an error.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    on every call, independent of how the work is split across the GPU.
+ */
+#ifndef VS_H
+#define VS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VS_OK = 0,
+    VS_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    VS_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be,
+                               or too large for 32-bit indices              */
+    VS_ERR_METRIC = 3,      /* unknown metric code                           */
+    VS_ERR_WORKSPACE = 4,   /* workspace smaller than *_workspace() returns  */
+    VS_ERR_ALIGN = 5,       /* float/int pointer not 4-byte aligned, or
+                               workspace not 256-byte aligned               */
+    VS_ERR_INDEX = 6,       /* an index argument is out of range             */
+    VS_ERR_UNSUPPORTED = 7, /* no GPU of a supported architecture            */
+    VS_ERR_HIP = 8          /* a HIP call failed; see vs_last_hip_error()    */
+} vs_status;
+
+typedef enum {
+    VS_L2SQ_MIN = 0, /* nearest by squared L2 (the BMU)              [BMU] */
+    VS_L2SQ_MAX = 1, /* farthest by squared L2                             */
+    VS_COS_MAX = 2,  /* most similar: rows unit-norm, score = dot          */
+    VS_COS_MIN = 3   /* most different: rows unit-norm, score = dot [DIV]  */
+} vs_metric;
+
+/*
+ * Dense search [BMU].
+ *   Q          nq x d float32, queries.
+ *   C          nc x d float32, candidates (codebook, one neuron per row).
+ *   metric     a vs_metric.  COS_* assume unit-norm rows and rank by q.c.
+ *   idx_out    int32[nq]: winning candidate per query (lowest index on ties).
+ *   score_out  float32[nq] (may be NULL): squared distance of the winner
+ *              (|q|^2 + |c|^2 - 2 q.c, clamped at 0) for L2SQ_*, q.c for COS_*.
+ * nq == 0 is a no-op.  nc must be in [1, 2^31-1], d in [1, 2^20].
+ */
+size_t vs_bmu_search_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric);
+int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                  int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse-query search over a feature-major codebook [BMU, section 3 and
+ * section 4 "The levers"].
+ *   indptr     int32[nq+1], indices int32[nnz], values float32[nnz]: CSR
+ *              queries over d features.  Column indices must be unique within
+ *              a row (their order is free).  Rows may be empty.
+ *   CT         d x nc float32, feature-major codebook: column j is neuron j.
+ *   metric, idx_out, score_out as for vs_bmu_search.
+ * Device-side guard: a row whose indptr range is not inside [0, nnz] or
+ * that holds a column index outside [0, d) is not scanned; it gets index -1
+ * and score NaN.  Nothing outside the arrays is ever read.
+ */
+size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric);
+int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                      int64_t nq, int64_t nnz, const float *CT, int64_t nc, int32_t d,
+                      int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * One step of the greedy diversity sequence [DIV] for nseq sequences at once.
+ *   C          n x d float32, unit-norm rows (the embedding table).
+ *   last_pick  int32[nseq]: each sequence's reference row (its last pick).
+ *   mask_bits  uint32[nseq][W], W = ceil(n/32), in/out: bit j (word j/32,
+ *              bit j%32, least significant first) set = row j excluded.
+ *              Bits at or above n are never read.
+ *   idx_out    int32[nseq]: the unmasked row with the smallest cosine to the
+ *              reference (lowest index on ties); its bit is then set in the
+ *              sequence's mask.  -1 if every row is masked or last_pick is
+ *              outside [0, n) (then the mask is left unchanged).
+ *   score_out  float32[nseq] or NULL: cosine (dot) of the pick.
+ * idx_out may alias last_pick, so a chain of steps can reuse one buffer.
+ */
+size_t vs_diversity_step_workspace(int64_t n, int32_t d, int64_t nseq);
+int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_pick,
+                      uint32_t *mask_bits, int64_t nseq, int32_t *idx_out, float *score_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Squared L2 norms of candidates, float32, fixed summation order (the same
+ * values the searches use).  feature_major == 0: C is nc x d (row j);
+ * otherwise C is d x nc (column j).  norms_out is float32[nc].
+ */
+int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t feature_major,
+                       float *norms_out, void *stream);
+
+/*
+ * Candidate tile rows that fit a cache with headroom: floor(cache_bytes *
+ * 0.85 / (d * bytes_per_value)), at least 1 ["Issue 9-014", "Intended
+ * Behavior" and "Suggested Implementation Steps"].  Host-only.  Returns 0
+ * for invalid arguments.
+ */
+int64_t vs_tile_rows(int64_t cache_bytes, int32_t d, int32_t bytes_per_value);
+
+/*
+ * Measurement hook (host-only bookkeeping, no device memory): while enabled,
+ * the dominant kernel of each call is bracketed by a pair of HIP events on
+ * the call's stream.  vs_timing_enable(max_launches) (re)starts recording
+ * for up to max_launches launches (0 disables); vs_timing_read() waits for
+ * the recorded events, returns the summed kernel time in milliseconds and the
+ * number of launches, and stops recording.  Kernel names: see
+ * vs_timing_kernel_name().
+ */
+int vs_timing_enable(int32_t max_launches);
+int vs_timing_read(double *total_ms, int64_t *launches);
+const char *vs_timing_kernel_name(void);
+
+const char *vs_status_str(int status);
+int vs_last_hip_error(void);
+const char *vs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VS_H */

@@ -1,0 +1,192 @@
+"""GPU parity of the dense search (vs_bmu_search) against the fp64 oracle.
+
+Sizes span several 128x128 work items and ragged tails on both axes; d spans
+ragged 32-feature slabs and the scalar-load (d % 4 != 0, misaligned) path.
+Acceptance: tests/parity.py (score within 1e-4 relative, index bit-exact
+outside the oracle's 1e-5 top-two gap, inside the gap otherwise).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from goldens import hand_cases
+from parity import check, l2_floor
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import farthest_vector_search_amd as vs  # noqa: E402
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, offset_elems=0):
+    """Copy to the GPU; offset_elems > 0 yields a contiguous tensor whose data
+    pointer is not 16-byte aligned (exercises the scalar-load path)."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if offset_elems == 0:
+        return t.to(dev())
+    flat = torch.empty(t.numel() + offset_elems, dtype=t.dtype, device=dev())
+    out = flat[offset_elems:].view(t.shape)
+    out.copy_(t.to(dev()))
+    return out
+
+
+def run_dense(Q, C, metric, offset=0):
+    idx, score = vs.vs_bmu_search(to_dev(Q, offset), to_dev(C, offset), metric)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy()
+
+
+def assert_parity(Q, C, metric, threads=8, offset=0):
+    idx, score = run_dense(Q, C, metric, offset)
+    o_idx, o_val, o_gap = oracle.dense(Q, C, metric, threads=threads)
+    floor = l2_floor(Q, C, o_idx) if metric in (0, 1) else 1e-2
+    fails, stats = check(idx, score, o_idx, o_val, o_gap, metric, floor,
+                         lambda r, c: oracle.pair_values(Q, C, metric, r, c))
+    assert not fails, fails
+    return stats
+
+
+@pytest.mark.parametrize("case", hand_cases(), ids=lambda c: c["name"])
+def test_hand_cases(case):
+    if case["mask"]:
+        pytest.skip("masks are an input of the diversity step only")
+    idx, score = run_dense(case["Q"], case["C"], case["metric"])
+    assert idx[0] == case["expect_idx"]
+    assert abs(score[0] - case["expect_value"]) <= 1e-6
+
+
+D_VALUES = [1, 3, 4, 5, 31, 32, 33, 64, 65, 255, 256, 257, 768, 769]
+
+
+@pytest.mark.parametrize("d", D_VALUES)
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+def test_feature_dims(d, metric):
+    dist = "unit" if metric in (2, 3) else "normal"
+    Q, C = synth.dense_case(65, 300, d, dist, key=d * 4 + metric)
+    assert_parity(Q, C, metric)
+
+
+SHAPES = [(1, 1), (1, 2), (2, 13), (63, 127), (65, 128), (129, 129), (200, 1000), (1, 5000)]
+
+
+@pytest.mark.parametrize("nq,nc", SHAPES)
+@pytest.mark.parametrize("metric", [0, 3])
+def test_shapes(nq, nc, metric):
+    dist = "unit" if metric == 3 else "uniform"
+    Q, C = synth.dense_case(nq, nc, 48, dist, key=nq * 7 + nc)
+    assert_parity(Q, C, metric)
+
+
+@pytest.mark.parametrize("d", [64, 66])
+def test_misaligned_pointers(d):
+    Q, C = synth.dense_case(70, 260, d, "normal", key=31 + d)
+    assert_parity(Q, C, 0, offset=1)
+
+
+def test_work_split_inside_query_tiles():
+    """More work items than workgroups: runs start and stop inside a query
+    tile's candidate sweep, so per-query results merge across workgroups."""
+    Q, C = synth.dense_case(128 * 41, 128 * 31 + 77, 64, "normal", key=77)
+    stats = assert_parity(Q, C, 0, threads=16)
+    assert stats["same_index"] >= 0.999 * Q.shape[0]
+
+
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+def test_duplicates_lowest_index(metric):
+    """Exact copies at j, j+n, j+2n (different tiles, workgroups and lane
+    halves) must resolve to the first copy."""
+    dist = "unit" if metric in (2, 3) else "normal"
+    Q, C0 = synth.dense_case(300, 173, 40, dist, key=90 + metric)
+    C = np.concatenate([C0, C0, C0])
+    idx, _ = run_dense(Q, C, metric)
+    o_idx, _, _ = oracle.dense(Q, C, metric, threads=8)
+    assert (o_idx < 173).all()
+    assert np.array_equal(idx, o_idx)
+
+
+def test_self_match_and_integer_ties():
+    """Queries equal to candidates; small-integer data with many exact ties
+    (every dot product exact in fp32, so the lowest index must win)."""
+    Q, C = synth.dense_case(100, 400, 16, "int", key=5)
+    Q[:50] = C[150:200]
+    idx, score = run_dense(Q, C, 0)
+    o_idx, o_val, _ = oracle.dense(Q, C, 0)
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(score.astype(np.float64), o_val)
+
+
+def test_determinism():
+    Q, C = synth.dense_case(1000, 3000, 96, "normal", key=8)
+    outs = [run_dense(Q, C, 0) for _ in range(5)]
+    for i, s in outs[1:]:
+        assert np.array_equal(i, outs[0][0])
+        assert np.array_equal(s.view(np.uint32), outs[0][1].view(np.uint32))
+
+
+def test_no_score_output():
+    Q, C = synth.dense_case(33, 99, 8, "normal", key=9)
+    idx, score = vs.vs_bmu_search(to_dev(Q), to_dev(C), 0, want_score=False)
+    assert score is None
+    o_idx, _, _ = oracle.dense(Q, C, 0)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+
+
+def test_candidate_norms():
+    X = synth.dense_case(1, 1001, 37, "normal", key=10)[1]
+    ref = oracle.sqnorms(X)
+    n_rows = vs.vs_candidate_norms(to_dev(X)).cpu().numpy()
+    n_cols = vs.vs_candidate_norms(to_dev(np.ascontiguousarray(X.T)), feature_major=True).cpu().numpy()
+    assert np.allclose(n_rows, ref, rtol=1e-5)
+    assert np.allclose(n_cols, ref, rtol=1e-5)
+
+
+def test_empty_query_set():
+    C = torch.zeros((5, 4), dtype=torch.float32, device=dev())
+    Q = torch.zeros((0, 4), dtype=torch.float32, device=dev())
+    idx, score = vs.vs_bmu_search(Q, C, 0)
+    assert idx.numel() == 0
+
+
+# ------------------------------------------------------------ workloads --
+
+def test_workload_1_all_queries():
+    w = synth.workload(1)
+    stats = assert_parity(w["Q"], w["C"], w["metric"])
+    assert stats["rows"] == 256
+
+
+@pytest.mark.slow
+def test_workload_2_sampled():
+    """65,536 x 16,384, d = 256 at full size, the launch the benchmark
+    times; 512 seeded queries are checked one by one against the oracle."""
+    w = synth.workload(2)
+    idx, score = run_dense(w["Q"], w["C"], w["metric"])
+    sel = synth.sample_queries(w["nq"], 512, key=2)
+    Qs = w["Q"][sel]
+    o_idx, o_val, o_gap = oracle.dense(Qs, w["C"], 0, threads=16)
+    fails, stats = check(idx[sel], score[sel], o_idx, o_val, o_gap, 0,
+                         l2_floor(Qs, w["C"], o_idx),
+                         lambda r, c: oracle.pair_values(Qs, w["C"], 0, r, c))
+    assert not fails, fails
+    assert (idx >= 0).all() and (idx < w["nc"]).all()
+    assert np.isfinite(score).all() and (score >= 0).all()
+
+
+@pytest.mark.slow
+def test_workload_5_subset():
+    """65,536 x 262,144, d = 256; the oracle checks the seeded subset of
+    1,024 queries."""
+    w = synth.workload(5)
+    idx, score = run_dense(w["Q"], w["C"], w["metric"])
+    sel = w["subset"]
+    Qs = w["Q"][sel]
+    o_idx, o_val, o_gap = oracle.dense(Qs, w["C"], 0, threads=16)
+    fails, stats = check(idx[sel], score[sel], o_idx, o_val, o_gap, 0,
+                         l2_floor(Qs, w["C"], o_idx),
+                         lambda r, c: oracle.pair_values(Qs, w["C"], 0, r, c))
+    assert not fails, fails

@@ -1,0 +1,264 @@
+"""GPU parity of the diversity step and the sparse-query search.
+
+Diversity: the GPU runs the whole chain of steps on the device (each step's
+picks feed the next as reference rows); the oracle then replays the GPU's
+prefix step by step against the fp64 cosine Gram matrix and validates every
+pick with the rule of tests/parity.py.  The masks must end up holding
+exactly the seed plus the picks.
+
+Sparse: CSR queries over a feature-major codebook, checked against the
+oracle's sparse scan (itself pinned to the dense scan on densified rows).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from goldens import csr_cases, diversity_walk
+from parity import check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import farthest_vector_search_amd as vs  # noqa: E402
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def T(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def seed_masks(n, seeds):
+    W = (n + 31) // 32
+    m = np.zeros((len(seeds), W), np.uint32)
+    for s, j in enumerate(seeds):
+        m[s, j // 32] |= np.uint32(1 << (j % 32))
+    return m
+
+
+def gpu_chain(C, seeds, steps):
+    """Run `steps` diversity steps on the GPU; returns picks, scores, masks."""
+    Cd = T(C)
+    nseq = len(seeds)
+    mask = T(seed_masks(C.shape[0], seeds).view(np.int32))
+    last = T(np.asarray(seeds, np.int32))
+    picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    scores = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    ws = torch.empty(vs.lib().vs_diversity_step_workspace(C.shape[0], C.shape[1], nseq),
+                     dtype=torch.uint8, device=dev())
+    for t in range(steps):
+        vs.vs_diversity_step(Cd, last, mask, idx_out=picks[t], score_out=scores[t], workspace=ws)
+        last = picks[t]
+    torch.cuda.synchronize()
+    return (picks.cpu().numpy().T.copy(), scores.cpu().numpy().T.copy(),
+            mask.cpu().numpy().view(np.uint32))
+
+
+def validate_chain(C, seeds, picks, scores, masks, threads=8):
+    G = oracle.gram_cos(C, threads=threads)
+    rep = oracle.div_replay(G, seeds, picks, threads=threads)
+    fails = []
+    live = rep["bidx"] >= 0
+    # every pick legal where something was left; -1 exactly where nothing was
+    if not (rep["pick_ok"][live] == 1).all():
+        fails.append("illegal pick (masked or out of range)")
+    if not (picks[~live] == -1).all():
+        fails.append("pick where nothing was left")
+    nseq, steps = picks.shape
+    floor = 1e-2
+    f, stats = check(picks.reshape(-1), scores.reshape(-1), rep["bidx"].reshape(-1),
+                     rep["best"].reshape(-1), rep["gap"].reshape(-1), 3, floor,
+                     lambda r, c: rep["pick_value"].reshape(-1)[r],
+                     legal=lambda r, c: rep["pick_ok"].reshape(-1)[r] == 1)
+    fails += f
+    # masks: seed plus every pick, nothing else
+    n = C.shape[0]
+    exp = seed_masks(n, seeds)
+    for s in range(nseq):
+        for p in picks[s]:
+            if p >= 0:
+                exp[s, p // 32] |= np.uint32(1 << (p % 32))
+    if not np.array_equal(exp, masks):
+        fails.append("final masks differ from seed + picks")
+    for s in range(nseq):
+        row = picks[s][picks[s] >= 0]
+        if len(np.unique(row)) != len(row) or seeds[s] in row:
+            fails.append(f"sequence {s} repeats a row")
+            break
+    return fails, stats
+
+
+def test_diversity_walk():
+    w = diversity_walk()
+    picks, scores, masks = gpu_chain(w["C"], [w["seed"]], len(w["picks"]))
+    assert list(picks[0]) == w["picks"]
+    for got, exp in zip(scores[0], w["values"]):
+        assert (np.isnan(got) and np.isnan(exp)) or abs(got - exp) <= 1e-6
+
+
+@pytest.mark.parametrize("n,d,nseq,steps", [(40, 3, 5, 41), (300, 64, 129, 20),
+                                            (1000, 65, 300, 12), (129, 768, 70, 6)])
+def test_diversity_chain(n, d, nseq, steps):
+    C = synth.dense_case(1, n, d, "unit", key=n + d)[1]
+    (r,) = synth.rng_children(900 + n, 1)
+    seeds = r.choice(n, nseq, replace=nseq > n).astype(np.int32)
+    picks, scores, masks = gpu_chain(C, seeds, steps)
+    fails, stats = validate_chain(C, seeds, picks, scores, masks)
+    assert not fails, fails
+
+
+def test_diversity_matches_direct_run():
+    """Tie-free small case: the GPU chain equals the oracle's own greedy run."""
+    C = synth.dense_case(1, 500, 32, "unit", key=4242)[1]
+    seeds = np.arange(0, 500, 7, dtype=np.int32)
+    picks, scores, _ = gpu_chain(C, seeds, 10)
+    o_picks, o_vals = oracle.div_run(C, seeds, 10)
+    assert np.array_equal(picks, o_picks)
+    assert np.allclose(scores, o_vals, rtol=1e-4, atol=1e-6)
+
+
+def test_diversity_invalid_reference():
+    """A reference outside [0, n) yields -1 and leaves the mask alone."""
+    C = synth.dense_case(1, 100, 8, "unit", key=3)[1]
+    Cd = T(C)
+    last = T(np.array([5, -1, 100, 7], np.int32))
+    mask = T(seed_masks(100, [5, 0, 0, 7]).view(np.int32))
+    before = mask.cpu().numpy().copy()
+    idx, score = vs.vs_diversity_step(Cd, last, mask)
+    idx = idx.cpu().numpy()
+    after = mask.cpu().numpy()
+    assert idx[1] == -1 and idx[2] == -1
+    assert idx[0] >= 0 and idx[3] >= 0
+    assert np.array_equal(after[1:3], before[1:3])
+
+
+@pytest.mark.slow
+def test_workload_3_full_chain():
+    """8,359 x 768 table, 3,584 sequences, 64 steps, every pick replayed."""
+    w = synth.workload(3)
+    picks, scores, masks = gpu_chain(w["C"], w["seeds"], w["steps"])
+    fails, stats = validate_chain(w["C"], w["seeds"], picks, scores, masks, threads=16)
+    assert not fails, fails
+    assert stats["rows"] == 3584 * 64
+
+
+# ------------------------------------------------------------------ CSR --
+
+def run_csr(indptr, indices, values, CT, metric):
+    idx, score = vs.vs_bmu_search_csr(T(indptr), T(indices), T(values), T(CT), metric)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy()
+
+
+def test_csr_hand_cases():
+    CT, rows = csr_cases()
+    for r in rows:
+        indptr = np.array([0, len(r["idx"])], np.int32)
+        idx, score = run_csr(indptr, np.array(r["idx"] or [0], np.int32)[:len(r["idx"])],
+                             np.array(r["val"] or [0], np.float32)[:len(r["val"])], CT,
+                             r["metric"])
+        assert idx[0] == r["expect_idx"], r
+        assert abs(score[0] - r["expect_value"]) <= 1e-6, r
+
+
+def csr_case(nq, d, nc, p, key, empty_rows=()):
+    (r,) = synth.rng_children(3000 + key, 1)
+    indptr, indices, values = synth.sparse_rows(r, nq, d, p)
+    for e in empty_rows:
+        lo, hi = int(indptr[e]), int(indptr[e + 1])
+        indices = np.concatenate([indices[:lo], indices[hi:]])
+        values = np.concatenate([values[:lo], values[hi:]])
+        indptr = indptr.copy()
+        indptr[e + 1:] -= hi - lo
+    CT = synth.uniform01(r, (d, nc))
+    synth.normalize_columns(CT)
+    return indptr, indices, values, CT
+
+
+def csr_parity(indptr, indices, values, CT, metric, threads=8):
+    idx, score = run_csr(indptr, indices, values, CT, metric)
+    o_idx, o_val, o_gap = oracle.csr(indptr, indices, values, CT, metric, threads=threads)
+    if metric in (0, 1):
+        qn = np.array([np.sum(values[indptr[i]:indptr[i + 1]].astype(np.float64) ** 2)
+                       for i in range(len(indptr) - 1)])
+        floor = 1e-2 * (qn + 1.0)
+    else:
+        floor = 1e-2
+    cscale = oracle.sqnorms(CT, feature_major=True)
+
+    def pv(rows, cand):
+        out = np.empty(rows.size)
+        for t, (i, j) in enumerate(zip(rows, cand)):
+            sub = np.array([0, indptr[i + 1] - indptr[i]], np.int32)
+            ii = indices[indptr[i]:indptr[i + 1]]
+            vv = values[indptr[i]:indptr[i + 1]]
+            col = np.ascontiguousarray(CT[:, j:j + 1])
+            _, v, _ = oracle.csr(sub, ii, vv, col, metric, col_sq=cscale[j:j + 1])
+            out[t] = v[0]
+        return out
+
+    fails, stats = check(idx, score, o_idx, o_val, o_gap, metric, floor, pv)
+    assert not fails, fails
+    return stats
+
+
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+@pytest.mark.parametrize("nc", [1, 63, 256, 1000, 1028])
+def test_csr_shapes(metric, nc):
+    empty = () if metric in (2, 3) else (0, 5)
+    indptr, indices, values, CT = csr_case(70, 300, nc, 0.05, key=nc * 4 + metric,
+                                           empty_rows=empty)
+    csr_parity(indptr, indices, values, CT, metric)
+
+
+def csr_select(indptr, indices, values, rows):
+    rows = np.asarray(rows)
+    ptr = np.concatenate([[0], np.cumsum(indptr[rows + 1] - indptr[rows])]).astype(np.int32)
+    idx = np.concatenate([indices[indptr[i]:indptr[i + 1]] for i in rows]).astype(np.int32)
+    val = np.concatenate([values[indptr[i]:indptr[i + 1]] for i in rows]).astype(np.float32)
+    return ptr, idx, val
+
+
+def test_csr_bad_rows_skipped():
+    """A column index outside [0, d) makes its row report (-1, NaN); the
+    other rows are unaffected."""
+    indptr, indices, values, CT = csr_case(10, 50, 64, 0.2, key=77)
+    bad = int(np.nonzero(indptr[1:] > indptr[:-1])[0][0])
+    indices = indices.copy()
+    indices[indptr[bad]] = 50  # == d
+    idx, score = run_csr(indptr, indices, values, CT, 0)
+    assert idx[bad] == -1 and np.isnan(score[bad])
+    good = np.array([i for i in range(10) if i != bad])
+    o_idx, _, _ = oracle.csr(*csr_select(indptr, indices, values, good), CT, 0)
+    assert np.array_equal(idx[good], o_idx)
+
+
+@pytest.mark.slow
+def test_workload_4_sampled():
+    """32,768 CSR rows (~164 nnz of 16,384) x 65,536 neurons at full size;
+    256 seeded rows are checked one by one against the oracle."""
+    w = synth.workload(4)
+    idx, score = run_csr(w["indptr"], w["indices"], w["values"], w["CT"], 0)
+    sel = synth.sample_queries(w["nq"], 256, key=4)
+    ptr = w["indptr"]
+    sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
+    sub_idx = np.concatenate([w["indices"][ptr[i]:ptr[i + 1]] for i in sel])
+    sub_val = np.concatenate([w["values"][ptr[i]:ptr[i + 1]] for i in sel])
+    col_sq = oracle.sqnorms(w["CT"], feature_major=True, threads=16)
+    o_idx, o_val, o_gap = oracle.csr(sub_ptr, sub_idx, sub_val, w["CT"], 0, col_sq=col_sq,
+                                     threads=16)
+    qn = np.array([np.sum(sub_val[sub_ptr[i]:sub_ptr[i + 1]].astype(np.float64) ** 2)
+                   for i in range(len(sel))])
+    fails, stats = check(idx[sel], score[sel], o_idx, o_val, o_gap, 0, 1e-2 * (qn + 1.0),
+                         lambda r, c: np.array([
+                             oracle.csr(np.array([0, sub_ptr[i + 1] - sub_ptr[i]], np.int32),
+                                        sub_idx[sub_ptr[i]:sub_ptr[i + 1]],
+                                        sub_val[sub_ptr[i]:sub_ptr[i + 1]],
+                                        np.ascontiguousarray(w["CT"][:, j:j + 1]), 0,
+                                        col_sq=col_sq[j:j + 1])[1][0]
+                             for i, j in zip(r, c)]))
+    assert not fails, fails
+    assert (idx >= 0).all()
