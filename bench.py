@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration mode: time a plain device copy of this many bytes "
+                         "(the reference kernel for scaling HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -124,8 +127,12 @@ def setup(k, torch, vs):
     indptr = torch.from_numpy(w["indptr"]).to(dev)
     indices = torch.from_numpy(w["indices"]).to(dev)
     values = torch.from_numpy(w["values"]).to(dev)
-    CT = torch.from_numpy(w["CT"]).to(dev)
+    # feature-major codebook with rows padded by 64 neurons: a row stride of
+    # 65,536 floats (a power of two) would alias every row's slice onto the
+    # same L2 sets
     nq, nc = w["nq"], w["nc"]
+    CT = torch.empty((w["d"], nc + 64), dtype=torch.float32, device=dev)[:, :nc]
+    CT.copy_(torch.from_numpy(w["CT"]).to(dev))
     idx = torch.empty(nq, dtype=torch.int32, device=dev)
     score = torch.empty(nq, dtype=torch.float32, device=dev)
     ws = torch.empty(vs.lib().vs_bmu_search_csr_workspace(nq, nc, w["d"], 0), dtype=torch.uint8,
@@ -137,8 +144,11 @@ def setup(k, torch, vs):
     pairs = nq * nc
     w["nnz"] = int(w["indices"].shape[0])
     flops = 2.0 * w["nnz"] * nc
-    cfg = dict(workload=w["name"], nq=nq, nc=nc, d=w["d"], nnz=w["nnz"], metric="l2sq_min")
-    return w, step, pairs, flops, 1, cfg
+    cfg = dict(workload=w["name"], nq=nq, nc=nc, d=w["d"], nnz=w["nnz"], metric="l2sq_min",
+               codebook_row_stride=nc + 64)
+    chunks = (nc + 63) // 64
+    rounds = (chunks + min(8, chunks) - 1) // min(8, chunks)  # one scan launch per round
+    return w, step, pairs, flops, rounds, cfg
 
 
 # ------------------------------------------------------------ cpu leg --
@@ -195,6 +205,26 @@ def cpu_baseline(k, w, target_s):
                 seconds=round(dt, 2))
 
 
+def copy_calibration(a, torch):
+    """A plain copy of known size (read n bytes, write n bytes) per launch."""
+    n = a.copy_bytes // 4
+    src = torch.rand(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(a.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(a.steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                      "launches": a.steps + a.warmup, "ms_per_copy": ms,
+                      "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +236,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
         sys.exit(1)
+    if a.copy_bytes > 0:
+        copy_calibration(a, torch)
+        return
     log(f"workload {a.workload}: generating inputs")
     w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs)
     torch.cuda.synchronize()
@@ -223,21 +256,23 @@ def main():
         dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / a.steps
     value = pairs * a.steps / dt
-    kernel_ms = kt.ms / max(kt.launches, 1)
-    flops_per_launch = flops / launches_per_step
-    roof = None
+    # roofline of the dominant kernel: algorithmic work of the timed steps over
+    # the summed durations of its launches (= per-launch work / mean launch time)
+    launches = max(kt.launches, 1)
+    kernel_ms = kt.ms / launches
+    kernel_s_total = kt.ms * 1e-3
     if w["kind"] in ("dense", "diversity"):
-        achieved = flops_per_launch / (kernel_ms * 1e-3) / 1e12
+        achieved = flops * a.steps / kernel_s_total / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4))
     else:
-        # sparse: algorithmic codebook bytes (4 B per non-zero x neuron) per
-        # launch against the HBM peak; the measured on-chip roof is reported
-        # separately in the design doc
-        bytes_per_launch = 4.0 * w["nnz"] * w["nc"]
-        achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+        # sparse: 4 codebook bytes per non-zero x neuron multiply-add, served
+        # from the XCDs' L2; reported against the HBM peak here, and against
+        # the measured L2 roof in the design notes
+        achieved = 4.0 * w["nnz"] * w["nc"] * a.steps / kernel_s_total / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
+    roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
     roof["traffic"] = load_traffic(a.traffic_json, kt.name, cfg["workload"])

@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
     L.vs_bmu_search.argtypes = [P, P, I64, I64, I32, I32, P, P, P, SZ, P]
     L.vs_bmu_search_csr_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_csr_workspace.restype = SZ
-    L.vs_bmu_search_csr.argtypes = [P, P, P, I64, I64, P, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_bmu_search_csr.argtypes = [P, P, P, I64, I64, P, I64, I64, I32, I32, P, P, P, SZ, P]
     L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
     L.vs_diversity_step_workspace.restype = SZ
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
@@ -159,14 +159,19 @@ def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, worksp
 
 def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=None,
                       score_out=None, workspace=None, want_score: bool = True):
-    """Best codebook column of CT (d x nc, feature-major) for every CSR row."""
+    """Best codebook column of CT (d x nc, feature-major) for every CSR row.
+
+    CT may be a row-padded view (CT.stride(0) > nc), e.g.
+    ``torch.empty(d, nc + 64)[:, :nc]``: its row stride is passed as ldct."""
     torch = _torch()
     L = lib()
     m = _metric(metric)
     _dev(indptr, "indptr", torch.int32, 1)
     _dev(indices, "indices", torch.int32, 1)
     _dev(values, "values", torch.float32, 1)
-    _dev(CT, "CT", torch.float32, 2)
+    if not isinstance(CT, torch.Tensor) or not CT.is_cuda or CT.dtype != torch.float32 \
+            or CT.dim() != 2 or CT.stride(1) != 1 or CT.stride(0) < CT.shape[1]:
+        raise ValueError("CT must be a float32 CUDA matrix with unit column stride")
     nq = indptr.numel() - 1
     nnz = indices.numel()
     if values.numel() != nnz:
@@ -181,7 +186,8 @@ def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=N
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_bmu_search_csr(_ptr(indptr), _ptr(indices) if nnz else None,
-                                 _ptr(values) if nnz else None, nq, nnz, _ptr(CT), nc, d, m,
+                                 _ptr(values) if nnz else None, nq, nnz, _ptr(CT), nc,
+                                 CT.stride(0), d, m,
                                  _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search_csr")

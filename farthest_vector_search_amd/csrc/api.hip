@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -75,6 +76,15 @@ Layout search_layout(int64_t nq, int64_t nc, int32_t metric) {
         L.total += up256((size_t)nc * 4);
     }
     return L;
+}
+
+// Dense kernel choice: queries in registers when d allows it (default), the
+// LDS-tiled kernel otherwise.  VS_DENSE_KERNEL=tiled|qreg overrides the
+// choice (both give identical results; used to test and compare them).
+bool use_qreg_kernel(int32_t d) {
+    const char *env = std::getenv("VS_DENSE_KERNEL");
+    if (env && std::strcmp(env, "tiled") == 0) return false;
+    return vs::qreg_supports(d);
 }
 
 #define VS_TRY_HIP(expr)                   \
@@ -191,30 +201,41 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     a.nq = nq;
     a.nc = nc;
     a.d = d;
-    VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu));
+    if (use_qreg_kernel(d)) VS_TRY_HIP(vs::launch_dense_qreg(a, metric, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu));
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
 }
 
 // ---- sparse-query search ---------------------------------------------------
 
+// Workspace of the CSR search: keys[nq] | qn[nq] | cn[nc] | partial keys
+// [csr_groups(nc)][nq].
+struct CsrLayout {
+    size_t keys = 0, qn = 0, cn = 0, part = 0, total = 0;
+};
+CsrLayout csr_layout(int64_t nq, int64_t nc) {
+    CsrLayout L;
+    L.qn = up256((size_t)nq * 8);
+    L.cn = L.qn + up256((size_t)nq * 4);
+    L.part = L.cn + up256((size_t)nc * 4);
+    L.total = L.part + up256((size_t)vs::csr_groups(nc) * (size_t)nq * 8);
+    return L;
+}
+
 VS_API size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric) {
     (void)d;
     if (nq < 0 || nc < 0 || metric < 0 || metric > 3) return 0;
-    Layout L;
-    L.total = up256((size_t)nq * 8);
-    L.total += up256((size_t)nq * 4);  // query norms (also used by the cosine metrics)
-    L.total += up256((size_t)nc * 4);
-    return L.total;
+    return csr_layout(nq, nc).total;
 }
 
 VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
-                             int64_t nq, int64_t nnz, const float *CT, int64_t nc, int32_t d,
-                             int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ldct,
+                             int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
     if (metric < 0 || metric > 3) return VS_ERR_METRIC;
     if (nq < 0 || nq > kMaxIndex || nnz < 0 || nnz > kMaxIndex || nc < 1 || nc > kMaxIndex ||
-        d < 1 || d > kMaxIndex)
+        ldct < nc || d < 1 || d > kMaxIndex)
         return VS_ERR_SHAPE;
     if (nq == 0) return VS_OK;
     if (!indptr || !CT || !idx_out || !workspace || (nnz > 0 && (!indices || !values)))
@@ -222,19 +243,19 @@ VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, cons
     if (!al4(indptr) || !al4(indices) || !al4(values) || !al4(CT) || !al4(idx_out) ||
         !al4(score_out) || !al256(workspace))
         return VS_ERR_ALIGN;
-    const size_t need = vs_bmu_search_csr_workspace(nq, nc, d, metric);
-    if (workspace_bytes < need) return VS_ERR_WORKSPACE;
+    const CsrLayout L = csr_layout(nq, nc);
+    if (workspace_bytes < L.total) return VS_ERR_WORKSPACE;
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    uint64_t *keys = reinterpret_cast<uint64_t *>(ws);
-    float *qn = reinterpret_cast<float *>(ws + up256((size_t)nq * 8));
-    float *cn = reinterpret_cast<float *>(ws + up256((size_t)nq * 8) + up256((size_t)nq * 4));
+    uint64_t *keys = reinterpret_cast<uint64_t *>(ws + L.keys);
+    float *qn = reinterpret_cast<float *>(ws + L.qn);
+    float *cn = reinterpret_cast<float *>(ws + L.cn);
+    uint64_t *part = reinterpret_cast<uint64_t *>(ws + L.part);
 
-    VS_TRY_HIP(vs::launch_fill_keys(keys, nq, st));
-    if (vs::metric_is_l2(metric)) VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, d, cn, st));
+    if (vs::metric_is_l2(metric)) VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, ldct, d, cn, st));
     if (vs::metric_is_l2(metric) && score_out)
         VS_TRY_HIP(vs::launch_csr_row_sqnorms(indptr, values, nq, nnz, qn, st));
 
@@ -248,8 +269,9 @@ VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, cons
     a.nq = nq;
     a.nnz = nnz;
     a.nc = nc;
+    a.ldct = ldct;
     a.d = d;
-    VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu));
+    VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu, part));
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
 }
@@ -307,7 +329,7 @@ VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t fea
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (feature_major) VS_TRY_HIP(vs::launch_col_sqnorms(C, nc, d, norms_out, st));
+    if (feature_major) VS_TRY_HIP(vs::launch_col_sqnorms(C, nc, nc, d, norms_out, st));
     else VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, norms_out, st));
     return VS_OK;
 }

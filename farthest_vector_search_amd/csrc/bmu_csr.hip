@@ -2,136 +2,205 @@
 // fused with the arg-reduction.
 //
 // Source: "From 80x to 385x: A Best-Matching-Unit Search at the L2 Roof ..."
-// (summary), section 3 (codebook stored feature-major, weight columns read
-// once and reused, argmin fused so no score block is stored) and section 4
-// (levers: articles per tile, neuron-axis chunking, vectorised loads).
+// (summary), section 3 (codebook stored feature-major, weight columns
+// reused, argmin fused so no score block is stored) and section 4 (levers:
+// neuron-axis chunking to keep the codebook slice cache-resident, tile
+// sizes, vectorised loads); section 6: the tuned kernel is bound by L2
+// bandwidth.
 //
 // For a query with non-zeros (k, v) the dot product with neuron n is
-// sum v * CT[k][n]; with the codebook feature-major, the neurons of one
-// feature are contiguous, so a wave that owns a chunk of consecutive neurons
-// reads each needed codebook row segment with fully coalesced loads
-// (16-byte loads when the layout allows: "vectorised loads").  The work
-// items are (neuron chunk, query) pairs in chunk-major order, so the waves
-// running at one time share one chunk of the codebook (neuron-axis
-// chunking), and the XCD-aware renumbering keeps an XCD's waves on
-// neighbouring queries of that chunk.
+// sum v * CT[k][n].  Feature-major storage makes the neurons of one feature
+// contiguous, so a half-wave that owns 32 consecutive neurons (one per lane)
+// reads the codebook row segment of each non-zero with one coalesced
+// 128-byte load; the two halves of a wave serve two queries.  On this data a codebook value is needed by ~1.3 of the
+// queries that share a tile, so reuse comes from the cache, not from LDS or
+// registers: the kernel is bound by on-chip (L2) bandwidth at 4 bytes per
+// multiply-add, and the design goal is that those bytes are L2 hits.
 //
-// Per item a wave accumulates the dot products of its neurons in CSR order
-// (a fixed order), ranks them (|c|^2 - 2 q.c for squared L2, +-q.c for
-// cosine), reduces over its lanes to one (value, index) pair with the lowest
-// index on ties, and merges it into the query's packed key with atomicMin.
+// Neuron-axis chunking, gfx950 style: the slice of the codebook for 32
+// neurons is d x 128 bytes (2 MiB at d = 16,384), half of one XCD's L2; the
+// CSR arrays, read once per round, are loaded non-temporally so that they do
+// not evict it.  A codebook row stride that is a multiple of a large power of
+// two maps every row's slice onto the same few L2 sets, so the row stride
+// (ldct) is a parameter and callers can pad it.  Each launch
+// is one "round": P <= 8 groups of workgroups, group x = blockIdx % P (the
+// hardware deals consecutive workgroups to the eight XCDs in turn, so with
+// P = 8 a group is one XCD) works on chunk round*P + x, its waves splitting
+// all queries between them.  The kernel boundary between rounds keeps every
+// XCD on a single chunk (a hard step, as the dispatch-per-tile variant of
+// "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache Locality",
+// "Intended Behavior", proposes), instead of letting waves drift across
+// chunks and thrash the L2.
+//
+// Merge: the wave that owns (group x, query q) is the only writer of
+// partial[x][q] in its round, and rounds are ordered on the stream, so the
+// running best per (group, query) is a plain read-min-write; a final pass
+// takes the minimum over the P groups.  Packed (value, index) keys make both
+// minima exact and order-independent (lowest index on ties).
 // Rows with an out-of-range indptr span or column index are skipped whole
 // (nothing outside the arrays is read) and keep the "no candidate" key.
+#include <cstdlib>
+
 #include "vs_internal.h"
 
 namespace vs {
 
-template <int NPL>
-struct VecT;
-template <>
-struct VecT<1> { typedef float T; };
-template <>
-struct VecT<2> { typedef float T __attribute__((ext_vector_type(2))); };
-template <>
-struct VecT<4> { typedef float T __attribute__((ext_vector_type(4))); };
+constexpr int kCsrWgPerCu = 7;   // 7 x 4 waves resident per CU (VGPR-limited)
+constexpr int kCsrUnroll = 8;
 
-template <int NPL>
-__device__ __forceinline__ void load_n(const float *p, float (&out)[NPL]) {
-    if constexpr (NPL == 1) {
-        out[0] = *p;
-    } else {
-        const typename VecT<NPL>::T v = *reinterpret_cast<const typename VecT<NPL>::T *>(p);
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) out[j] = v[j];
-    }
+template <typename T>
+__device__ __forceinline__ T stream_load(const T *p) {
+    return __builtin_nontemporal_load(p);
 }
 
-template <int M, int NPL>
-__global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a) {
-    constexpr int NCW = 64 * NPL;  // neurons per wave item
-    const int lane = threadIdx.x & 63;
-    int g = blockIdx.x;
-    const int G = gridDim.x;
-    if ((G & 7) == 0) g = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    const int64_t W = (int64_t)G * 4;
-    const int64_t w = (int64_t)g * 4 + (threadIdx.x >> 6);
-    const int64_t nq = a.nq, nc = a.nc;
+// HALVES = 1: a wave scans one query over a chunk of 64 neurons (one per
+// lane); HALVES = 2: each half-wave scans its own query over a chunk of 32.
+// A query's non-zeros are brought in 64 at a time with one coalesced,
+// non-temporal load (lane j takes non-zero t+j); lane j turns its (k, v)
+// into a record {address of codebook row k, v} in a wave-private LDS area.
+// The walk over the batch then costs, per non-zero, one broadcast LDS read
+// of the record, one 64-bit address add, one load of this lane's neuron and
+// one FMA.
+template <int M, int HALVES>
+__global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__restrict__ part,
+                                                int64_t round, int32_t groups) {
+    constexpr int NCW = 64 / HALVES;
+    constexpr int U = kCsrUnroll;
+    __shared__ uint64_t rec[4][HALVES][64];  // per wave, per query: row addresses
+    __shared__ float wgt[4][HALVES][64];     // ... and weights
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = HALVES == 2 ? (lane >> 5) : 0;
+    const int sub = lane % NCW;
+    const int x = (int)(blockIdx.x % (unsigned)groups);
+    const int64_t local = blockIdx.x / (unsigned)groups;
+    const int64_t chunk = round * groups + x;
+    if (chunk >= a.n_chunks) return;
+    const int64_t waves_per_group = (int64_t)(gridDim.x / (unsigned)groups) * 4;
+    const int64_t lw = __builtin_amdgcn_readfirstlane((int)(local * 4 + wave));
+    const int64_t nq = a.nq, nc = a.nc, ld = a.ldct;
     const int32_t d = a.d;
+    const int32_t n = (int32_t)(chunk * NCW + sub);
+    const bool live = n < nc;
+    const uint64_t off = (uint64_t)(live ? n : 0) * 4u;  // dead lanes read column 0
+    const float cn = (metric_is_l2(M) && live) ? a.cn[n] : 0.0f;
+    uint64_t *mine = part + (int64_t)x * nq;
+    const uint64_t ct = reinterpret_cast<uint64_t>(a.CT);
+    const int64_t qstep = HALVES * waves_per_group;
 
-    for (int64_t item = w; item < a.n_items; item += W) {
-        const int64_t chunk = item / nq;
-        const int64_t q = item - chunk * nq;
-        const int64_t n0 = chunk * NCW + (int64_t)lane * NPL;
-        const bool live = n0 < nc;  // NPL > 1 only when nc % NPL == 0
-        int64_t b = a.indptr[q], e = a.indptr[q + 1];
-        bool ok = b >= 0 && e >= b && e <= a.nnz;
-        if (!ok) b = e = 0;
-
-        float acc[NPL];
+    // A "pair" is the HALVES queries a wave scans together.
+    struct Pair {
+        int64_t q0, b[HALVES], len[HALVES], L;
+        bool ok[HALVES];
+    };
+    auto open_pair = [&](int64_t q0) {
+        Pair P;
+        P.q0 = q0;
+        P.L = 0;
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) acc[j] = 0.0f;
-        const float *base = a.CT + (live ? n0 : 0);
-
-        int64_t p = b;
-        for (; p + 4 <= e; p += 4) {
-            int32_t k[4];
-            float v[4], c[4][NPL];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                k[u] = a.indices[p + u];
-                v[u] = a.values[p + u];
-                if ((uint32_t)k[u] >= (uint32_t)d) {
-                    ok = false;
-                    k[u] = 0;
+        for (int hh = 0; hh < HALVES; ++hh) {
+            const int64_t q = q0 + hh;
+            P.b[hh] = 0;
+            P.len[hh] = 0;
+            P.ok[hh] = q < nq;
+            if (P.ok[hh]) {
+                const int64_t bb = a.indptr[q], ee = a.indptr[q + 1];
+                P.ok[hh] = bb >= 0 && ee >= bb && ee <= a.nnz;
+                if (P.ok[hh]) {
+                    P.b[hh] = bb;
+                    P.len[hh] = ee - bb;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (live) load_n<NPL>(base + (int64_t)k[u] * nc, c[u]);
-                else
-#pragma unroll
-                    for (int j = 0; j < NPL; ++j) c[u][j] = 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) acc[j] = __builtin_fmaf(v[u], c[u][j], acc[j]);
+            P.L = P.len[hh] > P.L ? P.len[hh] : P.L;
         }
-        for (; p < e; ++p) {
-            int32_t k = a.indices[p];
-            const float v = a.values[p];
-            if ((uint32_t)k >= (uint32_t)d) {
-                ok = false;
-                k = 0;
+        return P;
+    };
+    // lane j fetches non-zero t+j of each query of the pair (0, 0 past its end)
+    int32_t pk[HALVES];
+    float pv[HALVES];
+    auto prefetch = [&](const Pair &P, int64_t t) {
+#pragma unroll
+        for (int hh = 0; hh < HALVES; ++hh) {
+            pk[hh] = 0;
+            pv[hh] = 0.0f;
+            if (t + lane < P.len[hh]) {
+                pk[hh] = stream_load(a.indices + P.b[hh] + t + lane);
+                pv[hh] = stream_load(a.values + P.b[hh] + t + lane);
             }
-            float c[NPL];
-            if (live) load_n<NPL>(base + (int64_t)k * nc, c);
-            else
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) c[j] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) acc[j] = __builtin_fmaf(v, c[j], acc[j]);
         }
-        if (!ok) continue;  // same decision on every lane of the wave
+    };
+    auto issue = [&](int base, float (&c)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t addr = rec[wave][half][base + u] + off;
+            c[u] = *reinterpret_cast<const __attribute__((address_space(1))) float *>(addr);
+        }
+    };
+    auto consume = [&](int base, const float (&c)[U], float &acc) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = __builtin_fmaf(wgt[wave][half][base + u], c[u], acc);
+    };
 
-        float be = __builtin_inff();
-        int32_t bi = -1;
-        if (live) {
+    if (lw * HALVES >= nq) return;
+    Pair cur = open_pair(HALVES * lw);
+    prefetch(cur, 0);
+    while (true) {
+        float acc = 0.0f;
+        Pair nxt = cur;
+        bool more = false;
+        for (int64_t t = 0; t < cur.L; t += 64) {
+            // this batch's (k, v) arrived with the previous prefetch
+            int32_t kk[HALVES];
+            float vv[HALVES];
 #pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const int64_t n = n0 + j;
-                if (n < nc) {
-                    const float cnn = metric_is_l2(M) ? a.cn[n] : 0.0f;
-                    const float r = rank_value<M>(acc[j], cnn);
-                    if (r < be) {
-                        be = r;
-                        bi = (int32_t)n;
-                    }
+            for (int hh = 0; hh < HALVES; ++hh) {
+                kk[hh] = pk[hh];
+                vv[hh] = pv[hh];
+            }
+            // start fetching the next batch (of this pair, or of the next pair)
+            if (t + 64 < cur.L) {
+                prefetch(cur, t + 64);
+            } else if (cur.q0 + qstep < nq) {
+                nxt = open_pair(cur.q0 + qstep);
+                more = true;
+                prefetch(nxt, 0);
+            }
+#pragma unroll
+            for (int hh = 0; hh < HALVES; ++hh) {
+                const bool bad = (uint32_t)kk[hh] >= (uint32_t)d;
+                if (__any(bad)) cur.ok[hh] = false;
+                if (bad) {
+                    kk[hh] = 0;
+                    vv[hh] = 0.0f;
+                }
+                rec[wave][hh][lane] = ct + (uint64_t)kk[hh] * (uint64_t)ld * 4u;
+                wgt[wave][hh][lane] = vv[hh];
+            }
+            // walk the batch: U loads in flight while the previous U are used
+            const int64_t rem = cur.L - t;
+            const int cnt = (int)((rem < 64 ? rem : 64) + U - 1) / U * U;
+            float c0[U], c1[U];
+            issue(0, c0);
+            for (int u0 = 0; u0 < cnt; u0 += 2 * U) {
+                const bool two = u0 + U < cnt;
+                if (two) issue(u0 + U, c1);
+                consume(u0, c0, acc);
+                if (two) {
+                    if (u0 + 2 * U < cnt) issue(u0 + 2 * U, c0);
+                    consume(u0 + U, c1, acc);
                 }
             }
         }
+        if (cur.L == 0 && cur.q0 + qstep < nq) {  // an all-empty pair prefetches nothing above
+            nxt = open_pair(cur.q0 + qstep);
+            more = true;
+            prefetch(nxt, 0);
+        }
+
+        const bool row_ok = half ? cur.ok[HALVES - 1] : cur.ok[0];
+        float be = (live && row_ok) ? rank_value<M>(acc, cn) : __builtin_inff();
+        int32_t bi = (live && row_ok) ? n : -1;
 #pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
+        for (int s = NCW / 2; s >= 1; s >>= 1) {
             const float oe = __shfl_xor(be, s);
             const int32_t oi = __shfl_xor(bi, s);
             if (oi >= 0 && (bi < 0 || oe < be || (oe == be && oi < bi))) {
@@ -139,40 +208,83 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a) {
                 bi = oi;
             }
         }
-        if (lane == 0 && bi >= 0)
-            atomicMin(reinterpret_cast<unsigned long long *>(a.keys + q),
-                      (unsigned long long)pack_key(be, (uint32_t)bi));
+        if (sub == 0 && row_ok && bi >= 0) {
+            const int64_t q = cur.q0 + half;
+            const uint64_t key = pack_key(be, (uint32_t)bi);
+            if (key < mine[q]) mine[q] = key;
+        }
+        if (!more) break;
+        cur = nxt;
     }
 }
 
-template <int NPL>
-static void dispatch_metric(const CsrArgs &a, int metric, dim3 grid, hipStream_t st) {
-    switch (metric) {
-    case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MIN, NPL>), grid, dim3(256), 0, st, a); break;
-    case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MAX, NPL>), grid, dim3(256), 0, st, a); break;
-    case COS_MAX: hipLaunchKernelGGL((k_bmu_csr<COS_MAX, NPL>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_bmu_csr<COS_MIN, NPL>), grid, dim3(256), 0, st, a); break;
+__global__ __launch_bounds__(256) void k_min_partials(const uint64_t *__restrict__ part,
+                                                     int32_t groups, int64_t nq,
+                                                     uint64_t *__restrict__ keys) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nq) return;
+    uint64_t k = part[q];
+    for (int x = 1; x < groups; ++x) {
+        const uint64_t o = part[(int64_t)x * nq + q];
+        k = o < k ? o : k;
     }
+    keys[q] = k;
 }
 
-hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu) {
+// Neurons per chunk: 64 (one query per wave) by default, 32 (two queries
+// per wave, half the codebook slice per XCD) with VS_CSR_CHUNK=32.  Both give
+// identical results; 64 halves the rounds and with them the re-reads of the
+// CSR arrays, which measured faster on the 65,536-neuron codebook.
+static int csr_chunk() {
+    const char *env = getenv("VS_CSR_CHUNK");
+    return (env && env[0] == '3') ? 32 : 64;
+}
+
+int32_t csr_groups(int64_t nc) {
+    const int64_t chunks = (nc + 31) / 32;  // the larger count of the two chunk widths
+    return (int32_t)(chunks < 8 ? chunks : 8);
+}
+
+hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
+                      uint64_t *part) {
     CsrArgs a = a0;
-    const bool vec4 = (a.nc % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.CT) & 15) == 0);
-    const int npl = vec4 ? 4 : 1;
-    const int64_t ncw = 64 * npl;
+    const int ncw = csr_chunk();
     a.n_chunks = (a.nc + ncw - 1) / ncw;
-    a.n_items = a.n_chunks * a.nq;
-    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256) * 8;  // 8 workgroups (32 waves) per CU
-    const int64_t wg_needed = (a.n_items + 3) / 4;
-    int64_t grid = wg_needed < cap ? wg_needed : cap;
-    if (grid >= 8) grid &= ~int64_t(7);
-    if (grid < 1) grid = 1;
-    timing_before(st, "k_bmu_csr");
-    if (vec4) dispatch_metric<4>(a, metric, dim3((unsigned)grid), st);
-    else dispatch_metric<1>(a, metric, dim3((unsigned)grid), st);
-    const hipError_t err = hipGetLastError();
-    timing_after(st);
-    return err;
+    const int32_t groups = (int32_t)(a.n_chunks < 8 ? a.n_chunks : 8);
+    // workgroups per group: enough waves for the queries, at most a full chip
+    const int64_t cu = n_cu > 0 ? n_cu : 256;
+    int64_t per_group = (cu * kCsrWgPerCu) / groups;
+    const int64_t need = (a.nq + 4 * (64 / ncw) - 1) / (4 * (64 / ncw));
+    if (per_group > need) per_group = need;
+    if (per_group < 1) per_group = 1;
+    const dim3 grid((unsigned)(per_group * groups)), block(256);
+    const int64_t rounds = (a.n_chunks + groups - 1) / groups;
+    hipError_t err = launch_fill_keys(part, (int64_t)groups * a.nq, st);
+    if (err != hipSuccess) return err;
+    for (int64_t r = 0; r < rounds; ++r) {
+        timing_before(st, "k_bmu_csr");
+        if (ncw == 32) {
+            switch (metric) {
+            case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MIN, 2>), grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MAX, 2>), grid, block, 0, st, a, part, r, groups); break;
+            case COS_MAX: hipLaunchKernelGGL((k_bmu_csr<COS_MAX, 2>), grid, block, 0, st, a, part, r, groups); break;
+            default: hipLaunchKernelGGL((k_bmu_csr<COS_MIN, 2>), grid, block, 0, st, a, part, r, groups); break;
+            }
+        } else {
+            switch (metric) {
+            case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MIN, 1>), grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MAX, 1>), grid, block, 0, st, a, part, r, groups); break;
+            case COS_MAX: hipLaunchKernelGGL((k_bmu_csr<COS_MAX, 1>), grid, block, 0, st, a, part, r, groups); break;
+            default: hipLaunchKernelGGL((k_bmu_csr<COS_MIN, 1>), grid, block, 0, st, a, part, r, groups); break;
+            }
+        }
+        err = hipGetLastError();
+        timing_after(st);
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_min_partials, dim3((unsigned)((a.nq + 255) / 256)), block, 0, st, part,
+                       groups, a.nq, a.keys);
+    return hipGetLastError();
 }
 
 }  // namespace vs

@@ -1,0 +1,323 @@
+// bmu_qreg.hip -- dense scan for d <= 256 with the queries held in registers.
+//
+// Same computation and result as bmu_mfma.hip (fp32 MFMA dot products,
+// fused ranking and lowest-index arg-reduction, packed-key merge), arranged
+// so that HBM/L2 traffic stays near the algorithmic bytes: every wave keeps
+// its 32 query rows in VGPRs for its whole candidate sweep (d/2 registers per
+// lane), so a query is read from memory once per kernel, and only candidate
+// slabs move through LDS.  Sources, by page title and section:
+//  - "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache Locality",
+//    "Intended Behavior": every workgroup walks the same candidate tiles in
+//    the same order, so a tile is fetched into the cache once and served to
+//    all of them; the running best persists across tiles;
+//  - "From 80x to 385x: A Best-Matching-Unit Search at the L2 Roof ..."
+//    (summary), section 3: the argmin fused into the product;
+//  - "Tiling en memoria compartida: el factor 16", "Tiling en registros":
+//    the reused operand lives in registers (here the query block).
+//
+// Layout: workgroup = 8 waves = 256 queries (32 per wave, one MFMA column
+// block each); work item = (query tile of 256, candidate tile of 64 = two
+// 32-row MFMA blocks).  Candidate slabs of 64 features are double-buffered
+// in LDS (2 x 16 KiB); a row is 16 pieces of 16 bytes stored at slot
+// (piece XOR row%16), which keeps both the 256-byte coalesced global loads
+// and the 16-byte MFMA operand reads free of bank conflicts.  Lane half h
+// feeds features 8c+4h..8c+4h+3 of chunk c to four consecutive MFMAs from
+// one LDS read (candidates) and one register quad (queries); every pair's
+// dot product therefore runs over one fixed feature order.
+#include "vs_internal.h"
+
+namespace vs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kQW = 8;         // waves per workgroup
+constexpr int kBQ = 32 * kQW;  // queries per tile
+constexpr int kBC = 64;        // candidates per tile
+constexpr int kBK = 64;        // features per LDS slab
+constexpr int kCPS = kBK / 8;  // 8-feature chunks per slab
+constexpr int kPieces = kBK / 4;
+
+__device__ __forceinline__ int slab_at(int row, int piece) {
+    return row * kBK + ((piece ^ (row & 15)) << 2);
+}
+
+template <bool VEC>
+__device__ __forceinline__ f32x4 ld4(const float *p, int32_t k, int32_t d) {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p != nullptr) {
+        if constexpr (VEC) {
+            if (k < d) v = *reinterpret_cast<const f32x4 *>(p + k);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < d) v[e] = p[k + e];
+        }
+    }
+    return v;
+}
+
+}  // namespace
+
+// LDS-DMA (global_load_lds, 16 bytes per lane): lane l of the issuing wave
+// writes LDS bytes [base + 16 l, base + 16 l + 16).
+__device__ __forceinline__ void dma16(const float *g, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const float *g, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+}
+
+template <int M, bool VEC, int NSLAB>
+__global__ __launch_bounds__(64 * kQW) __attribute__((amdgpu_waves_per_eu(2)))
+void k_bmu_qreg(const DenseArgs a) {
+    constexpr int NT = 64 * kQW;
+    constexpr int NCH = NSLAB * kCPS;
+    constexpr int RPP = NT / kPieces;  // loader rows per pass (register path)
+    constexpr int AP = kBC / RPP;      // loader pieces per thread (register path)
+    constexpr int RPW = kBC / kQW;     // slab rows owned by each wave (DMA path)
+    static_assert(kBC % RPP == 0 && RPW % 4 == 0, "loader shape");
+
+    __shared__ __attribute__((aligned(16))) float sA[2][kBC * kBK];
+    __shared__ __attribute__((aligned(16))) float sN[2][kBC];  // candidate norms, by item parity
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wave = tid >> 6;
+
+    int g = blockIdx.x;
+    const int G = a.grid;
+    if ((G & 7) == 0) g = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+    const int64_t it0 = (int64_t)g * a.n_items / G;
+    const int64_t it1 = (int64_t)(g + 1) * a.n_items / G;
+    if (it0 >= it1) return;
+
+    const int32_t d = a.d;
+    const int64_t nq = a.nq, nc = a.nc, nct = a.n_ctiles;
+
+    f32x4 qreg[NCH];
+    auto load_queries = [&](int64_t qt) {
+        const int64_t q = qt * kBQ + wave * 32 + l32;
+        const float *p = q < nq ? a.Q + q * d : nullptr;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) qreg[c] = ld4<VEC>(p, 8 * c + 4 * h, d);
+    };
+
+    // ---- candidate slab loader ----------------------------------------
+    // VEC: direct-to-LDS.  Wave w fills rows [RPW w, RPW w + RPW); one
+    // instruction covers 4 rows x 16 slots, lane l -> row +l/16, slot l%16,
+    // which holds piece slot ^ (row % 16) of that row.  Elements outside the
+    // table (rows >= nc, features >= d) are written as zeros with ds_write.
+    // Scalar path: through registers, as in the tiled kernel.
+    const int lrow = tid / kPieces, lpiece = tid % kPieces;
+    const float *aptr[AP];
+    f32x4 ra[AP];
+    int64_t row_base = 0;  // first candidate of the item being loaded
+    auto set_rows = [&](int64_t item) {
+        row_base = (item % nct) * kBC;
+        if constexpr (!VEC) {
+#pragma unroll
+            for (int i = 0; i < AP; ++i) {
+                const int64_t c = row_base + lrow + i * RPP;
+                aptr[i] = c < nc ? a.C + c * d : nullptr;
+            }
+        }
+    };
+    auto load_slab = [&](int slab, int buf) {
+        if constexpr (VEC) {
+#pragma unroll
+            for (int i = 0; i < RPW / 4; ++i) {
+                const int row = wave * RPW + 4 * i + (lane >> 4);
+                const int slot = lane & 15;
+                const int piece = slot ^ (row & 15);
+                const int64_t c = row_base + row;
+                const int32_t k = slab * kBK + 4 * piece;
+                float *dst = &sA[buf][(wave * RPW + 4 * i) * kBK];
+                if (c < nc && k < d) dma16(a.C + c * d + k, dst);
+                else *reinterpret_cast<f32x4 *>(dst + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        } else {
+            const int32_t k = slab * kBK + 4 * lpiece;
+#pragma unroll
+            for (int i = 0; i < AP; ++i) ra[i] = ld4<false>(aptr[i], k, d);
+        }
+    };
+    auto finish_slab = [&](int buf) {  // register path: registers -> LDS
+        if constexpr (!VEC) {
+#pragma unroll
+            for (int i = 0; i < AP; ++i)
+                *reinterpret_cast<f32x4 *>(&sA[buf][slab_at(lrow + i * RPP, lpiece)]) = ra[i];
+        }
+    };
+    auto load_norms = [&](int par) {  // wave 0: the item's 64 candidate norms
+        if constexpr (metric_is_l2(M)) {
+            if (wave == 0) {
+                const int64_t c = row_base + lane;
+                if constexpr (VEC) {
+                    if (c < nc) dma4(a.cn + c, &sN[par][0]);
+                    else sN[par][lane] = 0.0f;
+                } else {
+                    sN[par][lane] = c < nc ? a.cn[c] : 0.0f;
+                }
+            }
+        }
+    };
+    auto wait_loads = [&]() {
+        if constexpr (VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    float best = __builtin_inff();
+    int32_t bidx = -1;
+
+    // Accumulator register r of a lane = candidate row 8*(r/4)+4h+(r%4) of
+    // its 32-row block, query column l32; rows rise with r and tiles are
+    // visited in ascending order, so strict "<" keeps the lowest index.
+    auto epilogue = [&](int64_t item, int par) {
+        const int64_t base = (item % nct) * kBC;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int row0 = cb * 32 + 8 * r4 + 4 * h;
+                f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (metric_is_l2(M))
+                    cn4 = *reinterpret_cast<const f32x4 *>(&sN[par][row0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t c = base + row0 + e;
+                    const float v = rank_value<M>(acc[cb][4 * r4 + e], cn4[e]);
+                    if (c < nc && v < best) {
+                        best = v;
+                        bidx = (int32_t)c;
+                    }
+                }
+            }
+            acc[cb] = f32x16{};
+        }
+    };
+    auto flush = [&](int64_t qt) {
+        const float oe = __shfl_xor(best, 32);
+        const int32_t oi = __shfl_xor(bidx, 32);
+        if (oi >= 0 && (bidx < 0 || oe < best || (oe == best && oi < bidx))) {
+            best = oe;
+            bidx = oi;
+        }
+        const int64_t q = qt * kBQ + wave * 32 + l32;
+        if (h == 0 && bidx >= 0 && q < nq)
+            atomicMin(reinterpret_cast<unsigned long long *>(a.keys + q),
+                      (unsigned long long)pack_key(best, (uint32_t)bidx));
+        best = __builtin_inff();
+        bidx = -1;
+    };
+
+    int64_t qt = it0 / nct;
+    load_queries(qt);
+    set_rows(it0);
+    load_slab(0, 0);
+    load_norms(0);
+    finish_slab(0);
+    wait_loads();
+    __syncthreads();
+    int buf = 0, par = 0;
+    for (int64_t item = it0; item < it1; ++item) {
+#pragma unroll
+        for (int s = 0; s < NSLAB; ++s) {
+            bool has_next = true;
+            if (s + 1 < NSLAB) {
+                load_slab(s + 1, buf ^ 1);
+            } else {
+                has_next = item + 1 < it1;
+                if (has_next) {
+                    set_rows(item + 1);
+                    load_slab(0, buf ^ 1);
+                    load_norms(par ^ 1);
+                }
+            }
+            // 8 chunks of 8 features; the operands of chunk cc+1 are read
+            // from LDS while the MFMAs of chunk cc run
+            const float *A = sA[buf];
+            f32x4 f0[2], f1[2];
+            f0[0] = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, h)]);
+            f1[0] = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, h)]);
+#pragma unroll
+            for (int cc = 0; cc < kCPS; ++cc) {
+                if (cc + 1 < kCPS) {
+                    const int piece = 2 * (cc + 1) + h;
+                    f0[(cc + 1) & 1] = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, piece)]);
+                    f1[(cc + 1) & 1] = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, piece)]);
+                }
+                const f32x4 a0 = f0[cc & 1], a1 = f1[cc & 1];
+                const f32x4 qv = qreg[s * kCPS + cc];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[e], qv[e], acc[0], 0, 0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], qv[e], acc[1], 0, 0, 0);
+                }
+            }
+            if (s == NSLAB - 1) epilogue(item, par);
+            if (has_next) finish_slab(buf ^ 1);
+            wait_loads();
+            __syncthreads();
+            buf ^= 1;
+        }
+        par ^= 1;
+        const int64_t next_qt = (item + 1) / nct;
+        if (item + 1 == it1 || next_qt != qt) {
+            flush(qt);
+            if (item + 1 < it1) {
+                qt = next_qt;
+                load_queries(qt);
+            }
+        }
+    }
+}
+
+template <int M, int NSLAB>
+static void dispatch_q(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) {
+    if (vec)
+        hipLaunchKernelGGL((k_bmu_qreg<M, true, NSLAB>), grid, dim3(64 * kQW), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_bmu_qreg<M, false, NSLAB>), grid, dim3(64 * kQW), 0, st, a);
+}
+
+template <int M>
+static void dispatch_slabs(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) {
+    const int nslab = (a.d + kBK - 1) / kBK;
+    switch (nslab) {
+    case 1: dispatch_q<M, 1>(a, vec, grid, st); break;
+    case 2: dispatch_q<M, 2>(a, vec, grid, st); break;
+    case 3: dispatch_q<M, 3>(a, vec, grid, st); break;
+    default: dispatch_q<M, 4>(a, vec, grid, st); break;
+    }
+}
+
+bool qreg_supports(int32_t d) { return d >= 1 && d <= 4 * kBK; }
+
+hipError_t launch_dense_qreg(const DenseArgs &a0, int metric, hipStream_t st, int n_cu) {
+    DenseArgs a = a0;
+    const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
+    a.n_ctiles = (a.nc + kBC - 1) / kBC;
+    a.n_items = nqt * a.n_ctiles;
+    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256);  // one 8-wave workgroup per CU
+    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    const bool vec = (a.d % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a.Q) & 15) == 0);
+    const dim3 grid((unsigned)a.grid);
+    timing_before(st, "k_bmu_qreg");
+    switch (metric) {
+    case L2SQ_MIN: dispatch_slabs<L2SQ_MIN>(a, vec, grid, st); break;
+    case L2SQ_MAX: dispatch_slabs<L2SQ_MAX>(a, vec, grid, st); break;
+    case COS_MAX: dispatch_slabs<COS_MAX>(a, vec, grid, st); break;
+    default: dispatch_slabs<COS_MIN>(a, vec, grid, st); break;
+    }
+    const hipError_t err = hipGetLastError();
+    timing_after(st);
+    return err;
+}
+
+}  // namespace vs

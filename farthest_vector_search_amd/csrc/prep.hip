@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X
     if (lane == 0) out[row] = acc;
 }
 
-// Feature-major X (d x cols): column j's squared norm.  A workgroup owns 64
+// Feature-major X (d rows of cols values, row stride ld): column j's squared norm.  A workgroup owns 64
 // columns (VEC: 256, four per lane); its 16 waves each sum one contiguous
 // range of features in order, then wave 0 adds the 16 partial sums in wave
 // order.  Vector width does not change any column's order of summation.
@@ -58,7 +58,8 @@ constexpr int kColWaves = 16;
 
 template <bool VEC>
 __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__restrict__ X,
-                                                               int64_t cols, int32_t d,
+                                                               int64_t cols, int64_t ld,
+                                                               int32_t d,
                                                                float *__restrict__ out) {
     constexpr int W = VEC ? 4 : 1;
     __shared__ f32x4 part[kColWaves][64];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__r
         if constexpr (VEC) {
 #pragma unroll 8
             for (int32_t k = k0; k < k1; ++k) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(x + (int64_t)k * cols);
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(x + (int64_t)k * ld);
                 acc.x = __builtin_fmaf(v.x, v.x, acc.x);
                 acc.y = __builtin_fmaf(v.y, v.y, acc.y);
                 acc.z = __builtin_fmaf(v.z, v.z, acc.z);
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__r
         } else {
 #pragma unroll 8
             for (int32_t k = k0; k < k1; ++k) {
-                const float v = x[(int64_t)k * cols];
+                const float v = x[(int64_t)k * ld];
                 acc.x = __builtin_fmaf(v, v, acc.x);
             }
         }
@@ -138,17 +139,18 @@ hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *ou
     return hipGetLastError();
 }
 
-hipError_t launch_col_sqnorms(const float *X, int64_t cols, int32_t d, float *out,
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int32_t d, float *out,
                               hipStream_t st) {
     if (cols <= 0) return hipSuccess;
-    const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
+    const bool vec = (cols % 4 == 0) && (ld % 4 == 0) &&
+                     ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
     if (vec)
         hipLaunchKernelGGL(k_col_sqnorms<true>, dim3(blocks_for(cols, 256)), dim3(64 * kColWaves),
-                           0, st, X, cols, d, out);
+                           0, st, X, cols, ld, d, out);
     else
         hipLaunchKernelGGL(k_col_sqnorms<false>, dim3(blocks_for(cols, 64)), dim3(64 * kColWaves),
-                           0, st, X, cols, d, out);
+                           0, st, X, cols, ld, d, out);
     return hipGetLastError();
 }
 

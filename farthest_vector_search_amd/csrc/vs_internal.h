@@ -69,28 +69,31 @@ struct DenseArgs {
 struct CsrArgs {
     const int32_t *indptr, *indices;
     const float *values;
-    const float *CT;        // d x nc
+    const float *CT;        // d rows of nc neurons, row stride ldct
     const float *cn;        // nc
     uint64_t *keys;         // nq
-    int64_t nq, nnz, nc;
+    int64_t nq, nnz, nc, ldct;
     int32_t d;
     int64_t n_chunks;       // candidate chunks
-    int64_t n_items;        // n_chunks * n_qgroups
-    int32_t qgroup;         // queries per wave item
 };
 
-// Launchers (return hipError_t of the launch).  `timed` brackets the launch
-// with the library's timing events when recording is on.
+// Launchers (return hipError_t of the launch).  The dominant kernel of each
+// entry point is bracketed by the library's timing events when recording.
 hipError_t launch_fill_keys(uint64_t *keys, int64_t n, hipStream_t st);
 hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *out,
                               hipStream_t st);
-hipError_t launch_col_sqnorms(const float *X, int64_t cols, int32_t d, float *out,
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int32_t d, float *out,
                               hipStream_t st);
 hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
                                   int64_t nnz, float *out, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t st,
                         int n_cu);
-hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu);
+// Queries-in-registers variant of the dense scan (d <= 256, no gather).
+bool qreg_supports(int32_t d);
+hipError_t launch_dense_qreg(const DenseArgs &a, int metric, hipStream_t st, int n_cu);
+// CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
+int32_t csr_groups(int64_t nc);
+hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);
 hipError_t launch_finalize(const uint64_t *keys, const float *qn, int64_t nq, int metric,
                            int32_t *idx_out, float *score_out, hipStream_t st);
 hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mask,

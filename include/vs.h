@@ -97,7 +97,12 @@ int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_
  *   indptr     int32[nq+1], indices int32[nnz], values float32[nnz]: CSR
  *              queries over d features.  Column indices must be unique within
  *              a row (their order is free).  Rows may be empty.
- *   CT         d x nc float32, feature-major codebook: column j is neuron j.
+ *   CT         feature-major codebook: d rows of nc float32, row k holding
+ *              feature k of every neuron (column j is neuron j).
+ *   ldct       row stride of CT in elements (>= nc).  Rows are read in slices
+ *              of a few neurons; a stride that is a multiple of a large power
+ *              of two (e.g. nc = 65,536 unpadded) maps every row's slice onto
+ *              the same cache sets, so pad it (e.g. ldct = nc + 64) for speed.
  *   metric, idx_out, score_out as for vs_bmu_search.
  * Device-side guard: a row whose indptr range is not inside [0, nnz] or
  * that holds a column index outside [0, d) is not scanned; it gets index -1
@@ -105,9 +110,9 @@ int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_
  */
 size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric);
 int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
-                      int64_t nq, int64_t nnz, const float *CT, int64_t nc, int32_t d,
-                      int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ldct,
+                      int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One step of the greedy diversity sequence [DIV] for nseq sequences at once.

@@ -103,13 +103,15 @@ def test_workspace_sizes(L):
 
 
 def test_csr_validation(L):
-    def call(indptr=FAKE, indices=FAKE, values=FAKE, nq=3, nnz=10, CT=FAKE, nc=16, d=8,
-             metric=0, idx=FAKE, score=FAKE, ws=FAKE, ws_bytes=1 << 20):
-        return L.vs_bmu_search_csr(_P(indptr), _P(indices), _P(values), nq, nnz, _P(CT), nc, d,
-                                   metric, _P(idx), _P(score), _P(ws), ws_bytes, None)
+    def call(indptr=FAKE, indices=FAKE, values=FAKE, nq=3, nnz=10, CT=FAKE, nc=16, ld=None,
+             d=8, metric=0, idx=FAKE, score=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_bmu_search_csr(_P(indptr), _P(indices), _P(values), nq, nnz, _P(CT), nc,
+                                   nc if ld is None else ld, d, metric, _P(idx), _P(score),
+                                   _P(ws), ws_bytes, None)
     assert call(metric=7) == 3
     assert call(nnz=-1) == 2
     assert call(nc=0) == 2
+    assert call(ld=15) == 2  # row stride below nc
     assert call(nq=0, indptr=0) == 0
     assert call(indptr=0) == 1
     assert call(indices=0) == 1

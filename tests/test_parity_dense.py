@@ -23,6 +23,14 @@ def dev():
     return torch.device("cuda:0")
 
 
+@pytest.fixture(params=["qreg", "tiled"])
+def kernel(request, monkeypatch):
+    """Run the test with each dense kernel (queries in registers for d <= 256,
+    the LDS-tiled kernel for any d); both must satisfy the same bar."""
+    monkeypatch.setenv("VS_DENSE_KERNEL", request.param)
+    return request.param
+
+
 def to_dev(a, offset_elems=0):
     """Copy to the GPU; offset_elems > 0 yields a contiguous tensor whose data
     pointer is not 16-byte aligned (exercises the scalar-load path)."""
@@ -65,7 +73,7 @@ D_VALUES = [1, 3, 4, 5, 31, 32, 33, 64, 65, 255, 256, 257, 768, 769]
 
 @pytest.mark.parametrize("d", D_VALUES)
 @pytest.mark.parametrize("metric", [0, 1, 2, 3])
-def test_feature_dims(d, metric):
+def test_feature_dims(d, metric, kernel):
     dist = "unit" if metric in (2, 3) else "normal"
     Q, C = synth.dense_case(65, 300, d, dist, key=d * 4 + metric)
     assert_parity(Q, C, metric)
@@ -76,19 +84,19 @@ SHAPES = [(1, 1), (1, 2), (2, 13), (63, 127), (65, 128), (129, 129), (200, 1000)
 
 @pytest.mark.parametrize("nq,nc", SHAPES)
 @pytest.mark.parametrize("metric", [0, 3])
-def test_shapes(nq, nc, metric):
+def test_shapes(nq, nc, metric, kernel):
     dist = "unit" if metric == 3 else "uniform"
     Q, C = synth.dense_case(nq, nc, 48, dist, key=nq * 7 + nc)
     assert_parity(Q, C, metric)
 
 
 @pytest.mark.parametrize("d", [64, 66])
-def test_misaligned_pointers(d):
+def test_misaligned_pointers(d, kernel):
     Q, C = synth.dense_case(70, 260, d, "normal", key=31 + d)
     assert_parity(Q, C, 0, offset=1)
 
 
-def test_work_split_inside_query_tiles():
+def test_work_split_inside_query_tiles(kernel):
     """More work items than workgroups: runs start and stop inside a query
     tile's candidate sweep, so per-query results merge across workgroups."""
     Q, C = synth.dense_case(128 * 41, 128 * 31 + 77, 64, "normal", key=77)
@@ -97,7 +105,7 @@ def test_work_split_inside_query_tiles():
 
 
 @pytest.mark.parametrize("metric", [0, 1, 2, 3])
-def test_duplicates_lowest_index(metric):
+def test_duplicates_lowest_index(metric, kernel):
     """Exact copies at j, j+n, j+2n (different tiles, workgroups and lane
     halves) must resolve to the first copy."""
     dist = "unit" if metric in (2, 3) else "normal"
@@ -109,7 +117,7 @@ def test_duplicates_lowest_index(metric):
     assert np.array_equal(idx, o_idx)
 
 
-def test_self_match_and_integer_ties():
+def test_self_match_and_integer_ties(kernel):
     """Queries equal to candidates; small-integer data with many exact ties
     (every dot product exact in fp32, so the lowest index must win)."""
     Q, C = synth.dense_case(100, 400, 16, "int", key=5)
@@ -120,7 +128,7 @@ def test_self_match_and_integer_ties():
     assert np.array_equal(score.astype(np.float64), o_val)
 
 
-def test_determinism():
+def test_determinism(kernel):
     Q, C = synth.dense_case(1000, 3000, 96, "normal", key=8)
     outs = [run_dense(Q, C, 0) for _ in range(5)]
     for i, s in outs[1:]:
@@ -153,6 +161,18 @@ def test_empty_query_set():
 
 
 # ------------------------------------------------------------ workloads --
+
+def test_kernels_agree_bitwise(monkeypatch):
+    """Both dense kernels run the same per-pair arithmetic in the same order,
+    so their outputs are identical bit for bit."""
+    Q, C = synth.dense_case(700, 2100, 200, "normal", key=12)
+    outs = []
+    for k in ("qreg", "tiled"):
+        monkeypatch.setenv("VS_DENSE_KERNEL", k)
+        outs.append(run_dense(Q, C, 0))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
 
 def test_workload_1_all_queries():
     w = synth.workload(1)

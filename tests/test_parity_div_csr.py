@@ -147,13 +147,25 @@ def test_workload_3_full_chain():
 
 # ------------------------------------------------------------------ CSR --
 
-def run_csr(indptr, indices, values, CT, metric):
-    idx, score = vs.vs_bmu_search_csr(T(indptr), T(indices), T(values), T(CT), metric)
+def padded(CT, pad):
+    """Device copy of CT whose rows are `pad` elements longer than nc (a view
+    with row stride nc + pad, as a caller avoiding cache-set aliasing would
+    allocate it)."""
+    if pad == 0:
+        return T(CT)
+    buf = torch.empty((CT.shape[0], CT.shape[1] + pad), dtype=torch.float32, device=dev())
+    view = buf[:, :CT.shape[1]]
+    view.copy_(torch.from_numpy(CT).to(dev()))
+    return view
+
+
+def run_csr(indptr, indices, values, CT, metric, pad=0):
+    idx, score = vs.vs_bmu_search_csr(T(indptr), T(indices), T(values), padded(CT, pad), metric)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), score.cpu().numpy()
 
 
-def test_csr_hand_cases():
+def test_csr_hand_cases(chunk):
     CT, rows = csr_cases()
     for r in rows:
         indptr = np.array([0, len(r["idx"])], np.int32)
@@ -162,6 +174,14 @@ def test_csr_hand_cases():
                              r["metric"])
         assert idx[0] == r["expect_idx"], r
         assert abs(score[0] - r["expect_value"]) <= 1e-6, r
+
+
+@pytest.fixture(params=["32", "64"])
+def chunk(request, monkeypatch):
+    """Run with each CSR chunk width (32 neurons = two queries per wave, 64 =
+    one query per wave); both must satisfy the same bar."""
+    monkeypatch.setenv("VS_CSR_CHUNK", request.param)
+    return request.param
 
 
 def csr_case(nq, d, nc, p, key, empty_rows=()):
@@ -207,11 +227,22 @@ def csr_parity(indptr, indices, values, CT, metric, threads=8):
 
 @pytest.mark.parametrize("metric", [0, 1, 2, 3])
 @pytest.mark.parametrize("nc", [1, 63, 256, 1000, 1028])
-def test_csr_shapes(metric, nc):
+def test_csr_shapes(metric, nc, chunk):
     empty = () if metric in (2, 3) else (0, 5)
     indptr, indices, values, CT = csr_case(70, 300, nc, 0.05, key=nc * 4 + metric,
                                            empty_rows=empty)
     csr_parity(indptr, indices, values, CT, metric)
+
+
+@pytest.mark.parametrize("pad", [1, 64])
+def test_csr_row_stride(pad, chunk):
+    """A padded codebook row stride (ldct > nc) gives bit-identical results."""
+    indptr, indices, values, CT = csr_case(90, 200, 700, 0.05, key=55)
+    a = run_csr(indptr, indices, values, CT, 0)
+    b = run_csr(indptr, indices, values, CT, 0, pad=pad)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    csr_parity(indptr, indices, values, CT, 0)
 
 
 def csr_select(indptr, indices, values, rows):
@@ -222,7 +253,7 @@ def csr_select(indptr, indices, values, rows):
     return ptr, idx, val
 
 
-def test_csr_bad_rows_skipped():
+def test_csr_bad_rows_skipped(chunk):
     """A column index outside [0, d) makes its row report (-1, NaN); the
     other rows are unaffected."""
     indptr, indices, values, CT = csr_case(10, 50, 64, 0.2, key=77)
@@ -241,7 +272,7 @@ def test_workload_4_sampled():
     """32,768 CSR rows (~164 nnz of 16,384) x 65,536 neurons at full size;
     256 seeded rows are checked one by one against the oracle."""
     w = synth.workload(4)
-    idx, score = run_csr(w["indptr"], w["indices"], w["values"], w["CT"], 0)
+    idx, score = run_csr(w["indptr"], w["indices"], w["values"], w["CT"], 0, pad=64)
     sel = synth.sample_queries(w["nq"], 256, key=4)
     ptr = w["indptr"]
     sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
