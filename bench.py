@@ -45,6 +45,13 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
+                                                          "COPY_WRITE_DB"),
+                    help="record HBM traffic per launch of the workload's dominant kernel from "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases of the workload and "
+                         "of the --copy-bytes calibration run, then exit")
+    ap.add_argument("--traffic-copy-bytes", type=int, default=268435456,
+                    help="bytes read (and written) per launch of the calibration copy")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -205,6 +212,50 @@ def cpu_baseline(k, w, target_s):
                 seconds=round(dt, 2))
 
 
+def _pmc_avg(db, counter, name_prefix):
+    """Average per-dispatch value (KiB) of a counter for kernels whose name
+    starts with name_prefix (after 'void ' and the namespace)."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                     (counter,)).fetchall()
+    vals = [v for k, v in rows if k.replace("void ", "").replace("vs::", "").startswith(name_prefix)]
+    if not vals:
+        raise SystemExit(f"{db}: no {counter} samples for {name_prefix}")
+    return sum(vals) / len(vals), len(vals)
+
+
+DOMINANT = {1: "k_bmu_qreg", 2: "k_bmu_qreg", 3: "k_bmu_mfma", 4: "k_bmu_csr", 5: "k_bmu_qreg"}
+
+
+def record_traffic(a):
+    """FETCH_SIZE and WRITE_SIZE count KiB per dispatch; each is scaled by
+    what the same counter reads for a plain copy of known size."""
+    import synth
+    f_db, w_db, cf_db, cw_db = a.traffic_from
+    kernel = DOMINANT[a.workload]
+    copy_kib = a.traffic_copy_bytes / 1024.0
+    cf, _ = _pmc_avg(cf_db, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    cw, _ = _pmc_avg(cw_db, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    f, nf = _pmc_avg(f_db, "FETCH_SIZE", kernel)
+    w, nw = _pmc_avg(w_db, "WRITE_SIZE", kernel)
+    fs, ws = copy_kib / cf, copy_kib / cw
+    total = (f * fs + w * ws) * 1024.0
+    name = synth.WORKLOADS[a.workload]["name"]
+    try:
+        with open(a.traffic_json) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    table[f"{name}:{kernel}"] = {
+        "bytes_per_launch": round(total), "fetch_kib_raw": round(f, 1),
+        "write_kib_raw": round(w, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+        "dispatches": [nf, nw], "kernel_source_hash": kernel_source_hash()}
+    with open(a.traffic_json, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    print(json.dumps({name: table[f"{name}:{kernel}"]}))
+
+
 def copy_calibration(a, torch):
     """A plain copy of known size (read n bytes, write n bytes) per launch."""
     n = a.copy_bytes // 4
@@ -227,6 +278,9 @@ def copy_calibration(a, torch):
 
 def main():
     a = parse()
+    if a.traffic_from:
+        record_traffic(a)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md). Use --gpus 1.", file=sys.stderr)
@@ -275,7 +329,7 @@ def main():
     roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
-    roof["traffic"] = load_traffic(a.traffic_json, kt.name, cfg["workload"])
+    roof["traffic"] = load_traffic(a.traffic_json, DOMINANT[a.workload], cfg["workload"])
     out = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
