@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--roof", choices=["l2"], default=None,
+                    help="measure the on-chip roof of the sparse scan's access pattern "
+                         "(256-byte dword row loads from an L2-resident region per XCD)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
                                                           "COPY_WRITE_DB"),
                     help="record HBM traffic per launch of the workload's dominant kernel from "
@@ -256,6 +259,44 @@ def record_traffic(a):
     print(json.dumps({name: table[f"{name}:{kernel}"]}))
 
 
+def measure_l2_roof(a, torch):
+    """L2 -> CU read bandwidth for row segments read the way the sparse scan
+    reads the codebook: each XCD reads its own 2 MiB region (rows of 64
+    floats, padded row stride), 256-byte dword loads (and 1 KiB dwordx4 loads
+    for comparison), 16 in flight per wave, 32 waves per CU."""
+    import ctypes
+    from farthest_vector_search_amd.build import ROOF_LIB
+    L = ctypes.CDLL(ROOF_LIB)
+    L.vs_roof_l2_read.restype = ctypes.c_int64
+    L.vs_roof_l2_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    wg_per_xcd = n_cu // 8 * 8
+    out = torch.empty(8 * wg_per_xcd * 4, device="cuda:0")
+    res = {}
+    for vw, rows, ld in ((1, 8192, 64 + 16), (4, 2048, 256 + 16)):
+        buf = torch.rand(8 * rows * ld, device="cuda:0")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for passes in (256,):
+            L.vs_roof_l2_read(ctypes.c_void_p(buf.data_ptr()), rows, ld, passes, vw, wg_per_xcd,
+                              ctypes.c_void_p(out.data_ptr()), stream)  # warm the L2s
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nbytes = 0
+            for _ in range(a.steps):
+                nbytes += L.vs_roof_l2_read(ctypes.c_void_p(buf.data_ptr()), rows, ld, passes, vw,
+                                            wg_per_xcd, ctypes.c_void_p(out.data_ptr()), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            res[f"{'dword' if vw == 1 else 'dwordx4'}_rows{rows}"] = dict(
+                GBps=round(nbytes / ms / 1e6, 1), bytes_per_launch=nbytes // a.steps,
+                ms_per_launch=round(ms / a.steps, 4), region_bytes_per_xcd=rows * ld * 4)
+        del buf
+    print(json.dumps({"l2_roof": res}), flush=True)
+
+
 def copy_calibration(a, torch):
     """A plain copy of known size (read n bytes, write n bytes) per launch."""
     n = a.copy_bytes // 4
@@ -292,6 +333,9 @@ def main():
         sys.exit(1)
     if a.copy_bytes > 0:
         copy_calibration(a, torch)
+        return
+    if a.roof == "l2":
+        measure_l2_roof(a, torch)
         return
     log(f"workload {a.workload}: generating inputs")
     w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs)

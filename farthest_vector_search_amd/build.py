@@ -16,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvs.so")
+ROOF_LIB = os.path.join(HERE, "libvs_roofs.so")  # measurement kernels, not the search ABI
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "prep.hip", "bmu_mfma.hip", "bmu_qreg.hip", "bmu_csr.hip", "finalize.hip"]
@@ -41,18 +42,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, out):
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + ["roofs.hip"]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], ROOF_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {ROOF_LIB}")
     return LIB
 
 

@@ -33,12 +33,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kQW = 8;         // waves per workgroup
-constexpr int kBQ = 32 * kQW;  // queries per tile
-constexpr int kBC = 64;        // candidates per tile
-constexpr int kBK = 64;        // features per LDS slab
-constexpr int kCPS = kBK / 8;  // 8-feature chunks per slab
+#ifndef VS_QREG_BK
+#define VS_QREG_BK 64
+#endif
+#ifndef VS_QREG_PRIO
+#define VS_QREG_PRIO 0
+#endif
+
+constexpr int kQW = 8;          // waves per workgroup
+constexpr int kBQ = 32 * kQW;   // queries per tile
+constexpr int kBC = 64;         // candidates per tile
+constexpr int kBK = VS_QREG_BK; // features per LDS slab (64 or 128)
+constexpr int kCPS = kBK / 8;   // 8-feature chunks per slab
 constexpr int kPieces = kBK / 4;
+constexpr int kMaxSlabs = 256 / kBK;
+static_assert(kBK == 64 || kBK == 128, "slab width");
 
 __device__ __forceinline__ int slab_at(int row, int piece) {
     return row * kBK + ((piece ^ (row & 15)) << 2);
@@ -80,7 +89,8 @@ void k_bmu_qreg(const DenseArgs a) {
     constexpr int RPP = NT / kPieces;  // loader rows per pass (register path)
     constexpr int AP = kBC / RPP;      // loader pieces per thread (register path)
     constexpr int RPW = kBC / kQW;     // slab rows owned by each wave (DMA path)
-    static_assert(kBC % RPP == 0 && RPW % 4 == 0, "loader shape");
+    constexpr int RPI = 64 / kPieces;  // rows per DMA instruction (1 KiB)
+    static_assert(kBC % RPP == 0 && RPW % RPI == 0, "loader shape");
 
     __shared__ __attribute__((aligned(16))) float sA[2][kBC * kBK];
     __shared__ __attribute__((aligned(16))) float sN[2][kBC];  // candidate norms, by item parity
@@ -109,8 +119,8 @@ void k_bmu_qreg(const DenseArgs a) {
 
     // ---- candidate slab loader ----------------------------------------
     // VEC: direct-to-LDS.  Wave w fills rows [RPW w, RPW w + RPW); one
-    // instruction covers 4 rows x 16 slots, lane l -> row +l/16, slot l%16,
-    // which holds piece slot ^ (row % 16) of that row.  Elements outside the
+    // instruction covers RPI rows x kPieces slots, lane l -> row +l/kPieces,
+    // slot l%kPieces, which holds piece slot ^ (row % 16) of that row.  Elements outside the
     // table (rows >= nc, features >= d) are written as zeros with ds_write.
     // Scalar path: through registers, as in the tiled kernel.
     const int lrow = tid / kPieces, lpiece = tid % kPieces;
@@ -130,13 +140,13 @@ void k_bmu_qreg(const DenseArgs a) {
     auto load_slab = [&](int slab, int buf) {
         if constexpr (VEC) {
 #pragma unroll
-            for (int i = 0; i < RPW / 4; ++i) {
-                const int row = wave * RPW + 4 * i + (lane >> 4);
-                const int slot = lane & 15;
+            for (int i = 0; i < RPW / RPI; ++i) {
+                const int row = wave * RPW + RPI * i + lane / kPieces;
+                const int slot = lane % kPieces;
                 const int piece = slot ^ (row & 15);
                 const int64_t c = row_base + row;
                 const int32_t k = slab * kBK + 4 * piece;
-                float *dst = &sA[buf][(wave * RPW + 4 * i) * kBK];
+                float *dst = &sA[buf][(wave * RPW + RPI * i) * kBK];
                 if (c < nc && k < d) dma16(a.C + c * d + k, dst);
                 else *reinterpret_cast<f32x4 *>(dst + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
@@ -240,6 +250,7 @@ void k_bmu_qreg(const DenseArgs a) {
             }
             // 8 chunks of 8 features; the operands of chunk cc+1 are read
             // from LDS while the MFMAs of chunk cc run
+            if constexpr (VS_QREG_PRIO) __builtin_amdgcn_s_setprio(1);
             const float *A = sA[buf];
             f32x4 f0[2], f1[2];
             f0[0] = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, h)]);
@@ -259,6 +270,7 @@ void k_bmu_qreg(const DenseArgs a) {
                     acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], qv[e], acc[1], 0, 0, 0);
                 }
             }
+            if constexpr (VS_QREG_PRIO) __builtin_amdgcn_s_setprio(0);
             if (s == NSLAB - 1) epilogue(item, par);
             if (has_next) finish_slab(buf ^ 1);
             wait_loads();
@@ -288,15 +300,20 @@ static void dispatch_q(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) 
 template <int M>
 static void dispatch_slabs(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) {
     const int nslab = (a.d + kBK - 1) / kBK;
-    switch (nslab) {
-    case 1: dispatch_q<M, 1>(a, vec, grid, st); break;
-    case 2: dispatch_q<M, 2>(a, vec, grid, st); break;
-    case 3: dispatch_q<M, 3>(a, vec, grid, st); break;
-    default: dispatch_q<M, 4>(a, vec, grid, st); break;
+    if constexpr (kMaxSlabs == 4) {
+        switch (nslab) {
+        case 1: dispatch_q<M, 1>(a, vec, grid, st); break;
+        case 2: dispatch_q<M, 2>(a, vec, grid, st); break;
+        case 3: dispatch_q<M, 3>(a, vec, grid, st); break;
+        default: dispatch_q<M, 4>(a, vec, grid, st); break;
+        }
+    } else {
+        if (nslab == 1) dispatch_q<M, 1>(a, vec, grid, st);
+        else dispatch_q<M, 2>(a, vec, grid, st);
     }
 }
 
-bool qreg_supports(int32_t d) { return d >= 1 && d <= 4 * kBK; }
+bool qreg_supports(int32_t d) { return d >= 1 && d <= 256; }
 
 hipError_t launch_dense_qreg(const DenseArgs &a0, int metric, hipStream_t st, int n_cu) {
     DenseArgs a = a0;

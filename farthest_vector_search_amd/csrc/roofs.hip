@@ -1,0 +1,77 @@
+// roofs.hip -- measurement kernels for the on-chip roof of the sparse scan.
+//
+// Not part of the search ABI (built into libvs_roofs.so, used by bench.py's
+// --roof mode).  The sparse scan reads codebook rows as 256-byte segments
+// (64 lanes x 4 bytes) out of a slice that lives in its XCD's L2; this kernel
+// reads the same shape from an L2-resident region so that the achieved
+// L2 -> CU bandwidth of that access pattern can be quoted as the roof.
+//
+// Each XCD (workgroup group = blockIdx % 8, as the hardware deals workgroups
+// to XCDs) reads its own region of `rows` rows x 64 floats, row stride `ld`
+// floats; every wave walks the rows in a scattered order, 16 loads in flight,
+// `passes` times.  One float per wave is written so the loads are not dead.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define VS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int VW>  // floats per lane per load: 1 (dword) or 4 (dwordx4)
+__global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, int64_t rows,
+                                                int64_t ld, int32_t passes,
+                                                float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int x = blockIdx.x & 7;
+    const int64_t local = blockIdx.x >> 3;
+    const int64_t wpx = (int64_t)(gridDim.x >> 3) * 4;  // waves per XCD
+    const int64_t w = local * 4 + (threadIdx.x >> 6);
+    const float *region = buf + (int64_t)x * rows * ld;
+    float acc = 0.0f;
+    const int64_t steps = (int64_t)passes * rows / wpx;
+    const int64_t mask = rows - 1;  // rows is a power of two
+    int64_t r = (w * 9973) & mask;
+    for (int64_t t = 0; t < steps; t += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int64_t row = (r + (int64_t)u * 4099) & mask;
+            if constexpr (VW == 1) {
+                v[u] = region[row * ld + lane];
+            } else {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(region + row * ld + 4 * lane);
+                v[u] = q.x + q.y + q.z + q.w;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
+        r = (r + 16 * 4099 + 1) & mask;
+    }
+    if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
+}  // namespace
+
+// Reads rows x (64 * vw) floats per XCD region (8 regions, row stride ld
+// >= 64 * vw, rows a power of two), `passes` times over.  Returns the bytes the kernel read; the
+// caller times the launch on `stream`.  out needs grid * 4 floats, grid =
+// 8 * wg_per_xcd.
+VS_API int64_t vs_roof_l2_read(const float *buf, int64_t rows, int64_t ld, int32_t passes,
+                               int32_t vw, int32_t wg_per_xcd, float *out, void *stream) {
+    if (!buf || !out || rows < 16 || (rows & (rows - 1)) != 0 || passes < 1 || wg_per_xcd < 1 ||
+        (vw != 1 && vw != 4) || ld < 64 * vw)
+        return -1;
+    const dim3 grid((unsigned)(8 * wg_per_xcd)), block(256);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (vw == 1)
+        hipLaunchKernelGGL(k_l2_roof<1>, grid, block, 0, st, buf, rows, ld, passes, out);
+    else
+        hipLaunchKernelGGL(k_l2_roof<4>, grid, block, 0, st, buf, rows, ld, passes, out);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const int64_t waves = (int64_t)8 * wg_per_xcd * 4;
+    const int64_t steps = (int64_t)passes * rows / (waves / 8);
+    const int64_t loads_per_wave = (steps + 15) / 16 * 16;
+    return waves * loads_per_wave * 64 * 4 * vw;
+}
