@@ -69,18 +69,24 @@ def load_traffic(path, kernel, workload):
         with open(path) as f:
             t = json.load(f)
         e = t.get(f"{workload}:{kernel}")
-        if e and e.get("kernel_source_hash") == kernel_source_hash():
+        if e and e.get("kernel_source_hash") == kernel_source_hash(kernel):
             return e.get("bytes_per_launch")
     except (OSError, ValueError):
         pass
     return None
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"k_bmu_qreg": "bmu_qreg.hip", "k_bmu_mfma": "bmu_mfma.hip",
+                  "k_bmu_csr": "bmu_csr.hip"}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the kernel's source file and the shared header: a recorded
+    traffic figure is reported only while both are unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "farthest_vector_search_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in (KERNEL_SOURCES[kernel], "vs_internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -253,7 +259,7 @@ def record_traffic(a):
     table[f"{name}:{kernel}"] = {
         "bytes_per_launch": round(total), "fetch_kib_raw": round(f, 1),
         "write_kib_raw": round(w, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
-        "dispatches": [nf, nw], "kernel_source_hash": kernel_source_hash()}
+        "dispatches": [nf, nw], "kernel_source_hash": kernel_source_hash(kernel)}
     with open(a.traffic_json, "w") as fh:
         json.dump(table, fh, indent=1, sort_keys=True)
     print(json.dumps({name: table[f"{name}:{kernel}"]}))

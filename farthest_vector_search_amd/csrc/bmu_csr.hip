@@ -45,8 +45,17 @@
 
 namespace vs {
 
-constexpr int kCsrWgPerCu = 7;   // 7 x 4 waves resident per CU (VGPR-limited)
-constexpr int kCsrUnroll = 8;
+#ifndef VS_CSR_WG_PER_CU
+#define VS_CSR_WG_PER_CU 7
+#endif
+constexpr int kCsrWgPerCu = VS_CSR_WG_PER_CU;  // x 4 waves resident per CU (VGPR-limited)
+#ifndef VS_CSR_UNROLL
+#define VS_CSR_UNROLL 8
+#endif
+constexpr int kCsrUnroll = VS_CSR_UNROLL;  // loads per group (two groups in flight)
+// a batch holds 64 records and its walk is rounded up to whole groups, so a
+// group size must divide 64 or the walk would read past the batch
+static_assert(64 % kCsrUnroll == 0, "unroll must divide the 64-record batch");
 
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
@@ -135,16 +144,21 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
             c[u] = *reinterpret_cast<const __attribute__((address_space(1))) float *>(addr);
         }
     };
-    auto consume = [&](int base, const float (&c)[U], float &acc) {
+    // non-zero j of a batch (batches start at multiples of 64, groups at
+    // multiples of U) goes to partial sum j % 4, the same split the
+    // four-rows-per-load kernel uses, so every CSR path gives the same bits
+    static_assert(U % 4 == 0, "groups must start at non-zero indices = 0 mod 4");
+    auto consume = [&](int base, const float (&c)[U], float (&acc)[4]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc = __builtin_fmaf(wgt[wave][half][base + u], c[u], acc);
+        for (int u = 0; u < U; ++u)
+            acc[u & 3] = __builtin_fmaf(wgt[wave][half][base + u], c[u], acc[u & 3]);
     };
 
     if (lw * HALVES >= nq) return;
     Pair cur = open_pair(HALVES * lw);
     prefetch(cur, 0);
     while (true) {
-        float acc = 0.0f;
+        float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         Pair nxt = cur;
         bool more = false;
         for (int64_t t = 0; t < cur.L; t += 64) {
@@ -183,13 +197,14 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
             for (int u0 = 0; u0 < cnt; u0 += 2 * U) {
                 const bool two = u0 + U < cnt;
                 if (two) issue(u0 + U, c1);
-                consume(u0, c0, acc);
+                consume(u0, c0, acc4);
                 if (two) {
                     if (u0 + 2 * U < cnt) issue(u0 + 2 * U, c0);
-                    consume(u0 + U, c1, acc);
+                    consume(u0 + U, c1, acc4);
                 }
             }
         }
+        const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
         if (cur.L == 0 && cur.q0 + qstep < nq) {  // an all-empty pair prefetches nothing above
             nxt = open_pair(cur.q0 + qstep);
             more = true;
@@ -215,6 +230,170 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
         }
         if (!more) break;
         cur = nxt;
+    }
+}
+
+// Four-rows-per-load form (codebook rows 16-byte aligned, nc % 4 == 0).  A
+// wave still owns 64 neurons, but one 16-byte-per-lane load now covers four
+// non-zeros: lane group g = lane / 16 reads row k of non-zero 4i+g, lanes of
+// a group four consecutive neurons each (16 x 16 B = one 256-byte row
+// segment).  Wide loads reach about twice the L2 -> CU bandwidth of 4-byte
+// loads on gfx950, and the codebook slice per XCD stays 4 MiB.  Each lane
+// sums every fourth non-zero for its 4 neurons in order; the four partial
+// sums are combined in one fixed order ((p0 + p1) + (p2 + p3)) at the end.
+template <int M>
+__global__ __launch_bounds__(256) void k_bmu_csr_q4(const CsrArgs a, uint64_t *__restrict__ part,
+                                                   int64_t round, int32_t groups) {
+    constexpr int U = 4;  // load instructions (16 non-zeros) per group, two groups in flight
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ uint64_t rec[4][64];  // per wave: row addresses of the batch
+    __shared__ float wgt[4][64];     // ... and weights
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, col = lane & 15;
+    const int x = (int)(blockIdx.x % (unsigned)groups);
+    const int64_t local = blockIdx.x / (unsigned)groups;
+    const int64_t chunk = round * groups + x;
+    if (chunk >= a.n_chunks) return;
+    const int64_t waves_per_group = (int64_t)(gridDim.x / (unsigned)groups) * 4;
+    const int64_t lw = __builtin_amdgcn_readfirstlane((int)(local * 4 + wave));
+    const int64_t nq = a.nq, nc = a.nc, ld = a.ldct;
+    const int32_t d = a.d;
+    const int32_t n0 = (int32_t)(chunk * 64 + 4 * col);  // this lane's 4 neurons
+    const bool live = n0 < nc;                            // nc % 4 == 0: all 4 or none
+    const uint64_t off = (uint64_t)(live ? n0 : 0) * 4u;
+    f4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (metric_is_l2(M) && live) cn4 = *reinterpret_cast<const f4 *>(a.cn + n0);
+    uint64_t *mine = part + (int64_t)x * nq;
+    const uint64_t ct = reinterpret_cast<uint64_t>(a.CT);
+
+    auto issue = [&](int base, f4 (&c)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t addr = rec[wave][base + 4 * u + grp] + off;
+            c[u] = *reinterpret_cast<const __attribute__((address_space(1))) f4 *>(addr);
+        }
+    };
+    auto consume = [&](int base, const f4 (&c)[U], f4 &acc) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = wgt[wave][base + 4 * u + grp];
+            acc.x = __builtin_fmaf(w, c[u].x, acc.x);
+            acc.y = __builtin_fmaf(w, c[u].y, acc.y);
+            acc.z = __builtin_fmaf(w, c[u].z, acc.z);
+            acc.w = __builtin_fmaf(w, c[u].w, acc.w);
+        }
+    };
+
+    if (lw >= nq) return;
+    // current query's span, and the next one's (prefetched one batch ahead)
+    auto span = [&](int64_t q, int64_t &b, int64_t &len, bool &ok) {
+        b = 0;
+        len = 0;
+        ok = q < nq;
+        if (ok) {
+            const int64_t bb = a.indptr[q], ee = a.indptr[q + 1];
+            ok = bb >= 0 && ee >= bb && ee <= a.nnz;
+            if (ok) {
+                b = bb;
+                len = ee - bb;
+            }
+        }
+    };
+    int32_t pk = 0;
+    float pv = 0.0f;
+    auto prefetch = [&](int64_t b, int64_t len, int64_t t) {
+        pk = 0;
+        pv = 0.0f;
+        if (t + lane < len) {
+            pk = stream_load(a.indices + b + t + lane);
+            pv = stream_load(a.values + b + t + lane);
+        }
+    };
+
+    int64_t q = lw, b, len;
+    bool ok;
+    span(q, b, len, ok);
+    prefetch(b, len, 0);
+    while (true) {
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        int64_t nb = 0, nlen = 0;
+        bool nok = false, more = false;
+        const int64_t qn = q + waves_per_group;
+        for (int64_t t = 0; t < len; t += 64) {
+            int32_t kk = pk;
+            float vv = pv;
+            if (t + 64 < len) {
+                prefetch(b, len, t + 64);
+            } else if (qn < nq) {
+                span(qn, nb, nlen, nok);
+                more = true;
+                prefetch(nb, nlen, 0);
+            }
+            const bool bad = (uint32_t)kk >= (uint32_t)d;
+            if (__any(bad)) ok = false;
+            if (bad) {
+                kk = 0;
+                vv = 0.0f;
+            }
+            rec[wave][lane] = ct + (uint64_t)kk * (uint64_t)ld * 4u;  // past the end: row 0,
+            wgt[wave][lane] = vv;                                    // weight 0
+            const int64_t rem = len - t;
+            const int cnt = (int)((rem < 64 ? rem : 64) + 4 * U - 1) / (4 * U) * (4 * U);
+            f4 c0[U], c1[U];
+            issue(0, c0);
+            for (int u0 = 0; u0 < cnt; u0 += 8 * U) {
+                const bool two = u0 + 4 * U < cnt;
+                if (two) issue(u0 + 4 * U, c1);
+                consume(u0, c0, acc);
+                if (two) {
+                    if (u0 + 8 * U < cnt) issue(u0 + 8 * U, c0);
+                    consume(u0 + 4 * U, c1, acc);
+                }
+            }
+        }
+        if (len == 0 && qn < nq) {  // an empty row prefetches nothing above
+            span(qn, nb, nlen, nok);
+            more = true;
+            prefetch(nb, nlen, 0);
+        }
+        // combine the four lane groups' partial sums: (p0 + p1) + (p2 + p3)
+#pragma unroll
+        for (int s2 = 16; s2 <= 32; s2 <<= 1) {
+            acc.x += __shfl_xor(acc.x, s2);
+            acc.y += __shfl_xor(acc.y, s2);
+            acc.z += __shfl_xor(acc.z, s2);
+            acc.w += __shfl_xor(acc.w, s2);
+        }
+        float be = __builtin_inff();
+        int32_t bi = -1;
+        if (live && ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float r = rank_value<M>(acc[e], cn4[e]);
+                if (r < be) {
+                    be = r;
+                    bi = n0 + e;
+                }
+            }
+        }
+#pragma unroll
+        for (int s2 = 8; s2 >= 1; s2 >>= 1) {  // within a lane group (all groups agree)
+            const float oe = __shfl_xor(be, s2);
+            const int32_t oi = __shfl_xor(bi, s2);
+            if (oi >= 0 && (bi < 0 || oe < be || (oe == be && oi < bi))) {
+                be = oe;
+                bi = oi;
+            }
+        }
+        if (lane == 0 && ok && bi >= 0) {
+            const uint64_t key = pack_key(be, (uint32_t)bi);
+            if (key < mine[q]) mine[q] = key;
+        }
+        if (!more) break;
+        q = qn;
+        b = nb;
+        len = nlen;
+        ok = nok;
     }
 }
 
@@ -261,9 +440,18 @@ hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
     const int64_t rounds = (a.n_chunks + groups - 1) / groups;
     hipError_t err = launch_fill_keys(part, (int64_t)groups * a.nq, st);
     if (err != hipSuccess) return err;
+    const bool q4 = ncw == 64 && a.nc % 4 == 0 && a.ldct % 4 == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.CT) & 15) == 0 && getenv("VS_CSR_DWORD") == nullptr;
     for (int64_t r = 0; r < rounds; ++r) {
         timing_before(st, "k_bmu_csr");
-        if (ncw == 32) {
+        if (q4) {
+            switch (metric) {
+            case L2SQ_MIN: hipLaunchKernelGGL(k_bmu_csr_q4<L2SQ_MIN>, grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MAX: hipLaunchKernelGGL(k_bmu_csr_q4<L2SQ_MAX>, grid, block, 0, st, a, part, r, groups); break;
+            case COS_MAX: hipLaunchKernelGGL(k_bmu_csr_q4<COS_MAX>, grid, block, 0, st, a, part, r, groups); break;
+            default: hipLaunchKernelGGL(k_bmu_csr_q4<COS_MIN>, grid, block, 0, st, a, part, r, groups); break;
+            }
+        } else if (ncw == 32) {
             switch (metric) {
             case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MIN, 2>), grid, block, 0, st, a, part, r, groups); break;
             case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr<L2SQ_MAX, 2>), grid, block, 0, st, a, part, r, groups); break;

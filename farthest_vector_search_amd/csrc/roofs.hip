@@ -27,8 +27,8 @@ __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, 
     const int x = blockIdx.x & 7;
     const int64_t local = blockIdx.x >> 3;
     const int64_t wpx = (int64_t)(gridDim.x >> 3) * 4;  // waves per XCD
-    const int64_t w = local * 4 + (threadIdx.x >> 6);
-    const float *region = buf + (int64_t)x * rows * ld;
+    const int64_t w = __builtin_amdgcn_readfirstlane((int)(local * 4 + (threadIdx.x >> 6)));
+    const float *region = buf + (int64_t)x * rows * ld + lane * VW;  // this lane's column
     float acc = 0.0f;
     const int64_t steps = (int64_t)passes * rows / wpx;
     const int64_t mask = rows - 1;  // rows is a power of two
@@ -39,9 +39,9 @@ __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, 
         for (int u = 0; u < 16; ++u) {
             const int64_t row = (r + (int64_t)u * 4099) & mask;
             if constexpr (VW == 1) {
-                v[u] = region[row * ld + lane];
+                v[u] = region[row * ld];
             } else {
-                const f32x4 q = *reinterpret_cast<const f32x4 *>(region + row * ld + 4 * lane);
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(region + row * ld);
                 v[u] = q.x + q.y + q.z + q.w;
             }
         }

@@ -245,6 +245,23 @@ def test_csr_row_stride(pad, chunk):
     csr_parity(indptr, indices, values, CT, 0)
 
 
+@pytest.mark.parametrize("metric", [0, 2])
+def test_csr_paths_agree_bitwise(metric, monkeypatch):
+    """The four-rows-per-load kernel and the 4-byte-load kernels (one or two
+    queries per wave) sum in the same order, so they agree bit for bit."""
+    indptr, indices, values, CT = csr_case(150, 300, 1030 - 1030 % 4, 0.06, key=66 + metric)
+    outs = []
+    for env in ({"VS_CSR_CHUNK": "64"}, {"VS_CSR_CHUNK": "64", "VS_CSR_DWORD": "1"},
+                {"VS_CSR_CHUNK": "32"}):
+        monkeypatch.delenv("VS_CSR_DWORD", raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        outs.append(run_csr(indptr, indices, values, CT, metric))
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0])
+        assert np.array_equal(o[1].view(np.uint32), outs[0][1].view(np.uint32))
+
+
 def csr_select(indptr, indices, values, rows):
     rows = np.asarray(rows)
     ptr = np.concatenate([[0], np.cumsum(indptr[rows + 1] - indptr[rows])]).astype(np.int32)
