@@ -78,13 +78,26 @@ Layout search_layout(int64_t nq, int64_t nc, int32_t metric) {
     return L;
 }
 
-// Dense kernel choice: queries in registers when d allows it (default), the
-// LDS-tiled kernel otherwise.  VS_DENSE_KERNEL=tiled|qreg overrides the
-// choice (both give identical results; used to test and compare them).
-bool use_qreg_kernel(int32_t d) {
+// Dense kernel choice: 32 queries per wave in registers for d <= 256, 16 per
+// wave for d <= 768 (d % 4 == 0, 16-byte aligned rows), the LDS-tiled kernel
+// otherwise.  VS_DENSE_KERNEL=qreg|q16|tiled forces one where it applies
+// (all give results within the same bound; qreg and tiled are bit-identical).
+enum class DenseKernel { QREG, Q16, TILED };
+DenseKernel dense_kernel(int32_t d, const float *C, const float *Q) {
     const char *env = std::getenv("VS_DENSE_KERNEL");
+    const bool q32 = vs::qreg_supports(d), q16 = vs::q16_supports(d, C, Q);
+    if (env && std::strcmp(env, "tiled") == 0) return DenseKernel::TILED;
+    if (env && std::strcmp(env, "q16") == 0 && q16) return DenseKernel::Q16;
+    if (q32) return DenseKernel::QREG;
+    return q16 ? DenseKernel::Q16 : DenseKernel::TILED;
+}
+
+// Diversity step: the 16-query kernel where it applies, the tiled kernel
+// otherwise or when VS_DIV_KERNEL=tiled.
+bool div_use_q16(int32_t d, const float *C) {
+    const char *env = std::getenv("VS_DIV_KERNEL");
     if (env && std::strcmp(env, "tiled") == 0) return false;
-    return vs::qreg_supports(d);
+    return vs::q16_supports(d, C, nullptr);
 }
 
 #define VS_TRY_HIP(expr)                   \
@@ -201,8 +214,11 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     a.nq = nq;
     a.nc = nc;
     a.d = d;
-    if (use_qreg_kernel(d)) VS_TRY_HIP(vs::launch_dense_qreg(a, metric, st, n_cu));
-    else VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu));
+    switch (dense_kernel(d, C, Q)) {
+    case DenseKernel::QREG: VS_TRY_HIP(vs::launch_dense_qreg(a, metric, st, n_cu)); break;
+    case DenseKernel::Q16: VS_TRY_HIP(vs::launch_dense_q16(a, metric, false, st, n_cu)); break;
+    default: VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu)); break;
+    }
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
 }
@@ -313,7 +329,8 @@ VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t
     a.nc = n;
     a.d = d;
     a.mask_words = W;
-    VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, true, st, n_cu));
+    if (div_use_q16(d, C)) VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, true, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, true, st, n_cu));
     VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
     return VS_OK;
 }

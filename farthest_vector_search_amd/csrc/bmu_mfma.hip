@@ -29,8 +29,8 @@
 //    x 128 candidates per work item, each wave a 2x2 grid of 32x32 MFMA
 //    blocks.  K runs in slabs of 32 features through double-buffered LDS
 //    (64 KiB), one barrier per slab.  Each LDS row is 8 pieces of 16 bytes
-//    stored at slot (piece XOR row%8): loads stay 128-byte coalesced and the
-//    16-byte LDS reads of the MFMA operands hit distinct banks.
+//    stored at slot (piece XOR (row/2)%8): loads stay 128-byte coalesced and
+//    the 16-byte LDS reads of the MFMA operands hit distinct banks.
 //  - Operand order inside K: lane half h feeds features {8c+4h .. 8c+4h+3}
 //    of chunk c, one per MFMA, from one 16-byte LDS read; both operands use
 //    the same map, so every pair's sum runs over the same fixed sequence of
@@ -53,8 +53,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 32;  // features per slab = 8 pieces of 4 floats
 
+// LDS banks are 64 x 4 bytes, so a 128-byte row covers half of them and rows
+// r and r+1 fall on opposite halves: the slot key uses row/2 so that the 16
+// rows one 16-lane group reads at a time land on 16 distinct bank groups.
 __device__ __forceinline__ int lds_at(int row, int piece) {
-    return row * kBK + ((piece ^ (row & 7)) << 2);
+    return row * kBK + ((piece ^ ((row >> 1) & 7)) << 2);
 }
 
 template <bool VEC>

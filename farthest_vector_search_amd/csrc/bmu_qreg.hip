@@ -70,17 +70,6 @@ __device__ __forceinline__ f32x4 ld4(const float *p, int32_t k, int32_t d) {
 
 }  // namespace
 
-// LDS-DMA (global_load_lds, 16 bytes per lane): lane l of the issuing wave
-// writes LDS bytes [base + 16 l, base + 16 l + 16).
-__device__ __forceinline__ void dma16(const float *g, float *lds_base) {
-    __builtin_amdgcn_global_load_lds(
-        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const float *g, float *lds_base) {
-    __builtin_amdgcn_global_load_lds(
-        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
-}
-
 template <int M, bool VEC, int NSLAB>
 __global__ __launch_bounds__(64 * kQW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_qreg(const DenseArgs a) {

@@ -49,6 +49,18 @@ __device__ __forceinline__ float rank_value(float s, float cn) {
     else return s;
 }
 
+// LDS-DMA (global_load_lds): lane l of the issuing wave writes LDS bytes
+// [base + w l, base + w l + w), w = 16 or 4 bytes; lanes that are switched
+// off write nothing.
+__device__ __forceinline__ void dma16(const float *g, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const float *g, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+}
+
 // ---------------------------------------------------------------- kernels --
 
 struct DenseArgs {
@@ -64,6 +76,7 @@ struct DenseArgs {
     int64_t n_items;        // query tiles x candidate tiles
     int64_t n_ctiles;
     int32_t grid;           // launched workgroups (for the item split)
+    int32_t split;          // 1, or 8: candidate tiles split into one range per XCD
 };
 
 struct CsrArgs {
@@ -91,6 +104,11 @@ hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t
 // Queries-in-registers variant of the dense scan (d <= 256, no gather).
 bool qreg_supports(int32_t d);
 hipError_t launch_dense_qreg(const DenseArgs &a, int metric, hipStream_t st, int n_cu);
+// 16-queries-per-wave variant (d <= 768, d % 4 == 0, 16-byte aligned rows);
+// also runs the gathered, masked diversity step.
+bool q16_supports(int32_t d, const float *C, const float *Q);
+hipError_t launch_dense_q16(const DenseArgs &a, int metric, bool gather, hipStream_t st,
+                            int n_cu);
 // CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
 int32_t csr_groups(int64_t nc);
 hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);

@@ -23,10 +23,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.fixture(params=["qreg", "tiled"])
+@pytest.fixture(params=["qreg", "q16", "tiled"])
 def kernel(request, monkeypatch):
-    """Run the test with each dense kernel (queries in registers for d <= 256,
-    the LDS-tiled kernel for any d); both must satisfy the same bar."""
+    """Run the test with each dense kernel: 32 queries per wave in registers
+    (d <= 256), 16 per wave (d <= 768, d % 4 == 0, aligned rows), the
+    LDS-tiled kernel (any d); a kernel that does not apply to a case hands it
+    to the next one.  All must satisfy the same bar."""
     monkeypatch.setenv("VS_DENSE_KERNEL", request.param)
     return request.param
 
@@ -68,7 +70,8 @@ def test_hand_cases(case):
     assert abs(score[0] - case["expect_value"]) <= 1e-6
 
 
-D_VALUES = [1, 3, 4, 5, 31, 32, 33, 64, 65, 255, 256, 257, 768, 769]
+D_VALUES = [1, 3, 4, 5, 31, 32, 33, 64, 65, 124, 192, 255, 256, 257, 260, 384, 452, 512,
+            600, 640, 700, 764, 768, 769]
 
 
 @pytest.mark.parametrize("d", D_VALUES)
@@ -126,6 +129,23 @@ def test_self_match_and_integer_ties(kernel):
     o_idx, o_val, _ = oracle.dense(Q, C, 0)
     assert np.array_equal(idx, o_idx)
     assert np.array_equal(score.astype(np.float64), o_val)
+
+
+@pytest.mark.parametrize("d", [64, 384, 768])
+@pytest.mark.parametrize("metric", [0, 3])
+def test_candidate_ranges_per_xcd(d, metric, monkeypatch):
+    """Fewer queries than candidates and a full grid: the 16-query kernel
+    splits the candidate tiles into one range per XCD.  Each pair's dot
+    product has one fixed feature order and the merge is exact, so the rows
+    also come out bit-identical from a launch too small to split."""
+    monkeypatch.setenv("VS_DENSE_KERNEL", "q16")
+    dist = "unit" if metric == 3 else "normal"
+    Q, C = synth.dense_case(300, 3000, d, dist, key=600 + d + metric)
+    assert_parity(Q, C, metric, threads=16)
+    full = run_dense(Q, C, metric)
+    part = run_dense(Q[:7], C, metric)
+    assert np.array_equal(full[0][:7], part[0])
+    assert np.array_equal(full[1][:7].view(np.uint32), part[1].view(np.uint32))
 
 
 def test_determinism(kernel):

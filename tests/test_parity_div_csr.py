@@ -91,6 +91,15 @@ def validate_chain(C, seeds, picks, scores, masks, threads=8):
     return fails, stats
 
 
+@pytest.fixture(params=["q16", "tiled"])
+def div_kernel(request, monkeypatch):
+    """Run a diversity test with each kernel that implements the step: 16
+    sequences per wave in registers (d <= 768, d % 4 == 0) and the LDS-tiled
+    kernel (any d)."""
+    monkeypatch.setenv("VS_DIV_KERNEL", request.param)
+    return request.param
+
+
 def test_diversity_walk():
     w = diversity_walk()
     picks, scores, masks = gpu_chain(w["C"], [w["seed"]], len(w["picks"]))
@@ -100,8 +109,10 @@ def test_diversity_walk():
 
 
 @pytest.mark.parametrize("n,d,nseq,steps", [(40, 3, 5, 41), (300, 64, 129, 20),
-                                            (1000, 65, 300, 12), (129, 768, 70, 6)])
-def test_diversity_chain(n, d, nseq, steps):
+                                            (1000, 65, 300, 12), (129, 768, 70, 6),
+                                            (3000, 128, 300, 4), (2000, 768, 260, 3),
+                                            (700, 500, 520, 5)])
+def test_diversity_chain(n, d, nseq, steps, div_kernel):
     C = synth.dense_case(1, n, d, "unit", key=n + d)[1]
     (r,) = synth.rng_children(900 + n, 1)
     seeds = r.choice(n, nseq, replace=nseq > n).astype(np.int32)
@@ -110,7 +121,7 @@ def test_diversity_chain(n, d, nseq, steps):
     assert not fails, fails
 
 
-def test_diversity_matches_direct_run():
+def test_diversity_matches_direct_run(div_kernel):
     """Tie-free small case: the GPU chain equals the oracle's own greedy run."""
     C = synth.dense_case(1, 500, 32, "unit", key=4242)[1]
     seeds = np.arange(0, 500, 7, dtype=np.int32)
@@ -120,7 +131,7 @@ def test_diversity_matches_direct_run():
     assert np.allclose(scores, o_vals, rtol=1e-4, atol=1e-6)
 
 
-def test_diversity_invalid_reference():
+def test_diversity_invalid_reference(div_kernel):
     """A reference outside [0, n) yields -1 and leaves the mask alone."""
     C = synth.dense_case(1, 100, 8, "unit", key=3)[1]
     Cd = T(C)
