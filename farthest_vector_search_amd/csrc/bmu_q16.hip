@@ -69,24 +69,6 @@ __device__ __forceinline__ int slab_at(int row, int piece) {
     return row * kBK + ((piece ^ (row & 15)) << 2);
 }
 
-// s_waitcnt vmcnt(n) for the counts the slab pipeline needs (0 .. 4)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which waits
-// for every outstanding load, including slab loads meant to stay in
-// flight); the waits that make LDS data visible are explicit at each use.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 }  // namespace
 
 template <int M, bool GATHER, int NSLAB>

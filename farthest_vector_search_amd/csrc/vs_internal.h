@@ -61,6 +61,25 @@ __device__ __forceinline__ void dma4(const float *g, float *lds_base) {
         (const void *)g, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
 }
 
+// s_waitcnt vmcnt(n) for the small counts the slab pipelines need (0 .. 4).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (the fence
+// waits for every outstanding load, including slab loads meant to stay in
+// flight across the barrier); callers make the LDS data they need visible
+// with explicit waits before it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- kernels --
 
 struct DenseArgs {
