@@ -31,10 +31,11 @@ if ROOT not in sys.path:
 METRIC = "query×candidate distance pairs/sec (BMU search) + % of fp32 MFMA/HBM roof"
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-# L2 -> CU read bandwidth of the whole chip for 16-byte-per-lane loads from an
-# L2-resident region per XCD, measured with `bench.py --roof l2` (kernel in
-# csrc/roofs.hip); the sparse scan is served from L2, so this is its roof
-PEAK_L2_WIDE_GBS = 28568.6
+# L2 -> CU read bandwidth of the whole chip in the sparse kernel's own access
+# shape (four 256-byte row segments per 16-byte-per-lane load, a 4 MiB slice
+# per XCD), measured with `bench.py --roof l2` (kernel in csrc/roofs.hip);
+# the sparse scan is served from L2, so this is its roof
+PEAK_L2_WIDE_GBS = 28029.5
 
 
 def parse():
@@ -44,6 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--csr-layout", choices=["blocked", "plain"], default="blocked",
+                    help="sparse workload: 'blocked' times the 64-neuron blocked copy of the "
+                         "codebook plus the search over it, 'plain' the search over the "
+                         "row-padded feature-major codebook")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -99,7 +104,7 @@ def kernel_source_hash(kernel):
 
 # ------------------------------------------------------------ workloads --
 
-def setup(k, torch, vs):
+def setup(k, torch, vs, a):
     import numpy as np
     import synth
     dev = torch.device("cuda:0")
@@ -158,14 +163,25 @@ def setup(k, torch, vs):
     ws = torch.empty(vs.lib().vs_bmu_search_csr_workspace(nq, nc, w["d"], 0), dtype=torch.uint8,
                      device=dev)
 
-    def step():
-        vs.vs_bmu_search_csr(indptr, indices, values, CT, 0, idx_out=idx, score_out=score,
-                             workspace=ws)
+    if a.csr_layout == "plain":
+        def step():
+            vs.vs_bmu_search_csr(indptr, indices, values, CT, 0, idx_out=idx, score_out=score,
+                                 workspace=ws)
+    else:
+        # each step re-blocks the feature-major codebook (as a caller holding
+        # it feature-major would) and searches the blocked copy
+        CB = torch.empty(vs.lib().vs_csr_blocked_bytes(nc, w["d"]) // 4, dtype=torch.float32,
+                         device=dev)
+
+        def step():
+            vs.vs_csr_block_codebook(CT, out=CB)
+            vs.vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, 0, d=w["d"],
+                                         idx_out=idx, score_out=score, workspace=ws)
     pairs = nq * nc
     w["nnz"] = int(w["indices"].shape[0])
     flops = 2.0 * w["nnz"] * nc
     cfg = dict(workload=w["name"], nq=nq, nc=nc, d=w["d"], nnz=w["nnz"], metric="l2sq_min",
-               codebook_row_stride=nc + 64)
+               codebook_row_stride=nc + 64, codebook_layout=a.csr_layout)
     chunks = (nc + 63) // 64
     rounds = (chunks + min(8, chunks) - 1) // min(8, chunks)  # one scan launch per round
     return w, step, pairs, flops, rounds, cfg
@@ -271,38 +287,45 @@ def record_traffic(a):
 
 def measure_l2_roof(a, torch):
     """L2 -> CU read bandwidth for row segments read the way the sparse scan
-    reads the codebook: each XCD reads its own 2 MiB region (rows of 64
-    floats, padded row stride), 256-byte dword loads (and 1 KiB dwordx4 loads
-    for comparison), 16 in flight per wave, 32 waves per CU."""
+    reads the codebook: each XCD reads its own 4 MiB region, 16 loads in
+    flight per wave, 16 waves per CU, in three shapes:
+    one 256-byte row per 4-byte-per-lane load, four 256-byte rows per
+    16-byte-per-lane load (the shape of the sparse kernel), and one 1 KiB row
+    per 16-byte-per-lane load."""
     import ctypes
     from farthest_vector_search_amd.build import ROOF_LIB
     L = ctypes.CDLL(ROOF_LIB)
     L.vs_roof_l2_read.restype = ctypes.c_int64
     L.vs_roof_l2_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    wg_per_xcd = n_cu // 8 * 8
+    wg_per_xcd = n_cu // 8 * 4
     out = torch.empty(8 * wg_per_xcd * 4, device="cuda:0")
     res = {}
-    for vw, rows, ld in ((1, 8192, 64 + 16), (4, 2048, 256 + 16)):
+    # 4 MiB per XCD in every shape, the size of one 64-neuron slice of the
+    # 16,384-feature codebook in the blocked layout (256-byte rows, no gaps)
+    shapes = (("dword_256B", 1, 1, 16384, 64), ("dwordx4_4x256B", 4, 4, 16384, 64),
+              ("dwordx4_1KiB", 4, 1, 4096, 256))
+    for name, vw, rpi, rows, ld in shapes:
         buf = torch.rand(8 * rows * ld, device="cuda:0")
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for passes in (256,):
-            L.vs_roof_l2_read(ctypes.c_void_p(buf.data_ptr()), rows, ld, passes, vw, wg_per_xcd,
-                              ctypes.c_void_p(out.data_ptr()), stream)  # warm the L2s
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            nbytes = 0
-            for _ in range(a.steps):
-                nbytes += L.vs_roof_l2_read(ctypes.c_void_p(buf.data_ptr()), rows, ld, passes, vw,
-                                            wg_per_xcd, ctypes.c_void_p(out.data_ptr()), stream)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            res[f"{'dword' if vw == 1 else 'dwordx4'}_rows{rows}"] = dict(
-                GBps=round(nbytes / ms / 1e6, 1), bytes_per_launch=nbytes // a.steps,
-                ms_per_launch=round(ms / a.steps, 4), region_bytes_per_xcd=rows * ld * 4)
+        passes = 64
+        args = (ctypes.c_void_p(buf.data_ptr()), rows, ld, passes, vw, rpi, wg_per_xcd,
+                ctypes.c_void_p(out.data_ptr()), stream)
+        L.vs_roof_l2_read(*args)  # warm the L2s
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nbytes = 0
+        for _ in range(a.steps):
+            nbytes += L.vs_roof_l2_read(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        res[name] = dict(GBps=round(nbytes / ms / 1e6, 1), bytes_per_launch=nbytes // a.steps,
+                         ms_per_launch=round(ms / a.steps, 4),
+                         region_bytes_per_xcd=rows * ld * 4)
         del buf
     print(json.dumps({"l2_roof": res}), flush=True)
 
@@ -348,7 +371,7 @@ def main():
         measure_l2_roof(a, torch)
         return
     log(f"workload {a.workload}: generating inputs")
-    w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs)
+    w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs, a)
     torch.cuda.synchronize()
     log(f"warmup {a.warmup} steps")
     for _ in range(a.warmup):
@@ -380,7 +403,7 @@ def main():
         achieved = 4.0 * w["nnz"] * w["nc"] * a.steps / kernel_s_total / 1e9
         roof = dict(bound="l2", achieved=round(achieved, 1), peak=PEAK_L2_WIDE_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_L2_WIDE_GBS, 4),
-                    peak_source="measured: bench.py --roof l2, 16-byte loads")
+                    peak_source="measured: bench.py --roof l2, dwordx4_4x256B")
     roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)

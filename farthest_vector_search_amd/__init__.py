@@ -9,6 +9,8 @@ calls raise.
 Functions (same names as the C entry points):
     vs_bmu_search(Q, C, metric)                        -> (idx, score)
     vs_bmu_search_csr(indptr, indices, values, CT, metric) -> (idx, score)
+    vs_csr_block_codebook(CT)                          -> CB (64-neuron blocked copy)
+    vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric) -> (idx, score)
     vs_diversity_step(C, last_pick, mask_bits)         -> (idx, score)
     vs_candidate_norms(C, feature_major=False)         -> norms
     vs_tile_rows(cache_bytes, d, bytes_per_value)      -> int (host only)
@@ -30,7 +32,8 @@ STATUS = {0: "VS_OK", 1: "VS_ERR_NULL", 2: "VS_ERR_SHAPE", 3: "VS_ERR_METRIC",
           7: "VS_ERR_UNSUPPORTED", 8: "VS_ERR_HIP"}
 
 EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_csr_workspace",
-           "vs_bmu_search_csr", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
+           "vs_bmu_search_csr_blocked", "vs_diversity_step_workspace", "vs_diversity_step",
            "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
            "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
 
@@ -63,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.vs_bmu_search_csr_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_csr_workspace.restype = SZ
     L.vs_bmu_search_csr.argtypes = [P, P, P, I64, I64, P, I64, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_csr_blocked_bytes.argtypes = [I64, I32]
+    L.vs_csr_blocked_bytes.restype = SZ
+    L.vs_csr_block_codebook.argtypes = [P, I64, I64, I32, P, P]
+    L.vs_bmu_search_csr_blocked.argtypes = [P, P, P, I64, I64, P, I64, I32, I32, P, P, P, SZ, P]
     L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
     L.vs_diversity_step_workspace.restype = SZ
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
@@ -75,7 +82,8 @@ def lib() -> ctypes.CDLL:
     L.vs_status_str.argtypes = [ctypes.c_int]
     L.vs_status_str.restype = ctypes.c_char_p
     L.vs_version.restype = ctypes.c_char_p
-    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_diversity_step",
+    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_csr_block_codebook",
+                 "vs_bmu_search_csr_blocked", "vs_diversity_step",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
         getattr(L, name).restype = ctypes.c_int
@@ -191,6 +199,65 @@ def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=N
                                  _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search_csr")
+    return idx_out, score_out
+
+
+def vs_csr_block_codebook(CT, out=None):
+    """64-neuron blocked copy of a feature-major codebook CT (d x nc, unit
+    column stride, any row stride): a flat float32 tensor holding, for every
+    block b, the d x 64 matrix of neurons 64 b .. 64 b + 63 (zeros past nc)."""
+    torch = _torch()
+    L = lib()
+    if not isinstance(CT, torch.Tensor) or not CT.is_cuda or CT.dtype != torch.float32 \
+            or CT.dim() != 2 or CT.stride(1) != 1 or CT.stride(0) < CT.shape[1]:
+        raise ValueError("CT must be a float32 CUDA matrix with unit column stride")
+    d, nc = CT.shape
+    n = L.vs_csr_blocked_bytes(nc, d) // 4
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=CT.device)
+    elif out.numel() < n or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor of at least {n} values")
+    with torch.cuda.device(CT.device):
+        rc = L.vs_csr_block_codebook(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
+                                     _stream(CT.device))
+    _check(rc, "vs_csr_block_codebook")
+    return out
+
+
+def vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric=VS_L2SQ_MIN, d=None,
+                              idx_out=None, score_out=None, workspace=None,
+                              want_score: bool = True):
+    """vs_bmu_search_csr over a codebook in the 64-neuron blocked layout that
+    vs_csr_block_codebook writes (nc neurons, d features)."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(indptr, "indptr", torch.int32, 1)
+    _dev(indices, "indices", torch.int32, 1)
+    _dev(values, "values", torch.float32, 1)
+    _dev(CB, "CB", torch.float32, 1)
+    nq = indptr.numel() - 1
+    nnz = indices.numel()
+    if values.numel() != nnz:
+        raise ValueError("indices and values differ in length")
+    nblk = (nc + 63) // 64
+    if d is None:
+        d = CB.numel() // (nblk * 64)
+    if CB.numel() < nblk * 64 * d:
+        raise ValueError("CB is smaller than the blocked layout of nc x d")
+    dev = CB.device
+    if idx_out is None:
+        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search_csr_blocked(_ptr(indptr), _ptr(indices) if nnz else None,
+                                         _ptr(values) if nnz else None, nq, nnz, _ptr(CB), nc,
+                                         d, m, _ptr(idx_out), _ptr(score_out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_bmu_search_csr_blocked")
     return idx_out, score_out
 
 

@@ -245,14 +245,13 @@ VS_API size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int
     return csr_layout(nq, nc).total;
 }
 
-VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
-                             int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ldct,
-                             int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
-                             void *workspace, size_t workspace_bytes, void *stream) {
-    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
-    if (nq < 0 || nq > kMaxIndex || nnz < 0 || nnz > kMaxIndex || nc < 1 || nc > kMaxIndex ||
-        ldct < nc || d < 1 || d > kMaxIndex)
-        return VS_ERR_SHAPE;
+// Shared by both codebook layouts: feature k of neuron 64 b + j at
+// CT + b * cstride bytes + (k * ld + j) floats (the column norms read the
+// same layout).
+static int csr_search(const int32_t *indptr, const int32_t *indices, const float *values,
+                      int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ld,
+                      int64_t cstride, int32_t d, int32_t metric, int32_t *idx_out,
+                      float *score_out, void *workspace, size_t workspace_bytes, void *stream) {
     if (nq == 0) return VS_OK;
     if (!indptr || !CT || !idx_out || !workspace || (nnz > 0 && (!indices || !values)))
         return VS_ERR_NULL;
@@ -271,7 +270,8 @@ VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, cons
     float *cn = reinterpret_cast<float *>(ws + L.cn);
     uint64_t *part = reinterpret_cast<uint64_t *>(ws + L.part);
 
-    if (vs::metric_is_l2(metric)) VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, ldct, d, cn, st));
+    if (vs::metric_is_l2(metric))
+        VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, ld, cstride / 4, d, cn, st));
     if (vs::metric_is_l2(metric) && score_out)
         VS_TRY_HIP(vs::launch_csr_row_sqnorms(indptr, values, nq, nnz, qn, st));
 
@@ -285,11 +285,54 @@ VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, cons
     a.nq = nq;
     a.nnz = nnz;
     a.nc = nc;
-    a.ldct = ldct;
+    a.ldct = ld;
+    a.cstride = cstride;
     a.d = d;
     VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu, part));
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
+}
+
+static bool csr_shape_ok(int64_t nq, int64_t nnz, int64_t nc, int32_t d) {
+    return !(nq < 0 || nq > kMaxIndex || nnz < 0 || nnz > kMaxIndex || nc < 1 ||
+             nc > kMaxIndex || d < 1 || d > kMaxIndex);
+}
+
+VS_API int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                             int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ldct,
+                             int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (!csr_shape_ok(nq, nnz, nc, d) || ldct < nc) return VS_ERR_SHAPE;
+    return csr_search(indptr, indices, values, nq, nnz, CT, nc, ldct, 256, d, metric, idx_out,
+                      score_out, workspace, workspace_bytes, stream);
+}
+
+VS_API size_t vs_csr_blocked_bytes(int64_t nc, int32_t d) {
+    if (nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxIndex) return 0;
+    return (size_t)((nc + 63) / 64) * 64u * (size_t)d * 4u;
+}
+
+VS_API int vs_csr_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
+                                 void *stream) {
+    if (nc < 1 || nc > kMaxIndex || ldct < nc || d < 1 || d > kMaxIndex) return VS_ERR_SHAPE;
+    if (!CT || !CB) return VS_ERR_NULL;
+    if (!al4(CT) || !al4(CB)) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_block_codebook(CT, nc, ldct, d, CB, reinterpret_cast<hipStream_t>(stream)));
+    return VS_OK;
+}
+
+VS_API int vs_bmu_search_csr_blocked(const int32_t *indptr, const int32_t *indices,
+                                     const float *values, int64_t nq, int64_t nnz,
+                                     const float *CB, int64_t nc, int32_t d, int32_t metric,
+                                     int32_t *idx_out, float *score_out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (!csr_shape_ok(nq, nnz, nc, d)) return VS_ERR_SHAPE;
+    return csr_search(indptr, indices, values, nq, nnz, CB, nc, 64, (int64_t)d * 256, d, metric,
+                      idx_out, score_out, workspace, workspace_bytes, stream);
 }
 
 // ---- diversity step ------------------------------------------------------
@@ -346,7 +389,7 @@ VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t fea
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (feature_major) VS_TRY_HIP(vs::launch_col_sqnorms(C, nc, nc, d, norms_out, st));
+    if (feature_major) VS_TRY_HIP(vs::launch_col_sqnorms(C, nc, nc, 64, d, norms_out, st));
     else VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, norms_out, st));
     return VS_OK;
 }

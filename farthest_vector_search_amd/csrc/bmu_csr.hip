@@ -10,19 +10,16 @@
 //
 // For a query with non-zeros (k, v) the dot product with neuron n is
 // sum v * CT[k][n].  Feature-major storage makes the neurons of one feature
-// contiguous, so a half-wave that owns 32 consecutive neurons (one per lane)
-// reads the codebook row segment of each non-zero with one coalesced
-// 128-byte load; the two halves of a wave serve two queries.  On this data a codebook value is needed by ~1.3 of the
-// queries that share a tile, so reuse comes from the cache, not from LDS or
-// registers: the kernel is bound by on-chip (L2) bandwidth at 4 bytes per
-// multiply-add, and the design goal is that those bytes are L2 hits.
+// contiguous, so the lanes that own consecutive neurons read the codebook
+// row segment of each non-zero with one coalesced load.  On this data a
+// codebook value is needed by ~1.3 of the queries that share a tile, so
+// reuse comes from the cache, not from LDS or registers: the kernel is bound
+// by on-chip (L2) bandwidth at 4 bytes per multiply-add, and the design goal
+// is that those bytes are L2 hits that arrive with enough loads in flight.
 //
-// Neuron-axis chunking, gfx950 style: the slice of the codebook for 32
-// neurons is d x 128 bytes (2 MiB at d = 16,384), half of one XCD's L2; the
-// CSR arrays, read once per round, are loaded non-temporally so that they do
-// not evict it.  A codebook row stride that is a multiple of a large power of
-// two maps every row's slice onto the same few L2 sets, so the row stride
-// (ldct) is a parameter and callers can pad it.  Each launch
+// Neuron-axis chunking, gfx950 style: a wave owns a chunk of 64 neurons (32
+// in the two-queries-per-wave variant); the codebook slice of a 64-neuron
+// chunk is d x 256 bytes (4 MiB at d = 16,384), one XCD's L2.  Each launch
 // is one "round": P <= 8 groups of workgroups, group x = blockIdx % P (the
 // hardware deals consecutive workgroups to the eight XCDs in turn, so with
 // P = 8 a group is one XCD) works on chunk round*P + x, its waves splitting
@@ -32,13 +29,22 @@
 // "Intended Behavior", proposes), instead of letting waves drift across
 // chunks and thrash the L2.
 //
+// Codebook addressing: feature k of neuron 64 b + j is at CT + b * cstride
+// bytes + (k * ldct + j) floats.  For the plain feature-major layout
+// cstride = 256 and the row stride ldct is a parameter (a stride that is a
+// multiple of a large power of two maps every row's slice onto the same few
+// L2 sets, so callers can pad it); a slice is then d segments spread over the
+// whole array, one address-translation entry each.  The 64-neuron blocked
+// layout (ldct = 64, cstride = d * 256) makes each slice contiguous.
+//
 // Merge: the wave that owns (group x, query q) is the only writer of
 // partial[x][q] in its round, and rounds are ordered on the stream, so the
-// running best per (group, query) is a plain read-min-write; a final pass
-// takes the minimum over the P groups.  Packed (value, index) keys make both
-// minima exact and order-independent (lowest index on ties).
-// Rows with an out-of-range indptr span or column index are skipped whole
-// (nothing outside the arrays is read) and keep the "no candidate" key.
+// running best per (group, query) is a read-min-write (an atomicMin in the
+// pipelined kernel); a final pass takes the minimum over the P groups.
+// Packed (value, index) keys make both minima exact and order-independent
+// (lowest index on ties).  Rows with an out-of-range indptr span or column
+// index are skipped whole (nothing outside the arrays is read) and keep the
+// "no candidate" key.
 #include <cstdlib>
 
 #include "vs_internal.h"
@@ -53,6 +59,11 @@ constexpr int kCsrWgPerCu = VS_CSR_WG_PER_CU;  // x 4 waves resident per CU (VGP
 #define VS_CSR_UNROLL 8
 #endif
 constexpr int kCsrUnroll = VS_CSR_UNROLL;  // loads per group (two groups in flight)
+#ifndef VS_CSR_RING
+#define VS_CSR_RING 16
+#endif
+
+constexpr int kCsrRing = VS_CSR_RING;  // loads in flight per wave in the pipelined scan
 // a batch holds 64 records and its walk is rounded up to whole groups, so a
 // group size must divide 64 or the walk would read past the batch
 static_assert(64 % kCsrUnroll == 0, "unroll must divide the 64-record batch");
@@ -90,10 +101,14 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
     const int32_t d = a.d;
     const int32_t n = (int32_t)(chunk * NCW + sub);
     const bool live = n < nc;
-    const uint64_t off = (uint64_t)(live ? n : 0) * 4u;  // dead lanes read column 0
+    // the chunk's first neuron inside its 64-neuron block; dead lanes read
+    // the chunk's first column
+    const int64_t n_first = chunk * NCW;
+    const uint64_t cbase = reinterpret_cast<uint64_t>(a.CT) + (uint64_t)(n_first >> 6) * a.cstride +
+                           (uint64_t)(n_first & 63) * 4u;
+    const uint64_t off = (uint64_t)(live ? sub : 0) * 4u;
     const float cn = (metric_is_l2(M) && live) ? a.cn[n] : 0.0f;
     uint64_t *mine = part + (int64_t)x * nq;
-    const uint64_t ct = reinterpret_cast<uint64_t>(a.CT);
     const int64_t qstep = HALVES * waves_per_group;
 
     // A "pair" is the HALVES queries a wave scans together.
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
                     kk[hh] = 0;
                     vv[hh] = 0.0f;
                 }
-                rec[wave][hh][lane] = ct + (uint64_t)kk[hh] * (uint64_t)ld * 4u;
+                rec[wave][hh][lane] = cbase + (uint64_t)kk[hh] * (uint64_t)ld * 4u;
                 wgt[wave][hh][lane] = vv[hh];
             }
             // walk the batch: U loads in flight while the previous U are used
@@ -233,143 +248,151 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
     }
 }
 
-// Four-rows-per-load form (codebook rows 16-byte aligned, nc % 4 == 0).  A
-// wave still owns 64 neurons, but one 16-byte-per-lane load now covers four
-// non-zeros: lane group g = lane / 16 reads row k of non-zero 4i+g, lanes of
-// a group four consecutive neurons each (16 x 16 B = one 256-byte row
+// Four-rows-per-load, pipelined form (codebook rows 16-byte aligned,
+// nc % 4 == 0).  A wave owns 64 neurons; one 16-byte-per-lane load covers
+// four non-zeros: lane group g = lane / 16 reads row k of non-zero 4i+g, the
+// 16 lanes of a group four consecutive neurons each (one 256-byte row
 // segment).  Wide loads reach about twice the L2 -> CU bandwidth of 4-byte
-// loads on gfx950, and the codebook slice per XCD stays 4 MiB.  Each lane
-// sums every fourth non-zero for its 4 neurons in order; the four partial
-// sums are combined in one fixed order ((p0 + p1) + (p2 + p3)) at the end.
-template <int M>
-__global__ __launch_bounds__(256) void k_bmu_csr_q4(const CsrArgs a, uint64_t *__restrict__ part,
-                                                   int64_t round, int32_t groups) {
-    constexpr int U = 4;  // load instructions (16 non-zeros) per group, two groups in flight
+// loads.  Each lane sums every fourth non-zero for its 4 neurons in order;
+// the four partial sums are combined in one fixed order ((p0 + p1) +
+// (p2 + p3)), the order the 4-byte-load kernel also uses, so both give the
+// same bits.  The scan is latency-bound: what limits it is how many
+// codebook loads each wave keeps in flight.  Here a wave's work is one stream of
+// batches of 4N non-zeros (a query is cut into ceil(len / 4N) batches, at
+// least one; the tail of its last batch is zero weights).  A batch is N
+// load units (LU: four consecutive non-zeros, one 16-byte load per lane),
+// and a ring of N register slots runs one batch behind the loads: rotation
+// r consumes the LUs of batch r - 1 slot by slot and refills each slot with
+// the matching LU of batch r, so N loads stay in flight across batch and
+// query boundaries instead of draining at each batch.
+//  - At the start of a rotation the batch's (k, v) (brought into LDS by DMA
+//    during the previous rotation) become row-address records; then the
+//    (k, v) of the next batch are staged.  No register load of the stream is
+//    ever waited for by the compiler, and every step issues exactly one
+//    codebook load, so the wait for a slot is vmcnt(N - 1).
+//  - A query is finalised after the rotation that consumed its last batch;
+//    the (group, query) result is merged with a 64-bit atomicMin (nothing
+//    returned, nothing waited for).
+template <int M, int N>
+__global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t *__restrict__ part,
+                                                     int64_t round, int32_t groups) {
     typedef float f4 __attribute__((ext_vector_type(4)));
-    __shared__ uint64_t rec[4][64];  // per wave: row addresses of the batch
-    __shared__ float wgt[4][64];     // ... and weights
+    constexpr int B = 4 * N;  // non-zeros per batch
+    static_assert(B <= 64, "a batch is staged by one wave, one non-zero per lane");
+    __shared__ uint64_t rec[4][2][B]; // per wave, by rotation parity: row addresses of a batch
+    __shared__ float wgt[4][2][B];    // ... and weights
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 4, col = lane & 15;
     const int x = (int)(blockIdx.x % (unsigned)groups);
     const int64_t local = blockIdx.x / (unsigned)groups;
     const int64_t chunk = round * groups + x;
     if (chunk >= a.n_chunks) return;
-    const int64_t waves_per_group = (int64_t)(gridDim.x / (unsigned)groups) * 4;
+    const int64_t wpg = (int64_t)(gridDim.x / (unsigned)groups) * 4;  // waves per group
     const int64_t lw = __builtin_amdgcn_readfirstlane((int)(local * 4 + wave));
     const int64_t nq = a.nq, nc = a.nc, ld = a.ldct;
     const int32_t d = a.d;
+    if (lw >= nq) return;
     const int32_t n0 = (int32_t)(chunk * 64 + 4 * col);  // this lane's 4 neurons
     const bool live = n0 < nc;                            // nc % 4 == 0: all 4 or none
-    const uint64_t off = (uint64_t)(live ? n0 : 0) * 4u;
+    const uint64_t off = (uint64_t)(live ? 4 * col : 0) * 4u;
     f4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
     if (metric_is_l2(M) && live) cn4 = *reinterpret_cast<const f4 *>(a.cn + n0);
-    uint64_t *mine = part + (int64_t)x * nq;
-    const uint64_t ct = reinterpret_cast<uint64_t>(a.CT);
+    unsigned long long *mine = reinterpret_cast<unsigned long long *>(part + (int64_t)x * nq);
+    const uint64_t cbase = reinterpret_cast<uint64_t>(a.CT) + (uint64_t)chunk * a.cstride;
+    const __attribute__((address_space(4))) int32_t *indptr =
+        (const __attribute__((address_space(4))) int32_t *)a.indptr;
+    const int32_t n_my = (int32_t)((nq - lw + wpg - 1) / wpg);  // queries of this wave
 
-    auto issue = [&](int base, f4 (&c)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint64_t addr = rec[wave][base + 4 * u + grp] + off;
-            c[u] = *reinterpret_cast<const __attribute__((address_space(1))) f4 *>(addr);
-        }
+    // ---- the batch stream (wave-uniform state).  "Staged": the batch whose
+    // (k, v) are in (pk, pv) (or on their way).
+    int32_t s_n = 0;      // its query (number within this wave's queries)
+    int64_t s_b = 0;      // the query's CSR base
+    int32_t s_len = 0;    // the query's length
+    bool s_ok = true;     // the query's span is valid
+    int32_t s_t = 0;      // the batch's first non-zero
+    bool s_has = false;   // a staged batch exists
+    // (readfirstlane keeps the stream state in scalar registers, so the
+    // span is read with scalar loads, which never hold the vector-load
+    // counter the ring relies on)
+    auto open_query = [&](int32_t n) {
+        n = __builtin_amdgcn_readfirstlane(n);
+        const int64_t q = lw + (int64_t)n * wpg;
+        const int32_t bb = __builtin_amdgcn_readfirstlane(indptr[q]);
+        const int32_t ee = __builtin_amdgcn_readfirstlane(indptr[q + 1]);
+        s_ok = bb >= 0 && ee >= bb && ee <= a.nnz;
+        s_b = s_ok ? bb : 0;
+        s_len = s_ok ? ee - bb : 0;
+        s_n = n;
+        s_t = 0;
+        s_has = true;
     };
-    auto consume = [&](int base, const f4 (&c)[U], f4 &acc) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float w = wgt[wave][base + 4 * u + grp];
-            acc.x = __builtin_fmaf(w, c[u].x, acc.x);
-            acc.y = __builtin_fmaf(w, c[u].y, acc.y);
-            acc.z = __builtin_fmaf(w, c[u].z, acc.z);
-            acc.w = __builtin_fmaf(w, c[u].w, acc.w);
-        }
-    };
-
-    if (lw >= nq) return;
-    // current query's span, and the next one's (prefetched one batch ahead)
-    auto span = [&](int64_t q, int64_t &b, int64_t &len, bool &ok) {
-        b = 0;
-        len = 0;
-        ok = q < nq;
-        if (ok) {
-            const int64_t bb = a.indptr[q], ee = a.indptr[q + 1];
-            ok = bb >= 0 && ee >= bb && ee <= a.nnz;
-            if (ok) {
-                b = bb;
-                len = ee - bb;
-            }
-        }
-    };
+    // lane j < B fetches non-zero s_t + j of the staged batch into (pk, pv),
+    // plain loads with the index clamped into the row (lanes past its end
+    // are zeroed when the records are made); an empty row loads nothing
     int32_t pk = 0;
     float pv = 0.0f;
-    auto prefetch = [&](int64_t b, int64_t len, int64_t t) {
-        pk = 0;
-        pv = 0.0f;
-        if (t + lane < len) {
-            pk = stream_load(a.indices + b + t + lane);
-            pv = stream_load(a.values + b + t + lane);
+    auto stage = [&]() {
+        if (s_len > 0) {
+            const int32_t t = s_t + lane;
+            const int64_t at = s_b + (t < s_len ? t : s_len - 1);
+            pk = a.indices[at];  // plain loads: non-temporal ones measured slower here
+            pv = a.values[at];
         }
     };
 
-    int64_t q = lw, b, len;
-    bool ok;
-    span(q, b, len, ok);
-    prefetch(b, len, 0);
-    while (true) {
-        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        int64_t nb = 0, nlen = 0;
-        bool nok = false, more = false;
-        const int64_t qn = q + waves_per_group;
-        for (int64_t t = 0; t < len; t += 64) {
-            int32_t kk = pk;
-            float vv = pv;
-            if (t + 64 < len) {
-                prefetch(b, len, t + 64);
-            } else if (qn < nq) {
-                span(qn, nb, nlen, nok);
-                more = true;
-                prefetch(nb, nlen, 0);
-            }
-            const bool bad = (uint32_t)kk >= (uint32_t)d;
-            if (__any(bad)) ok = false;
-            if (bad) {
-                kk = 0;
-                vv = 0.0f;
-            }
-            rec[wave][lane] = ct + (uint64_t)kk * (uint64_t)ld * 4u;  // past the end: row 0,
-            wgt[wave][lane] = vv;                                    // weight 0
-            const int64_t rem = len - t;
-            const int cnt = (int)((rem < 64 ? rem : 64) + 4 * U - 1) / (4 * U) * (4 * U);
-            f4 c0[U], c1[U];
-            issue(0, c0);
-            for (int u0 = 0; u0 < cnt; u0 += 8 * U) {
-                const bool two = u0 + 4 * U < cnt;
-                if (two) issue(u0 + 4 * U, c1);
-                consume(u0, c0, acc);
-                if (two) {
-                    if (u0 + 8 * U < cnt) issue(u0 + 8 * U, c0);
-                    consume(u0 + 4 * U, c1, acc);
-                }
-            }
+    // Turns the staged batch into the records of parity p and stages the
+    // next one.  Returns, for the batch now in the records: its query,
+    // whether it is the query's last batch, and whether the query is still
+    // valid.
+    bool i_ok = true;  // validity of the query being issued, over its batches so far
+    auto make_records = [&](int p, int32_t &q_out, bool &last_out, bool &ok_out) {
+        const bool in = lane < B && s_t + lane < s_len;
+        int32_t kk = in ? pk : 0;
+        float vv = in ? pv : 0.0f;
+        const bool bad = (uint32_t)kk >= (uint32_t)d;
+        if (bad) {
+            kk = 0;
+            vv = 0.0f;
         }
-        if (len == 0 && qn < nq) {  // an empty row prefetches nothing above
-            span(qn, nb, nlen, nok);
-            more = true;
-            prefetch(nb, nlen, 0);
+        if (lane < B) {
+            rec[wave][p][lane] = cbase + (uint64_t)kk * (uint64_t)ld * 4u;  // past the end: row 0,
+            wgt[wave][p][lane] = vv;                                        // weight 0
         }
+        if (s_t == 0) i_ok = s_ok;
+        if (__any(bad)) i_ok = false;
+        q_out = s_n;
+        ok_out = i_ok;
+        last_out = s_t + B >= s_len;
+        // the next batch
+        if (!last_out) {
+            s_t += B;
+        } else if (s_n + 1 < n_my) {
+            open_query(s_n + 1);
+        } else {
+            s_has = false;
+            return;
+        }
+        stage();
+    };
+
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto finalize = [&](int32_t n, bool ok) {
+        const int64_t q = lw + (int64_t)__builtin_amdgcn_readfirstlane(n) * wpg;
+        f4 s4 = acc;
         // combine the four lane groups' partial sums: (p0 + p1) + (p2 + p3)
 #pragma unroll
         for (int s2 = 16; s2 <= 32; s2 <<= 1) {
-            acc.x += __shfl_xor(acc.x, s2);
-            acc.y += __shfl_xor(acc.y, s2);
-            acc.z += __shfl_xor(acc.z, s2);
-            acc.w += __shfl_xor(acc.w, s2);
+            s4.x += __shfl_xor(s4.x, s2);
+            s4.y += __shfl_xor(s4.y, s2);
+            s4.z += __shfl_xor(s4.z, s2);
+            s4.w += __shfl_xor(s4.w, s2);
         }
         float be = __builtin_inff();
         int32_t bi = -1;
         if (live && ok) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float r = rank_value<M>(acc[e], cn4[e]);
+                const float r = rank_value<M>(s4[e], cn4[e]);
                 if (r < be) {
                     be = r;
                     bi = n0 + e;
@@ -385,15 +408,59 @@ __global__ __launch_bounds__(256) void k_bmu_csr_q4(const CsrArgs a, uint64_t *_
                 bi = oi;
             }
         }
-        if (lane == 0 && ok && bi >= 0) {
-            const uint64_t key = pack_key(be, (uint32_t)bi);
-            if (key < mine[q]) mine[q] = key;
+        if (lane == 0 && ok && bi >= 0)
+            atomicMin(mine + q, (unsigned long long)pack_key(be, (uint32_t)bi));
+        acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    // ---- prologue: batch 0 staged, made current, and issued into the ring
+    open_query(0);
+    stage();
+    int32_t q_cur = 0;
+    bool last_cur = false, ok_cur = true;
+    int par = 0;
+    make_records(par, q_cur, last_cur, ok_cur);
+    f4 buf[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        buf[j] = *reinterpret_cast<const __attribute__((address_space(1))) f4 *>(
+            rec[wave][par][4 * j + grp] + off);
+    while (true) {
+        // the ring holds the batch of parity par; the staged batch becomes
+        // the next one
+        const int32_t q_prev = q_cur;
+        const bool last_prev = last_cur, ok_prev = ok_cur;
+        const int pp = par;
+        if (s_has) {
+            par ^= 1;
+            make_records(par, q_cur, last_cur, ok_cur);
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                const int r = 4 * j + grp;
+                const float w = wgt[wave][pp][r];
+                acc.x = __builtin_fmaf(w, buf[j].x, acc.x);
+                acc.y = __builtin_fmaf(w, buf[j].y, acc.y);
+                acc.z = __builtin_fmaf(w, buf[j].z, acc.z);
+                acc.w = __builtin_fmaf(w, buf[j].w, acc.w);
+                buf[j] = *reinterpret_cast<const __attribute__((address_space(1))) f4 *>(
+                    rec[wave][par][r] + off);
+                // keep slot j's refill after its use (hoisting the loads would
+                // need a second set of slot registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (last_prev) finalize(q_prev, ok_prev);
+        } else {  // last rotation: nothing left to issue
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                const float w = wgt[wave][pp][4 * j + grp];
+                acc.x = __builtin_fmaf(w, buf[j].x, acc.x);
+                acc.y = __builtin_fmaf(w, buf[j].y, acc.y);
+                acc.z = __builtin_fmaf(w, buf[j].z, acc.z);
+                acc.w = __builtin_fmaf(w, buf[j].w, acc.w);
+            }
+            finalize(q_prev, ok_prev);  // the stream's last batch ends its query
+            break;
         }
-        if (!more) break;
-        q = qn;
-        b = nb;
-        len = nlen;
-        ok = nok;
     }
 }
 
@@ -427,29 +494,32 @@ int32_t csr_groups(int64_t nc) {
 hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
                       uint64_t *part) {
     CsrArgs a = a0;
+    const bool wide_ok = a.nc % 4 == 0 && a.ldct % 4 == 0 && a.cstride % 16 == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.CT) & 15) == 0 &&
+                         getenv("VS_CSR_DWORD") == nullptr;
     const int ncw = csr_chunk();
     a.n_chunks = (a.nc + ncw - 1) / ncw;
     const int32_t groups = (int32_t)(a.n_chunks < 8 ? a.n_chunks : 8);
     // workgroups per group: enough waves for the queries, at most a full chip
     const int64_t cu = n_cu > 0 ? n_cu : 256;
     int64_t per_group = (cu * kCsrWgPerCu) / groups;
-    const int64_t need = (a.nq + 4 * (64 / ncw) - 1) / (4 * (64 / ncw));
+    const int qpw = ncw == 32 ? 2 : 1;  // queries per wave
+    const int64_t need = (a.nq + 4 * qpw - 1) / (4 * qpw);
     if (per_group > need) per_group = need;
     if (per_group < 1) per_group = 1;
     const dim3 grid((unsigned)(per_group * groups)), block(256);
     const int64_t rounds = (a.n_chunks + groups - 1) / groups;
     hipError_t err = launch_fill_keys(part, (int64_t)groups * a.nq, st);
     if (err != hipSuccess) return err;
-    const bool q4 = ncw == 64 && a.nc % 4 == 0 && a.ldct % 4 == 0 &&
-                    (reinterpret_cast<uintptr_t>(a.CT) & 15) == 0 && getenv("VS_CSR_DWORD") == nullptr;
+    const bool ring = ncw == 64 && wide_ok;
     for (int64_t r = 0; r < rounds; ++r) {
         timing_before(st, "k_bmu_csr");
-        if (q4) {
+        if (ring) {
             switch (metric) {
-            case L2SQ_MIN: hipLaunchKernelGGL(k_bmu_csr_q4<L2SQ_MIN>, grid, block, 0, st, a, part, r, groups); break;
-            case L2SQ_MAX: hipLaunchKernelGGL(k_bmu_csr_q4<L2SQ_MAX>, grid, block, 0, st, a, part, r, groups); break;
-            case COS_MAX: hipLaunchKernelGGL(k_bmu_csr_q4<COS_MAX>, grid, block, 0, st, a, part, r, groups); break;
-            default: hipLaunchKernelGGL(k_bmu_csr_q4<COS_MIN>, grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MIN, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MAX, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
+            case COS_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MAX, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
+            default: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MIN, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
             }
         } else if (ncw == 32) {
             switch (metric) {

@@ -50,8 +50,10 @@ __global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X
     if (lane == 0) out[row] = acc;
 }
 
-// Feature-major X (d rows of cols values, row stride ld): column j's squared norm.  A workgroup owns 64
-// columns (VEC: 256, four per lane); its 16 waves each sum one contiguous
+// Feature-major X: column j's squared norm, feature k of column j at
+// X[(j / 64) * cs + k * ld + j % 64] (cs = 64 for plain rows of stride ld;
+// cs = d * 64, ld = 64 for the 64-column blocked layout).  A workgroup owns
+// 64 columns (VEC: 256, four per lane); its 16 waves each sum one contiguous
 // range of features in order, then wave 0 adds the 16 partial sums in wave
 // order.  Vector width does not change any column's order of summation.
 constexpr int kColWaves = 16;
@@ -59,7 +61,7 @@ constexpr int kColWaves = 16;
 template <bool VEC>
 __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__restrict__ X,
                                                                int64_t cols, int64_t ld,
-                                                               int32_t d,
+                                                               int64_t cs, int32_t d,
                                                                float *__restrict__ out) {
     constexpr int W = VEC ? 4 : 1;
     __shared__ f32x4 part[kColWaves][64];
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__r
     const int32_t k1 = (int32_t)((int64_t)d * (wave + 1) / kColWaves);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c0 < cols) {
-        const float *x = X + c0;
+        const float *x = X + (c0 >> 6) * cs + (c0 & 63);
         if constexpr (VEC) {
 #pragma unroll 8
             for (int32_t k = k0; k < k1; ++k) {
@@ -139,18 +141,59 @@ hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *ou
     return hipGetLastError();
 }
 
-hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int32_t d, float *out,
-                              hipStream_t st) {
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int64_t cs, int32_t d,
+                              float *out, hipStream_t st) {
     if (cols <= 0) return hipSuccess;
-    const bool vec = (cols % 4 == 0) && (ld % 4 == 0) &&
+    const bool vec = (cols % 4 == 0) && (ld % 4 == 0) && (cs % 4 == 0) &&
                      ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
     if (vec)
         hipLaunchKernelGGL(k_col_sqnorms<true>, dim3(blocks_for(cols, 256)), dim3(64 * kColWaves),
-                           0, st, X, cols, ld, d, out);
+                           0, st, X, cols, ld, cs, d, out);
     else
         hipLaunchKernelGGL(k_col_sqnorms<false>, dim3(blocks_for(cols, 64)), dim3(64 * kColWaves),
-                           0, st, X, cols, ld, d, out);
+                           0, st, X, cols, ld, cs, d, out);
+    return hipGetLastError();
+}
+
+// 64-column blocked copy of a feature-major codebook: CB[b][k][j] =
+// CT[k * ldct + 64 b + j] for 64 b + j < nc, 0 for the padding columns of the
+// last block.  One thread per 4 values (VEC) or per value; both sides move
+// in 256-byte row segments.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_block_codebook(const float *__restrict__ CT, int64_t nc,
+                                                       int64_t ldct, int32_t d, int64_t total,
+                                                       float *__restrict__ CB) {
+    constexpr int W = VEC ? 4 : 1;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * W;
+    for (int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * W; e < total; e += stride) {
+        const int64_t j = e & 63, k = (e >> 6) % d, b = (e >> 6) / d;
+        const int64_t n = b * 64 + j;
+        if constexpr (VEC) {
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (n < nc) v = *reinterpret_cast<const f32x4 *>(CT + k * ldct + n);  // nc % 4 == 0
+            *reinterpret_cast<f32x4 *>(CB + e) = v;
+        } else {
+            CB[e] = n < nc ? CT[k * ldct + n] : 0.0f;
+        }
+    }
+}
+
+hipError_t launch_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
+                                 hipStream_t st) {
+    const int64_t total = (nc + 63) / 64 * 64 * (int64_t)d;
+    const bool vec = nc % 4 == 0 && ldct % 4 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(CT) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(CB) & 15) == 0);
+    const int64_t per = vec ? 4 : 1;
+    int64_t blocks = (total / per + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (vec)
+        hipLaunchKernelGGL(k_block_codebook<true>, dim3((unsigned)blocks), dim3(256), 0, st, CT,
+                           nc, ldct, d, total, CB);
+    else
+        hipLaunchKernelGGL(k_block_codebook<false>, dim3((unsigned)blocks), dim3(256), 0, st, CT,
+                           nc, ldct, d, total, CB);
     return hipGetLastError();
 }
 

@@ -1,14 +1,15 @@
 // roofs.hip -- measurement kernels for the on-chip roof of the sparse scan.
 //
 // Not part of the search ABI (built into libvs_roofs.so, used by bench.py's
-// --roof mode).  The sparse scan reads codebook rows as 256-byte segments
-// (64 lanes x 4 bytes) out of a slice that lives in its XCD's L2; this kernel
-// reads the same shape from an L2-resident region so that the achieved
-// L2 -> CU bandwidth of that access pattern can be quoted as the roof.
+// --roof mode).  The sparse scan reads codebook rows as 256-byte segments,
+// one per 4-byte load instruction or four per 16-byte load instruction, out
+// of a slice that lives in its XCD's L2; this kernel reads the same shapes
+// from an L2-resident region so that the achieved L2 -> CU bandwidth of that
+// access pattern can be quoted as the roof.
 //
 // Each XCD (workgroup group = blockIdx % 8, as the hardware deals workgroups
-// to XCDs) reads its own region of `rows` rows x 64 floats, row stride `ld`
-// floats; every wave walks the rows in a scattered order, 16 loads in flight,
+// to XCDs) reads its own region of `rows` rows, row stride `ld` floats;
+// every wave walks the rows in a scattered order, 16 loads in flight,
 // `passes` times.  One float per wave is written so the loads are not dead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,16 +20,19 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int VW>  // floats per lane per load: 1 (dword) or 4 (dwordx4)
+template <int VW, int RPI>  // floats per lane per load; rows per load instruction
 __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, int64_t rows,
                                                 int64_t ld, int32_t passes,
                                                 float *__restrict__ out) {
+    constexpr int LPR = 64 / RPI;  // lanes per row
     const int lane = threadIdx.x & 63;
     const int x = blockIdx.x & 7;
     const int64_t local = blockIdx.x >> 3;
     const int64_t wpx = (int64_t)(gridDim.x >> 3) * 4;  // waves per XCD
     const int64_t w = __builtin_amdgcn_readfirstlane((int)(local * 4 + (threadIdx.x >> 6)));
-    const float *region = buf + (int64_t)x * rows * ld + lane * VW;  // this lane's column
+    // this lane's column; lane group lane / LPR reads its own row of each load
+    const float *region = buf + (int64_t)x * rows * ld + (lane % LPR) * VW;
+    const int64_t sub = lane / LPR;  // row offset of this lane group
     float acc = 0.0f;
     const int64_t steps = (int64_t)passes * rows / wpx;
     const int64_t mask = rows - 1;  // rows is a power of two
@@ -37,7 +41,7 @@ __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, 
         float v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int64_t row = (r + (int64_t)u * 4099) & mask;
+            const int64_t row = (r + (int64_t)u * 4099 + sub * 1031) & mask;
             if constexpr (VW == 1) {
                 v[u] = region[row * ld];
             } else {
@@ -54,21 +58,27 @@ __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, 
 
 }  // namespace
 
-// Reads rows x (64 * vw) floats per XCD region (8 regions, row stride ld
-// >= 64 * vw, rows a power of two), `passes` times over.  Returns the bytes the kernel read; the
-// caller times the launch on `stream`.  out needs grid * 4 floats, grid =
-// 8 * wg_per_xcd.
+// Reads, per XCD region (8 regions, rows a power of two, row stride ld),
+// `passes` times over: with rpi = 1 one row segment of 64 * vw floats per
+// load instruction, with rpi = 4 (vw = 4) four row segments of 64 floats
+// (256 bytes) per instruction, one per 16-lane group.  Returns the bytes the
+// kernel read; the caller times the launch on `stream`.  out needs grid * 4
+// floats, grid = 8 * wg_per_xcd.
 VS_API int64_t vs_roof_l2_read(const float *buf, int64_t rows, int64_t ld, int32_t passes,
-                               int32_t vw, int32_t wg_per_xcd, float *out, void *stream) {
+                               int32_t vw, int32_t rpi, int32_t wg_per_xcd, float *out,
+                               void *stream) {
     if (!buf || !out || rows < 16 || (rows & (rows - 1)) != 0 || passes < 1 || wg_per_xcd < 1 ||
-        (vw != 1 && vw != 4) || ld < 64 * vw)
+        (vw != 1 && vw != 4) || (rpi != 1 && rpi != 4) || (rpi == 4 && vw != 4) ||
+        ld < 64 * vw / rpi)
         return -1;
     const dim3 grid((unsigned)(8 * wg_per_xcd)), block(256);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (vw == 1)
-        hipLaunchKernelGGL(k_l2_roof<1>, grid, block, 0, st, buf, rows, ld, passes, out);
+        hipLaunchKernelGGL((k_l2_roof<1, 1>), grid, block, 0, st, buf, rows, ld, passes, out);
+    else if (rpi == 1)
+        hipLaunchKernelGGL((k_l2_roof<4, 1>), grid, block, 0, st, buf, rows, ld, passes, out);
     else
-        hipLaunchKernelGGL(k_l2_roof<4>, grid, block, 0, st, buf, rows, ld, passes, out);
+        hipLaunchKernelGGL((k_l2_roof<4, 4>), grid, block, 0, st, buf, rows, ld, passes, out);
     if (hipGetLastError() != hipSuccess) return -1;
     const int64_t waves = (int64_t)8 * wg_per_xcd * 4;
     const int64_t steps = (int64_t)passes * rows / (waves / 8);

@@ -70,6 +70,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
+// s_waitcnt vmcnt(N) for a compile-time count N (0 .. 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (the fence
 // waits for every outstanding load, including slab loads meant to stay in
 // flight across the barrier); callers make the LDS data they need visible
@@ -101,10 +108,12 @@ struct DenseArgs {
 struct CsrArgs {
     const int32_t *indptr, *indices;
     const float *values;
-    const float *CT;        // d rows of nc neurons, row stride ldct
+    const float *CT;        // codebook: feature k of neuron 64 b + j at
+                            // CT + b * cstride (bytes) + (k * ldct + j) floats
     const float *cn;        // nc
     uint64_t *keys;         // nq
     int64_t nq, nnz, nc, ldct;
+    int64_t cstride;        // bytes between 64-neuron blocks: 256 (plain rows) or d * 256
     int32_t d;
     int64_t n_chunks;       // candidate chunks
 };
@@ -114,8 +123,11 @@ struct CsrArgs {
 hipError_t launch_fill_keys(uint64_t *keys, int64_t n, hipStream_t st);
 hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *out,
                               hipStream_t st);
-hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int32_t d, float *out,
-                              hipStream_t st);
+// feature k of column j at X[(j / 64) * cs + k * ld + j % 64]
+hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int64_t cs, int32_t d,
+                              float *out, hipStream_t st);
+hipError_t launch_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
+                                 hipStream_t st);
 hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
                                   int64_t nnz, float *out, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t st,

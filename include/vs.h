@@ -115,6 +115,34 @@ int vs_bmu_search_csr(const int32_t *indptr, const int32_t *indices, const float
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * 64-neuron blocked codebook layout for the sparse-query search [BMU,
+ * section 3 (feature-major storage) and section 4 "The levers" (neuron-axis
+ * chunking)].  Feature k of neuron 64 b + j (0 <= j < 64) is stored at
+ * CB[(b * d + k) * 64 + j]: each block is a d x 64 feature-major matrix, so
+ * the codebook slice one 64-neuron chunk of the search reads is contiguous
+ * (a few large pages) instead of d row segments spread over the whole
+ * feature-major array, which costs address-translation misses.
+ *   vs_csr_blocked_bytes   size of CB in bytes: ceil(nc / 64) * 64 * d * 4
+ *                          (0 for invalid sizes).  Host-only.
+ *   vs_csr_block_codebook  writes CB from a feature-major CT (d rows of nc,
+ *                          row stride ldct >= nc); columns past nc in the
+ *                          last block are written as 0.  CB is caller-owned
+ *                          device memory of vs_csr_blocked_bytes bytes;
+ *                          CT and CB must not overlap.
+ *   vs_bmu_search_csr_blocked  vs_bmu_search_csr over CB; same arguments
+ *                          otherwise (workspace: vs_bmu_search_csr_workspace)
+ *                          and bit-identical results.
+ */
+size_t vs_csr_blocked_bytes(int64_t nc, int32_t d);
+int vs_csr_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
+                          void *stream);
+int vs_bmu_search_csr_blocked(const int32_t *indptr, const int32_t *indices,
+                              const float *values, int64_t nq, int64_t nnz, const float *CB,
+                              int64_t nc, int32_t d, int32_t metric, int32_t *idx_out,
+                              float *score_out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * One step of the greedy diversity sequence [DIV] for nseq sequences at once.
  *   C          n x d float32, unit-norm rows (the embedding table).
  *   last_pick  int32[nseq]: each sequence's reference row (its last pick).

@@ -37,8 +37,9 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     fns = header_functions()
-    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_diversity_step",
-                 "vs_candidate_norms", "vs_tile_rows", "vs_status_str"):
+    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_bmu_search_csr_blocked",
+                 "vs_csr_block_codebook", "vs_diversity_step", "vs_candidate_norms",
+                 "vs_tile_rows", "vs_status_str"):
         assert name in fns
     assert sorted(vs.EXPORTS) == fns
 
@@ -117,6 +118,34 @@ def test_csr_validation(L):
     assert call(indices=0) == 1
     assert call(nnz=0, indices=0, values=0, ws_bytes=0) == 4  # empty arrays allowed
     assert call(CT=FAKE + 1) == 5
+    assert call(ws_bytes=10) == 4
+
+
+def test_csr_blocked_validation(L):
+    assert L.vs_csr_blocked_bytes(1, 1) == 256
+    assert L.vs_csr_blocked_bytes(65, 10) == 2 * 64 * 10 * 4
+    assert L.vs_csr_blocked_bytes(0, 10) == 0
+    assert L.vs_csr_blocked_bytes(10, 0) == 0
+    blk = lambda CT=FAKE, nc=16, ld=16, d=8, CB=FAKE: L.vs_csr_block_codebook(
+        _P(CT), nc, ld, d, _P(CB), None)
+    assert blk(ld=15) == 2
+    assert blk(nc=0) == 2
+    assert blk(d=0) == 2
+    assert blk(CT=0) == 1
+    assert blk(CB=0) == 1
+    assert blk(CB=FAKE + 2) == 5
+
+    def call(indptr=FAKE, indices=FAKE, values=FAKE, nq=3, nnz=10, CB=FAKE, nc=16, d=8,
+             metric=0, idx=FAKE, score=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_bmu_search_csr_blocked(_P(indptr), _P(indices), _P(values), nq, nnz, _P(CB),
+                                           nc, d, metric, _P(idx), _P(score), _P(ws), ws_bytes,
+                                           None)
+    assert call(metric=5) == 3
+    assert call(nc=0) == 2
+    assert call(d=0) == 2
+    assert call(nq=0, indptr=0) == 0
+    assert call(CB=0) == 1
+    assert call(CB=FAKE + 1) == 5
     assert call(ws_bytes=10) == 4
 
 

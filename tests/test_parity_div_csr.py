@@ -273,6 +273,47 @@ def test_csr_paths_agree_bitwise(metric, monkeypatch):
         assert np.array_equal(o[1].view(np.uint32), outs[0][1].view(np.uint32))
 
 
+def run_csr_blocked(indptr, indices, values, CT, metric, pad=0):
+    CB = vs.vs_csr_block_codebook(padded(CT, pad))
+    idx, score = vs.vs_bmu_search_csr_blocked(T(indptr), T(indices), T(values), CB,
+                                              CT.shape[1], metric, d=CT.shape[0])
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy()
+
+
+@pytest.mark.parametrize("nc,pad", [(1, 0), (63, 0), (64, 0), (700, 3), (1030, 0), (1028, 64)])
+def test_csr_block_codebook_layout(nc, pad):
+    """The blocked copy holds feature k of neuron 64 b + j at (b d + k) 64 + j
+    and zeros past nc (an exact copy, checked against numpy indexing)."""
+    d = 37
+    (r,) = synth.rng_children(4100 + nc, 1)
+    CT = synth.uniform01(r, (d, nc))
+    CB = vs.vs_csr_block_codebook(padded(CT, pad)).cpu().numpy()
+    nb = (nc + 63) // 64
+    exp = np.zeros((nb, d, 64), np.float32)
+    for b in range(nb):
+        w = min(64, nc - 64 * b)
+        exp[b, :, :w] = CT[:, 64 * b:64 * b + w]
+    assert CB.shape == (nb * d * 64,)
+    assert np.array_equal(CB.reshape(nb, d, 64).view(np.uint32), exp.view(np.uint32))
+
+
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+@pytest.mark.parametrize("nc", [1, 63, 700, 1028])
+def test_csr_blocked_matches_plain(metric, nc, chunk):
+    """The blocked layout is read by the same kernels in the same order:
+    results are bit-identical to the plain feature-major search, which the
+    oracle checks."""
+    empty = () if metric in (2, 3) else (0, 5)
+    indptr, indices, values, CT = csr_case(70, 300, nc, 0.05, key=nc * 8 + metric,
+                                           empty_rows=empty)
+    a = run_csr(indptr, indices, values, CT, metric)
+    b = run_csr_blocked(indptr, indices, values, CT, metric)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    csr_parity(indptr, indices, values, CT, metric)
+
+
 def csr_select(indptr, indices, values, rows):
     rows = np.asarray(rows)
     ptr = np.concatenate([[0], np.cumsum(indptr[rows + 1] - indptr[rows])]).astype(np.int32)
@@ -301,6 +342,10 @@ def test_workload_4_sampled():
     256 seeded rows are checked one by one against the oracle."""
     w = synth.workload(4)
     idx, score = run_csr(w["indptr"], w["indices"], w["values"], w["CT"], 0, pad=64)
+    # the blocked layout (the form the benchmark times) gives the same bits
+    bidx, bscore = run_csr_blocked(w["indptr"], w["indices"], w["values"], w["CT"], 0)
+    assert np.array_equal(idx, bidx)
+    assert np.array_equal(score.view(np.uint32), bscore.view(np.uint32))
     sel = synth.sample_queries(w["nq"], 256, key=4)
     ptr = w["indptr"]
     sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
