@@ -55,6 +55,14 @@ namespace vs {
 #define VS_CSR_WG_PER_CU 7
 #endif
 constexpr int kCsrWgPerCu = VS_CSR_WG_PER_CU;  // x 4 waves resident per CU (VGPR-limited)
+// The pipelined kernel is launched with more workgroups than can be resident
+// (4 waves per SIMD fit): its queries are dealt round-robin to waves, so more,
+// shorter waves even out the end of a round (measured: 0.512 ms per round at
+// 4 workgroups per CU, 0.491 at 8, 0.472 at 32)
+#ifndef VS_CSR_RING_WG_PER_CU
+#define VS_CSR_RING_WG_PER_CU 32
+#endif
+constexpr int kCsrRingWgPerCu = VS_CSR_RING_WG_PER_CU;
 #ifndef VS_CSR_UNROLL
 #define VS_CSR_UNROLL 8
 #endif
@@ -502,7 +510,8 @@ hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
     const int32_t groups = (int32_t)(a.n_chunks < 8 ? a.n_chunks : 8);
     // workgroups per group: enough waves for the queries, at most a full chip
     const int64_t cu = n_cu > 0 ? n_cu : 256;
-    int64_t per_group = (cu * kCsrWgPerCu) / groups;
+    const bool ring = ncw == 64 && wide_ok;
+    int64_t per_group = (cu * (ring ? kCsrRingWgPerCu : kCsrWgPerCu)) / groups;
     const int qpw = ncw == 32 ? 2 : 1;  // queries per wave
     const int64_t need = (a.nq + 4 * qpw - 1) / (4 * qpw);
     if (per_group > need) per_group = need;
@@ -511,7 +520,6 @@ hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
     const int64_t rounds = (a.n_chunks + groups - 1) / groups;
     hipError_t err = launch_fill_keys(part, (int64_t)groups * a.nq, st);
     if (err != hipSuccess) return err;
-    const bool ring = ncw == 64 && wide_ok;
     for (int64_t r = 0; r < rounds; ++r) {
         timing_before(st, "k_bmu_csr");
         if (ring) {

@@ -259,7 +259,8 @@ def test_csr_row_stride(pad, chunk):
 @pytest.mark.parametrize("metric", [0, 2])
 def test_csr_paths_agree_bitwise(metric, monkeypatch):
     """The four-rows-per-load kernel and the 4-byte-load kernels (one or two
-    queries per wave) sum in the same order, so they agree bit for bit."""
+    queries per wave) sum in the same order, so they agree bit for bit, on
+    both codebook layouts."""
     indptr, indices, values, CT = csr_case(150, 300, 1030 - 1030 % 4, 0.06, key=66 + metric)
     outs = []
     for env in ({"VS_CSR_CHUNK": "64"}, {"VS_CSR_CHUNK": "64", "VS_CSR_DWORD": "1"},
@@ -268,6 +269,7 @@ def test_csr_paths_agree_bitwise(metric, monkeypatch):
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         outs.append(run_csr(indptr, indices, values, CT, metric))
+        outs.append(run_csr_blocked(indptr, indices, values, CT, metric))
     for o in outs[1:]:
         assert np.array_equal(o[0], outs[0][0])
         assert np.array_equal(o[1].view(np.uint32), outs[0][1].view(np.uint32))
