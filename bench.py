@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--csr-storage", choices=["f32", "f16"], default="f32",
+                    help="sparse workload: codebook storage type ('f16': the 128-neuron "
+                         "blocked fp16 copy, fp32 arithmetic)")
     ap.add_argument("--csr-layout", choices=["blocked", "plain"], default="blocked",
                     help="sparse workload: 'blocked' times the 64-neuron blocked copy of the "
                          "codebook plus the search over it, 'plain' the search over the "
@@ -163,7 +166,17 @@ def setup(k, torch, vs, a):
     ws = torch.empty(vs.lib().vs_bmu_search_csr_workspace(nq, nc, w["d"], 0), dtype=torch.uint8,
                      device=dev)
 
-    if a.csr_layout == "plain":
+    if a.csr_storage == "f16":
+        # each step writes the fp16 blocked copy of the fp32 codebook and
+        # searches it (load fp16, compute fp32)
+        CB16 = torch.empty(vs.lib().vs_csr_blocked_f16_bytes(nc, w["d"]) // 2,
+                           dtype=torch.float16, device=dev)
+
+        def step():
+            vs.vs_csr_block_codebook_f16(CT, out=CB16)
+            vs.vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, 0, d=w["d"],
+                                             idx_out=idx, score_out=score, workspace=ws)
+    elif a.csr_layout == "plain":
         def step():
             vs.vs_bmu_search_csr(indptr, indices, values, CT, 0, idx_out=idx, score_out=score,
                                  workspace=ws)
@@ -181,8 +194,11 @@ def setup(k, torch, vs, a):
     w["nnz"] = int(w["indices"].shape[0])
     flops = 2.0 * w["nnz"] * nc
     cfg = dict(workload=w["name"], nq=nq, nc=nc, d=w["d"], nnz=w["nnz"], metric="l2sq_min",
-               codebook_row_stride=nc + 64, codebook_layout=a.csr_layout)
-    chunks = (nc + 63) // 64
+               codebook_row_stride=nc + 64,
+               codebook_layout="blocked" if a.csr_storage == "f16" else a.csr_layout,
+               codebook_storage=a.csr_storage)
+    w["value_bytes"] = 2 if a.csr_storage == "f16" else 4
+    chunks = (nc + (127 if a.csr_storage == "f16" else 63)) // (128 if a.csr_storage == "f16" else 64)
     rounds = (chunks + min(8, chunks) - 1) // min(8, chunks)  # one scan launch per round
     return w, step, pairs, flops, rounds, cfg
 
@@ -397,10 +413,11 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4))
     else:
-        # sparse: 4 codebook bytes per non-zero x neuron multiply-add, served
-        # from the XCDs' L2 (each XCD's 4 MiB slice is read from HBM once per
-        # round), so the roof is the measured L2 -> CU bandwidth, not HBM
-        achieved = 4.0 * w["nnz"] * w["nc"] * a.steps / kernel_s_total / 1e9
+        # sparse: 4 (fp32) or 2 (fp16 storage) codebook bytes per non-zero x
+        # neuron multiply-add, served from the XCDs' L2 (each XCD's 4 MiB slice
+        # is read from HBM once per round), so the roof is the measured
+        # L2 -> CU bandwidth, not HBM
+        achieved = w["value_bytes"] * w["nnz"] * w["nc"] * a.steps / kernel_s_total / 1e9
         roof = dict(bound="l2", achieved=round(achieved, 1), peak=PEAK_L2_WIDE_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_L2_WIDE_GBS, 4),
                     peak_source="measured: bench.py --roof l2, dwordx4_4x256B")

@@ -11,6 +11,8 @@ Functions (same names as the C entry points):
     vs_bmu_search_csr(indptr, indices, values, CT, metric) -> (idx, score)
     vs_csr_block_codebook(CT)                          -> CB (64-neuron blocked copy)
     vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric) -> (idx, score)
+    vs_csr_block_codebook_f16(CT)                      -> CB16 (fp16, 128-neuron blocks)
+    vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, metric) -> (idx, score)
     vs_diversity_step(C, last_pick, mask_bits)         -> (idx, score)
     vs_candidate_norms(C, feature_major=False)         -> norms
     vs_tile_rows(cache_bytes, d, bytes_per_value)      -> int (host only)
@@ -33,7 +35,8 @@ STATUS = {0: "VS_OK", 1: "VS_ERR_NULL", 2: "VS_ERR_SHAPE", 3: "VS_ERR_METRIC",
 
 EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_csr_workspace",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
-           "vs_bmu_search_csr_blocked", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
+           "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
            "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
            "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
 
@@ -70,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.vs_csr_blocked_bytes.restype = SZ
     L.vs_csr_block_codebook.argtypes = [P, I64, I64, I32, P, P]
     L.vs_bmu_search_csr_blocked.argtypes = [P, P, P, I64, I64, P, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_csr_blocked_f16_bytes.argtypes = [I64, I32]
+    L.vs_csr_blocked_f16_bytes.restype = SZ
+    L.vs_csr_block_codebook_f16.argtypes = [P, I64, I64, I32, P, P]
+    L.vs_bmu_search_csr_blocked_f16.argtypes = [P, P, P, I64, I64, P, I64, I32, I32, P, P, P, SZ,
+                                                P]
     L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
     L.vs_diversity_step_workspace.restype = SZ
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
@@ -83,7 +91,8 @@ def lib() -> ctypes.CDLL:
     L.vs_status_str.restype = ctypes.c_char_p
     L.vs_version.restype = ctypes.c_char_p
     for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_csr_block_codebook",
-                 "vs_bmu_search_csr_blocked", "vs_diversity_step",
+                 "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
+                 "vs_bmu_search_csr_blocked_f16", "vs_diversity_step",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
         getattr(L, name).restype = ctypes.c_int
@@ -258,6 +267,66 @@ def vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric=VS_L2SQ_MI
                                          d, m, _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search_csr_blocked")
+    return idx_out, score_out
+
+
+def vs_csr_block_codebook_f16(CT, out=None):
+    """fp16 copy of a feature-major fp32 codebook CT (d x nc, unit column
+    stride, any row stride) in 128-neuron blocks: a flat torch.float16 tensor
+    holding, for every block b, the d x 128 matrix of neurons 128 b ..
+    128 b + 127 (zeros past nc), rounded to nearest even."""
+    torch = _torch()
+    L = lib()
+    if not isinstance(CT, torch.Tensor) or not CT.is_cuda or CT.dtype != torch.float32 \
+            or CT.dim() != 2 or CT.stride(1) != 1 or CT.stride(0) < CT.shape[1]:
+        raise ValueError("CT must be a float32 CUDA matrix with unit column stride")
+    d, nc = CT.shape
+    n = L.vs_csr_blocked_f16_bytes(nc, d) // 2
+    if out is None:
+        out = torch.empty(n, dtype=torch.float16, device=CT.device)
+    elif out.numel() < n or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float16 tensor of at least {n} values")
+    with torch.cuda.device(CT.device):
+        rc = L.vs_csr_block_codebook_f16(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
+                                         _stream(CT.device))
+    _check(rc, "vs_csr_block_codebook_f16")
+    return out
+
+
+def vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, metric=VS_L2SQ_MIN, d=None,
+                                  idx_out=None, score_out=None, workspace=None,
+                                  want_score: bool = True):
+    """vs_bmu_search_csr over an fp16 codebook in the 128-neuron blocked layout
+    that vs_csr_block_codebook_f16 writes (fp32 arithmetic throughout)."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(indptr, "indptr", torch.int32, 1)
+    _dev(indices, "indices", torch.int32, 1)
+    _dev(values, "values", torch.float32, 1)
+    _dev(CB16, "CB16", torch.float16, 1)
+    nq = indptr.numel() - 1
+    nnz = indices.numel()
+    if values.numel() != nnz:
+        raise ValueError("indices and values differ in length")
+    nblk = (nc + 127) // 128
+    if d is None:
+        d = CB16.numel() // (nblk * 128)
+    if CB16.numel() < nblk * 128 * d:
+        raise ValueError("CB16 is smaller than the blocked layout of nc x d")
+    dev = CB16.device
+    if idx_out is None:
+        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search_csr_blocked_f16(_ptr(indptr), _ptr(indices) if nnz else None,
+                                             _ptr(values) if nnz else None, nq, nnz, _ptr(CB16),
+                                             nc, d, m, _ptr(idx_out), _ptr(score_out), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_bmu_search_csr_blocked_f16")
     return idx_out, score_out
 
 

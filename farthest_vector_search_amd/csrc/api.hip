@@ -251,7 +251,8 @@ VS_API size_t vs_bmu_search_csr_workspace(int64_t nq, int64_t nc, int32_t d, int
 static int csr_search(const int32_t *indptr, const int32_t *indices, const float *values,
                       int64_t nq, int64_t nnz, const float *CT, int64_t nc, int64_t ld,
                       int64_t cstride, int32_t d, int32_t metric, int32_t *idx_out,
-                      float *score_out, void *workspace, size_t workspace_bytes, void *stream) {
+                      float *score_out, void *workspace, size_t workspace_bytes, void *stream,
+                      bool f16 = false) {
     if (nq == 0) return VS_OK;
     if (!indptr || !CT || !idx_out || !workspace || (nnz > 0 && (!indices || !values)))
         return VS_ERR_NULL;
@@ -270,8 +271,13 @@ static int csr_search(const int32_t *indptr, const int32_t *indices, const float
     float *cn = reinterpret_cast<float *>(ws + L.cn);
     uint64_t *part = reinterpret_cast<uint64_t *>(ws + L.part);
 
-    if (vs::metric_is_l2(metric))
-        VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, ld, cstride / 4, d, cn, st));
+    if (vs::metric_is_l2(metric)) {
+        if (f16)
+            VS_TRY_HIP(vs::launch_col_sqnorms_f16(reinterpret_cast<const uint16_t *>(CT), nc, d,
+                                                  cn, st));
+        else
+            VS_TRY_HIP(vs::launch_col_sqnorms(CT, nc, ld, cstride / 4, d, cn, st));
+    }
     if (vs::metric_is_l2(metric) && score_out)
         VS_TRY_HIP(vs::launch_csr_row_sqnorms(indptr, values, nq, nnz, qn, st));
 
@@ -288,7 +294,8 @@ static int csr_search(const int32_t *indptr, const int32_t *indices, const float
     a.ldct = ld;
     a.cstride = cstride;
     a.d = d;
-    VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu, part));
+    if (f16) VS_TRY_HIP(vs::launch_csr_f16(a, metric, st, n_cu, part));
+    else VS_TRY_HIP(vs::launch_csr(a, metric, st, n_cu, part));
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
 }
@@ -322,6 +329,36 @@ VS_API int vs_csr_block_codebook(const float *CT, int64_t nc, int64_t ldct, int3
     if (const int s = device_ready(&n_cu)) return s;
     VS_TRY_HIP(vs::launch_block_codebook(CT, nc, ldct, d, CB, reinterpret_cast<hipStream_t>(stream)));
     return VS_OK;
+}
+
+VS_API size_t vs_csr_blocked_f16_bytes(int64_t nc, int32_t d) {
+    if (nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxIndex) return 0;
+    return (size_t)((nc + 127) / 128) * 128u * (size_t)d * 2u;
+}
+
+VS_API int vs_csr_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
+                                     uint16_t *CB16, void *stream) {
+    if (nc < 1 || nc > kMaxIndex || ldct < nc || d < 1 || d > kMaxIndex) return VS_ERR_SHAPE;
+    if (!CT || !CB16) return VS_ERR_NULL;
+    if (!al4(CT) || (reinterpret_cast<uintptr_t>(CB16) & 15) != 0) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_block_codebook_f16(CT, nc, ldct, d, CB16,
+                                             reinterpret_cast<hipStream_t>(stream)));
+    return VS_OK;
+}
+
+VS_API int vs_bmu_search_csr_blocked_f16(const int32_t *indptr, const int32_t *indices,
+                                         const float *values, int64_t nq, int64_t nnz,
+                                         const uint16_t *CB16, int64_t nc, int32_t d,
+                                         int32_t metric, int32_t *idx_out, float *score_out,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (!csr_shape_ok(nq, nnz, nc, d)) return VS_ERR_SHAPE;
+    if (CB16 && (reinterpret_cast<uintptr_t>(CB16) & 15) != 0) return VS_ERR_ALIGN;
+    return csr_search(indptr, indices, values, nq, nnz, reinterpret_cast<const float *>(CB16), nc,
+                      128, (int64_t)d * 256, d, metric, idx_out, score_out, workspace,
+                      workspace_bytes, stream, true);
 }
 
 VS_API int vs_bmu_search_csr_blocked(const int32_t *indptr, const int32_t *indices,

@@ -281,10 +281,14 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
 //  - A query is finalised after the rotation that consumed its last batch;
 //    the (group, query) result is merged with a 64-bit atomicMin (nothing
 //    returned, nothing waited for).
-template <int M, int N>
+template <int M, int N, bool HALF>
 __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t *__restrict__ part,
                                                      int64_t round, int32_t groups) {
     typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    constexpr int NPL = HALF ? 8 : 4;    // neurons per lane (one 16-byte load)
+    constexpr int CW = 16 * NPL;         // neurons per chunk
+    constexpr uint64_t ESZ = HALF ? 2 : 4;  // bytes per codebook value
     constexpr int B = 4 * N;  // non-zeros per batch
     static_assert(B <= 64, "a batch is staged by one wave, one non-zero per lane");
     __shared__ uint64_t rec[4][2][B]; // per wave, by rotation parity: row addresses of a batch
@@ -300,11 +304,16 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
     const int64_t nq = a.nq, nc = a.nc, ld = a.ldct;
     const int32_t d = a.d;
     if (lw >= nq) return;
-    const int32_t n0 = (int32_t)(chunk * 64 + 4 * col);  // this lane's 4 neurons
-    const bool live = n0 < nc;                            // nc % 4 == 0: all 4 or none
-    const uint64_t off = (uint64_t)(live ? 4 * col : 0) * 4u;
-    f4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (metric_is_l2(M) && live) cn4 = *reinterpret_cast<const f4 *>(a.cn + n0);
+    const int32_t n0 = (int32_t)(chunk * CW + NPL * col);  // this lane's NPL neurons
+    // a lane past nc reads the chunk's first columns (fp32: nc % 4 == 0, so a
+    // lane's 4 neurons are all live or all dead; fp16: the blocked copy is
+    // padded to whole chunks, and each neuron is checked at the end)
+    const bool live = n0 < nc;
+    const uint64_t off = (uint64_t)(HALF || live ? NPL * col : 0) * ESZ;
+    float cnv[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+        cnv[e] = (metric_is_l2(M) && n0 + e < nc) ? a.cn[n0 + e] : 0.0f;
     unsigned long long *mine = reinterpret_cast<unsigned long long *>(part + (int64_t)x * nq);
     const uint64_t cbase = reinterpret_cast<uint64_t>(a.CT) + (uint64_t)chunk * a.cstride;
     const __attribute__((address_space(4))) int32_t *indptr =
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
             vv = 0.0f;
         }
         if (lane < B) {
-            rec[wave][p][lane] = cbase + (uint64_t)kk * (uint64_t)ld * 4u;  // past the end: row 0,
+            rec[wave][p][lane] = cbase + (uint64_t)kk * (uint64_t)ld * ESZ;  // past the end: row 0,
             wgt[wave][p][lane] = vv;                                        // weight 0
         }
         if (s_t == 0) i_ok = s_ok;
@@ -383,25 +392,26 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
         stage();
     };
 
-    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) acc[e] = 0.0f;
     auto finalize = [&](int32_t n, bool ok) {
         const int64_t q = lw + (int64_t)__builtin_amdgcn_readfirstlane(n) * wpg;
-        f4 s4 = acc;
+        float sv[NPL];
         // combine the four lane groups' partial sums: (p0 + p1) + (p2 + p3)
 #pragma unroll
-        for (int s2 = 16; s2 <= 32; s2 <<= 1) {
-            s4.x += __shfl_xor(s4.x, s2);
-            s4.y += __shfl_xor(s4.y, s2);
-            s4.z += __shfl_xor(s4.z, s2);
-            s4.w += __shfl_xor(s4.w, s2);
+        for (int e = 0; e < NPL; ++e) {
+            sv[e] = acc[e];
+            sv[e] += __shfl_xor(sv[e], 16);
+            sv[e] += __shfl_xor(sv[e], 32);
         }
         float be = __builtin_inff();
         int32_t bi = -1;
-        if (live && ok) {
+        if (ok) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float r = rank_value<M>(s4[e], cn4[e]);
-                if (r < be) {
+            for (int e = 0; e < NPL; ++e) {
+                const float r = rank_value<M>(sv[e], cnv[e]);
+                if (n0 + e < nc && r < be) {
                     be = r;
                     bi = n0 + e;
                 }
@@ -418,7 +428,20 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
         }
         if (lane == 0 && ok && bi >= 0)
             atomicMin(mine + q, (unsigned long long)pack_key(be, (uint32_t)bi));
-        acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) acc[e] = 0.0f;
+    };
+    // one load unit into the running sums: NPL products of weight w and the
+    // slot's values (fp16 values are widened exactly to fp32 first)
+    auto fma_slot = [&](float w, const f4 &v) {
+        if constexpr (HALF) {
+            const h8 hv = __builtin_bit_cast(h8, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)hv[e], acc[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+        }
     };
 
     // ---- prologue: batch 0 staged, made current, and issued into the ring
@@ -445,11 +468,7 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
 #pragma unroll
             for (int j = 0; j < N; ++j) {
                 const int r = 4 * j + grp;
-                const float w = wgt[wave][pp][r];
-                acc.x = __builtin_fmaf(w, buf[j].x, acc.x);
-                acc.y = __builtin_fmaf(w, buf[j].y, acc.y);
-                acc.z = __builtin_fmaf(w, buf[j].z, acc.z);
-                acc.w = __builtin_fmaf(w, buf[j].w, acc.w);
+                fma_slot(wgt[wave][pp][r], buf[j]);
                 buf[j] = *reinterpret_cast<const __attribute__((address_space(1))) f4 *>(
                     rec[wave][par][r] + off);
                 // keep slot j's refill after its use (hoisting the loads would
@@ -460,11 +479,7 @@ __global__ __launch_bounds__(256) void k_bmu_csr_ring(const CsrArgs a, uint64_t 
         } else {  // last rotation: nothing left to issue
 #pragma unroll
             for (int j = 0; j < N; ++j) {
-                const float w = wgt[wave][pp][4 * j + grp];
-                acc.x = __builtin_fmaf(w, buf[j].x, acc.x);
-                acc.y = __builtin_fmaf(w, buf[j].y, acc.y);
-                acc.z = __builtin_fmaf(w, buf[j].z, acc.z);
-                acc.w = __builtin_fmaf(w, buf[j].w, acc.w);
+                fma_slot(wgt[wave][pp][4 * j + grp], buf[j]);
             }
             finalize(q_prev, ok_prev);  // the stream's last batch ends its query
             break;
@@ -524,10 +539,10 @@ hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
         timing_before(st, "k_bmu_csr");
         if (ring) {
             switch (metric) {
-            case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MIN, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
-            case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MAX, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
-            case COS_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MAX, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
-            default: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MIN, kCsrRing>), grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MIN, kCsrRing, false>), grid, block, 0, st, a, part, r, groups); break;
+            case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MAX, kCsrRing, false>), grid, block, 0, st, a, part, r, groups); break;
+            case COS_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MAX, kCsrRing, false>), grid, block, 0, st, a, part, r, groups); break;
+            default: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MIN, kCsrRing, false>), grid, block, 0, st, a, part, r, groups); break;
             }
         } else if (ncw == 32) {
             switch (metric) {
@@ -543,6 +558,42 @@ hipError_t launch_csr(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
             case COS_MAX: hipLaunchKernelGGL((k_bmu_csr<COS_MAX, 1>), grid, block, 0, st, a, part, r, groups); break;
             default: hipLaunchKernelGGL((k_bmu_csr<COS_MIN, 1>), grid, block, 0, st, a, part, r, groups); break;
             }
+        }
+        err = hipGetLastError();
+        timing_after(st);
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_min_partials, dim3((unsigned)((a.nq + 255) / 256)), block, 0, st, part,
+                       groups, a.nq, a.keys);
+    return hipGetLastError();
+}
+
+// fp16 codebook in the 128-neuron blocked layout (feature k of neuron
+// 128 b + j at CT + b * cstride + (k * 128 + j) halves): the pipelined scan
+// with eight neurons per lane, 128-neuron chunks (a 4 MiB slice at
+// d = 16,384), every value widened exactly to fp32 before its FMA.
+hipError_t launch_csr_f16(const CsrArgs &a0, int metric, hipStream_t st, int n_cu,
+                          uint64_t *part) {
+    CsrArgs a = a0;
+    constexpr int CW = 128;
+    a.n_chunks = (a.nc + CW - 1) / CW;
+    const int32_t groups = (int32_t)(a.n_chunks < 8 ? a.n_chunks : 8);
+    const int64_t cu = n_cu > 0 ? n_cu : 256;
+    int64_t per_group = (cu * kCsrRingWgPerCu) / groups;
+    const int64_t need = (a.nq + 3) / 4;
+    if (per_group > need) per_group = need;
+    if (per_group < 1) per_group = 1;
+    const dim3 grid((unsigned)(per_group * groups)), block(256);
+    const int64_t rounds = (a.n_chunks + groups - 1) / groups;
+    hipError_t err = launch_fill_keys(part, (int64_t)groups * a.nq, st);
+    if (err != hipSuccess) return err;
+    for (int64_t r = 0; r < rounds; ++r) {
+        timing_before(st, "k_bmu_csr");
+        switch (metric) {
+        case L2SQ_MIN: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MIN, kCsrRing, true>), grid, block, 0, st, a, part, r, groups); break;
+        case L2SQ_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<L2SQ_MAX, kCsrRing, true>), grid, block, 0, st, a, part, r, groups); break;
+        case COS_MAX: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MAX, kCsrRing, true>), grid, block, 0, st, a, part, r, groups); break;
+        default: hipLaunchKernelGGL((k_bmu_csr_ring<COS_MIN, kCsrRing, true>), grid, block, 0, st, a, part, r, groups); break;
         }
         err = hipGetLastError();
         timing_after(st);

@@ -58,8 +58,23 @@ __global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X
 // order.  Vector width does not change any column's order of summation.
 constexpr int kColWaves = 16;
 
-template <bool VEC>
-__global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__restrict__ X,
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// four consecutive values widened to fp32 (fp16 exactly)
+template <typename T>
+__device__ __forceinline__ f32x4 load4_f32(const T *p) {
+    if constexpr (sizeof(T) == 2) {
+        const f16x4 h = *reinterpret_cast<const f16x4 *>(p);
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(p);
+    }
+}
+
+// T = float, or _Float16 for the fp16 blocked codebook (CB = 128, with
+// 128-column blocks); plain fp32 layouts use CB = 64.
+template <typename T, bool VEC, int CB = 64>
+__global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const T *__restrict__ X,
                                                                int64_t cols, int64_t ld,
                                                                int64_t cs, int32_t d,
                                                                float *__restrict__ out) {
@@ -71,11 +86,11 @@ __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__r
     const int32_t k1 = (int32_t)((int64_t)d * (wave + 1) / kColWaves);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c0 < cols) {
-        const float *x = X + (c0 >> 6) * cs + (c0 & 63);
+        const T *x = X + (c0 / CB) * cs + (c0 % CB);
         if constexpr (VEC) {
 #pragma unroll 8
             for (int32_t k = k0; k < k1; ++k) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(x + (int64_t)k * ld);
+                const f32x4 v = load4_f32(x + (int64_t)k * ld);
                 acc.x = __builtin_fmaf(v.x, v.x, acc.x);
                 acc.y = __builtin_fmaf(v.y, v.y, acc.y);
                 acc.z = __builtin_fmaf(v.z, v.z, acc.z);
@@ -84,7 +99,7 @@ __global__ __launch_bounds__(64 * kColWaves) void k_col_sqnorms(const float *__r
         } else {
 #pragma unroll 8
             for (int32_t k = k0; k < k1; ++k) {
-                const float v = x[(int64_t)k * ld];
+                const float v = (float)x[(int64_t)k * ld];
                 acc.x = __builtin_fmaf(v, v, acc.x);
             }
         }
@@ -148,11 +163,11 @@ hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int64_t 
                      ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
     if (vec)
-        hipLaunchKernelGGL(k_col_sqnorms<true>, dim3(blocks_for(cols, 256)), dim3(64 * kColWaves),
-                           0, st, X, cols, ld, cs, d, out);
+        hipLaunchKernelGGL((k_col_sqnorms<float, true>), dim3(blocks_for(cols, 256)),
+                           dim3(64 * kColWaves), 0, st, X, cols, ld, cs, d, out);
     else
-        hipLaunchKernelGGL(k_col_sqnorms<false>, dim3(blocks_for(cols, 64)), dim3(64 * kColWaves),
-                           0, st, X, cols, ld, cs, d, out);
+        hipLaunchKernelGGL((k_col_sqnorms<float, false>), dim3(blocks_for(cols, 64)),
+                           dim3(64 * kColWaves), 0, st, X, cols, ld, cs, d, out);
     return hipGetLastError();
 }
 
@@ -177,6 +192,48 @@ __global__ __launch_bounds__(256) void k_block_codebook(const float *__restrict_
             CB[e] = n < nc ? CT[k * ldct + n] : 0.0f;
         }
     }
+}
+
+// Column norms of the fp16 128-column blocked codebook (feature k of column
+// j at X[(j / 128) * d * 128 + k * 128 + j % 128]).
+hipError_t launch_col_sqnorms_f16(const uint16_t *X, int64_t cols, int32_t d, float *out,
+                                  hipStream_t st) {
+    if (cols <= 0) return hipSuccess;
+    const _Float16 *Xh = reinterpret_cast<const _Float16 *>(X);
+    const int64_t cs = (int64_t)d * 128;
+    const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 7) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    if (vec)
+        hipLaunchKernelGGL((k_col_sqnorms<_Float16, true, 128>), dim3(blocks_for(cols, 256)),
+                           dim3(64 * kColWaves), 0, st, Xh, cols, (int64_t)128, cs, d, out);
+    else
+        hipLaunchKernelGGL((k_col_sqnorms<_Float16, false, 128>), dim3(blocks_for(cols, 64)),
+                           dim3(64 * kColWaves), 0, st, Xh, cols, (int64_t)128, cs, d, out);
+    return hipGetLastError();
+}
+
+// 128-column blocked fp16 copy of a feature-major fp32 codebook: CB[b][k][j]
+// = fp16(CT[k * ldct + 128 b + j]) (round to nearest even) for 128 b + j < nc,
+// 0 past nc.  One thread per value.
+__global__ __launch_bounds__(256) void k_block_codebook_f16(const float *__restrict__ CT, int64_t nc,
+                                                           int64_t ldct, int32_t d, int64_t total,
+                                                           _Float16 *__restrict__ CB) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t j = e & 127, k = (e >> 7) % d, b = (e >> 7) / d;
+        const int64_t n = b * 128 + j;
+        CB[e] = n < nc ? (_Float16)CT[k * ldct + n] : (_Float16)0.0f;
+    }
+}
+
+hipError_t launch_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
+                                     uint16_t *CB, hipStream_t st) {
+    const int64_t total = (nc + 127) / 128 * 128 * (int64_t)d;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_block_codebook_f16, dim3((unsigned)blocks), dim3(256), 0, st, CT, nc,
+                       ldct, d, total, reinterpret_cast<_Float16 *>(CB));
+    return hipGetLastError();
 }
 
 hipError_t launch_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,

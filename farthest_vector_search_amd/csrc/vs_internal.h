@@ -128,6 +128,12 @@ hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int64_t 
                               float *out, hipStream_t st);
 hipError_t launch_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
                                  hipStream_t st);
+// fp16 codebook, 128-neuron blocks: feature k of neuron 128 b + j at
+// CB[(b * d + k) * 128 + j]
+hipError_t launch_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
+                                     uint16_t *CB, hipStream_t st);
+hipError_t launch_col_sqnorms_f16(const uint16_t *X, int64_t cols, int32_t d, float *out,
+                                  hipStream_t st);
 hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
                                   int64_t nnz, float *out, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t st,
@@ -143,6 +149,9 @@ hipError_t launch_dense_q16(const DenseArgs &a, int metric, bool gather, hipStre
 // CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
 int32_t csr_groups(int64_t nc);
 hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);
+// CSR scan over the fp16 128-neuron blocked codebook (a.CT points at it,
+// a.ldct = 128, a.cstride = d * 256)
+hipError_t launch_csr_f16(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);
 hipError_t launch_finalize(const uint64_t *keys, const float *qn, int64_t nq, int metric,
                            int32_t *idx_out, float *score_out, hipStream_t st);
 hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mask,

@@ -143,6 +143,34 @@ int vs_bmu_search_csr_blocked(const int32_t *indptr, const int32_t *indices,
                               void *stream);
 
 /*
+ * fp16 storage of the sparse-query search's codebook, fp32 arithmetic
+ * ["Issue 9-014", "FP16 storage (compounding optimization)": store the table
+ * in half precision, load FP16 and compute FP32; BMU, section 4 "The levers"
+ * (vectorised loads)].  The codebook is held as IEEE binary16 in a
+ * 128-neuron blocked layout: feature k of neuron 128 b + j (0 <= j < 128) at
+ * CB16[(b * d + k) * 128 + j].  Every value is widened exactly to fp32 before
+ * it is multiplied, and sums, norms and scores are fp32, so the results are
+ * those of vs_bmu_search_csr over the fp16-rounded codebook, bit for bit;
+ * the codebook bytes (the scan's roof) are halved.
+ *   vs_csr_blocked_f16_bytes   size of CB16 in bytes: ceil(nc / 128) * 128
+ *                              * d * 2 (0 for invalid sizes).  Host-only.
+ *   vs_csr_block_codebook_f16  writes CB16 from a feature-major fp32 CT (d
+ *                              rows of nc, row stride ldct >= nc), rounding
+ *                              to nearest even; columns past nc are 0.
+ *                              CB16 must be 16-byte aligned, caller-owned.
+ *   vs_bmu_search_csr_blocked_f16  the search over CB16; other arguments and
+ *                              workspace as for vs_bmu_search_csr.
+ */
+size_t vs_csr_blocked_f16_bytes(int64_t nc, int32_t d);
+int vs_csr_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
+                              uint16_t *CB16, void *stream);
+int vs_bmu_search_csr_blocked_f16(const int32_t *indptr, const int32_t *indices,
+                                  const float *values, int64_t nq, int64_t nnz,
+                                  const uint16_t *CB16, int64_t nc, int32_t d, int32_t metric,
+                                  int32_t *idx_out, float *score_out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * One step of the greedy diversity sequence [DIV] for nseq sequences at once.
  *   C          n x d float32, unit-norm rows (the embedding table).
  *   last_pick  int32[nseq]: each sequence's reference row (its last pick).

@@ -149,6 +149,28 @@ def test_csr_blocked_validation(L):
     assert call(ws_bytes=10) == 4
 
 
+def test_csr_f16_validation(L):
+    assert L.vs_csr_blocked_f16_bytes(1, 1) == 256
+    assert L.vs_csr_blocked_f16_bytes(129, 10) == 2 * 128 * 10 * 2
+    assert L.vs_csr_blocked_f16_bytes(0, 3) == 0
+    blk = lambda CT=FAKE, nc=16, ld=16, d=8, CB=FAKE: L.vs_csr_block_codebook_f16(
+        _P(CT), nc, ld, d, _P(CB), None)
+    assert blk(ld=15) == 2
+    assert blk(CT=0) == 1
+    assert blk(CB=FAKE + 8) == 5  # 16-byte alignment
+
+    def call(indptr=FAKE, indices=FAKE, values=FAKE, nq=3, nnz=10, CB=FAKE, nc=16, d=8,
+             metric=0, idx=FAKE, score=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_bmu_search_csr_blocked_f16(_P(indptr), _P(indices), _P(values), nq, nnz,
+                                               _P(CB), nc, d, metric, _P(idx), _P(score),
+                                               _P(ws), ws_bytes, None)
+    assert call(metric=9) == 3
+    assert call(nc=0) == 2
+    assert call(CB=0) == 1
+    assert call(CB=FAKE + 8) == 5
+    assert call(ws_bytes=10) == 4
+
+
 def test_diversity_validation(L):
     def call(C=FAKE, n=100, d=8, pick=FAKE, mask=FAKE, nseq=5, idx=FAKE, score=FAKE, ws=FAKE,
              ws_bytes=1 << 20):

@@ -316,6 +316,54 @@ def test_csr_blocked_matches_plain(metric, nc, chunk):
     csr_parity(indptr, indices, values, CT, metric)
 
 
+def run_csr_f16(indptr, indices, values, CT, metric, pad=0):
+    CB16 = vs.vs_csr_block_codebook_f16(padded(CT, pad))
+    idx, score = vs.vs_bmu_search_csr_blocked_f16(T(indptr), T(indices), T(values), CB16,
+                                                  CT.shape[1], metric, d=CT.shape[0])
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy()
+
+
+def f16_rounded(CT):
+    """The codebook as the fp16 path stores it (IEEE binary16, nearest even),
+    held in fp32 (exact)."""
+    return CT.astype(np.float16).astype(np.float32)
+
+
+@pytest.mark.parametrize("nc,pad", [(1, 0), (100, 0), (128, 0), (300, 5), (1030, 0)])
+def test_csr_block_codebook_f16_layout(nc, pad):
+    """The fp16 blocked copy holds fp16(feature k of neuron 128 b + j) at
+    (b d + k) 128 + j and zeros past nc: numpy's float16 rounding (nearest
+    even) bit for bit."""
+    d = 29
+    (r,) = synth.rng_children(4200 + nc, 1)
+    CT = synth.normal(r, (d, nc), std=2.0)
+    CB = vs.vs_csr_block_codebook_f16(padded(CT, pad)).cpu().numpy()
+    nb = (nc + 127) // 128
+    exp = np.zeros((nb, d, 128), np.float16)
+    for b in range(nb):
+        w = min(128, nc - 128 * b)
+        exp[b, :, :w] = CT[:, 128 * b:128 * b + w].astype(np.float16)
+    assert CB.shape == (nb * d * 128,)
+    assert np.array_equal(CB.reshape(nb, d, 128).view(np.uint16), exp.view(np.uint16))
+
+
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+@pytest.mark.parametrize("nc", [1, 100, 700, 1028])
+def test_csr_f16_storage(metric, nc):
+    """fp16 storage, fp32 arithmetic: bit-identical to the fp32 search over
+    the fp16-rounded codebook, which the oracle checks."""
+    empty = () if metric in (2, 3) else (0, 5)
+    indptr, indices, values, CT = csr_case(70, 300, nc, 0.05, key=nc * 16 + metric,
+                                           empty_rows=empty)
+    CT16 = f16_rounded(CT)
+    a = run_csr_f16(indptr, indices, values, CT, metric)
+    b = run_csr(indptr, indices, values, CT16, metric)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    csr_parity(indptr, indices, values, CT16, metric)
+
+
 def csr_select(indptr, indices, values, rows):
     rows = np.asarray(rows)
     ptr = np.concatenate([[0], np.cumsum(indptr[rows + 1] - indptr[rows])]).astype(np.int32)
@@ -348,6 +396,7 @@ def test_workload_4_sampled():
     bidx, bscore = run_csr_blocked(w["indptr"], w["indices"], w["values"], w["CT"], 0)
     assert np.array_equal(idx, bidx)
     assert np.array_equal(score.view(np.uint32), bscore.view(np.uint32))
+    del bidx, bscore
     sel = synth.sample_queries(w["nq"], 256, key=4)
     ptr = w["indptr"]
     sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
@@ -368,3 +417,35 @@ def test_workload_4_sampled():
                              for i, j in zip(r, c)]))
     assert not fails, fails
     assert (idx >= 0).all()
+
+
+@pytest.mark.slow
+def test_workload_4_f16_storage():
+    """The full-size sparse workload with the codebook stored in fp16: equal,
+    bit for bit, to the fp32 search over the fp16-rounded codebook, and 256
+    seeded rows checked one by one against the oracle on that codebook."""
+    w = synth.workload(4)
+    CT16 = f16_rounded(w["CT"])
+    idx, score = run_csr_f16(w["indptr"], w["indices"], w["values"], w["CT"], 0)
+    ridx, rscore = run_csr(w["indptr"], w["indices"], w["values"], CT16, 0, pad=64)
+    assert np.array_equal(idx, ridx)
+    assert np.array_equal(score.view(np.uint32), rscore.view(np.uint32))
+    sel = synth.sample_queries(w["nq"], 256, key=44)
+    ptr = w["indptr"]
+    sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
+    sub_idx = np.concatenate([w["indices"][ptr[i]:ptr[i + 1]] for i in sel])
+    sub_val = np.concatenate([w["values"][ptr[i]:ptr[i + 1]] for i in sel])
+    col_sq = oracle.sqnorms(CT16, feature_major=True, threads=16)
+    o_idx, o_val, o_gap = oracle.csr(sub_ptr, sub_idx, sub_val, CT16, 0, col_sq=col_sq,
+                                     threads=16)
+    qn = np.array([np.sum(sub_val[sub_ptr[i]:sub_ptr[i + 1]].astype(np.float64) ** 2)
+                   for i in range(len(sel))])
+    fails, stats = check(idx[sel], score[sel], o_idx, o_val, o_gap, 0, 1e-2 * (qn + 1.0),
+                         lambda r, c: np.array([
+                             oracle.csr(np.array([0, sub_ptr[i + 1] - sub_ptr[i]], np.int32),
+                                        sub_idx[sub_ptr[i]:sub_ptr[i + 1]],
+                                        sub_val[sub_ptr[i]:sub_ptr[i + 1]],
+                                        np.ascontiguousarray(CT16[:, j:j + 1]), 0,
+                                        col_sq=col_sq[j:j + 1])[1][0]
+                             for i, j in zip(r, c)]))
+    assert not fails, fails
