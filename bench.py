@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--div-mode", choices=["step", "gram"], default="step",
+                    help="diversity workload: 'step' runs the MFMA scan every step, 'gram' "
+                         "builds the table's Gram matrix once per run and scans one row of it "
+                         "per sequence and step")
     ap.add_argument("--csr-storage", choices=["f32", "f16"], default="f32",
                     help="sparse workload: codebook storage type ('f16': the 128-neuron "
                          "blocked fp16 copy, fp32 arithmetic)")
@@ -139,17 +143,35 @@ def setup(k, torch, vs, a):
         ws = torch.empty(vs.lib().vs_diversity_step_workspace(n, d, nseq), dtype=torch.uint8,
                          device=dev)
 
-        def step():
-            mask.copy_(mask0)
-            last = seeds
-            for t in range(steps):
-                vs.vs_diversity_step(C, last, mask, idx_out=picks[t], workspace=ws,
-                                     want_score=False)
-                last = picks[t]
+        if a.div_mode == "gram":
+            # one run = the Gram matrix of the table (once) + `steps` scans of
+            # one Gram row per sequence
+            ldg = (n + 63) // 64 * 64
+            Gbuf = torch.empty((n, ldg), dtype=torch.float32, device=dev)
+
+            def step():
+                mask.copy_(mask0)
+                G = vs.vs_diversity_gram(C, out=Gbuf)
+                last = seeds
+                for t in range(steps):
+                    vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t],
+                                              want_score=False)
+                    last = picks[t]
+            # algorithmic bytes of one scan: a row of n fp32 per sequence, its
+            # mask row read and written, the pick read and written
+            w["scan_bytes"] = nseq * (4 * n + 8 * W + 8)
+        else:
+            def step():
+                mask.copy_(mask0)
+                last = seeds
+                for t in range(steps):
+                    vs.vs_diversity_step(C, last, mask, idx_out=picks[t], workspace=ws,
+                                         want_score=False)
+                    last = picks[t]
         pairs = nseq * n * steps
         flops = 2.0 * d * pairs
         cfg = dict(workload=w["name"], n=n, d=d, nseq=nseq, steps_per_run=steps,
-                   metric="cos_min_masked")
+                   metric="cos_min_masked", mode=a.div_mode)
         return w, step, pairs, flops, steps, cfg
     # sparse
     indptr = torch.from_numpy(w["indptr"]).to(dev)
@@ -408,7 +430,12 @@ def main():
     launches = max(kt.launches, 1)
     kernel_ms = kt.ms / launches
     kernel_s_total = kt.ms * 1e-3
-    if w["kind"] in ("dense", "diversity"):
+    if w["kind"] == "diversity" and a.div_mode == "gram":
+        # the Gram scans are HBM-bound reads of one table row per sequence
+        achieved = w["scan_bytes"] * launches / kernel_s_total / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    elif w["kind"] in ("dense", "diversity"):
         achieved = flops * a.steps / kernel_s_total / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4))
@@ -424,7 +451,8 @@ def main():
     roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
-    roof["traffic"] = load_traffic(a.traffic_json, DOMINANT[a.workload], cfg["workload"])
+    roof["traffic"] = (None if (w["kind"] == "diversity" and a.div_mode == "gram") else
+                       load_traffic(a.traffic_json, DOMINANT[a.workload], cfg["workload"]))
     out = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,

@@ -14,6 +14,8 @@ Functions (same names as the C entry points):
     vs_csr_block_codebook_f16(CT)                      -> CB16 (fp16, 128-neuron blocks)
     vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, metric) -> (idx, score)
     vs_diversity_step(C, last_pick, mask_bits)         -> (idx, score)
+    vs_diversity_gram(C)                               -> G (n x ldg Gram matrix)
+    vs_diversity_step_gram(G, n, last_pick, mask_bits) -> (idx, score)
     vs_candidate_norms(C, feature_major=False)         -> norms
     vs_tile_rows(cache_bytes, d, bytes_per_value)      -> int (host only)
 Metrics: VS_L2SQ_MIN, VS_L2SQ_MAX, VS_COS_MAX, VS_COS_MIN.
@@ -37,6 +39,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_csr_worksp
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_diversity_gram", "vs_diversity_step_gram",
            "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
            "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
 
@@ -81,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
     L.vs_diversity_step_workspace.restype = SZ
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
+    L.vs_diversity_gram.argtypes = [P, I64, I32, P, I64, P]
+    L.vs_diversity_step_gram.argtypes = [P, I64, I64, P, P, I64, P, P, P]
     L.vs_candidate_norms.argtypes = [P, I64, I32, I32, P, P]
     L.vs_tile_rows.argtypes = [I64, I32, I32]
     L.vs_tile_rows.restype = I64
@@ -92,7 +97,8 @@ def lib() -> ctypes.CDLL:
     L.vs_version.restype = ctypes.c_char_p
     for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_csr_block_codebook",
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
-                 "vs_bmu_search_csr_blocked_f16", "vs_diversity_step",
+                 "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
+                 "vs_diversity_step_gram",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
         getattr(L, name).restype = ctypes.c_int
@@ -357,6 +363,56 @@ def vs_diversity_step(C, last_pick, mask_bits, idx_out=None, score_out=None, wor
                                  _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_diversity_step")
+    return idx_out, score_out
+
+
+def vs_diversity_gram(C, out=None):
+    """Gram matrix of the table C (n x d, unit rows) by the diversity step's
+    own arithmetic: returns G, an n x ldg float32 view (ldg = n rounded up to
+    a multiple of 64) whose entry [r, j] is C[r] . C[j]."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    n, d = C.shape
+    ldg = (n + 63) // 64 * 64
+    if out is None:
+        out = torch.empty((n, ldg), dtype=torch.float32, device=C.device)
+    elif out.dtype != torch.float32 or out.dim() != 2 or out.shape[0] != n \
+            or out.shape[1] < n or out.stride(1) != 1 or out.stride(0) % 4:
+        raise ValueError("out must be a float32 n x ldg matrix (ldg >= n, ldg % 4 == 0)")
+    with torch.cuda.device(C.device):
+        rc = L.vs_diversity_gram(_ptr(C), n, d, _ptr(out), out.stride(0), _stream(C.device))
+    _check(rc, "vs_diversity_gram")
+    return out[:, :n]
+
+
+def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None,
+                           want_score: bool = True):
+    """One diversity step for every sequence from a cached Gram matrix G (a
+    view returned by vs_diversity_gram); updates mask_bits in place."""
+    torch = _torch()
+    L = lib()
+    if not isinstance(G, torch.Tensor) or not G.is_cuda or G.dtype != torch.float32 \
+            or G.dim() != 2 or G.stride(1) != 1 or G.shape[0] != G.shape[1]:
+        raise ValueError("G must be a square float32 CUDA matrix view with unit column stride")
+    _dev(last_pick, "last_pick", torch.int32, 1)
+    n = G.shape[0]
+    nseq = last_pick.numel()
+    W = (n + 31) // 32
+    if mask_bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask_bits must be int32 or uint32 words")
+    _dev(mask_bits, "mask_bits", mask_bits.dtype, 2)
+    if tuple(mask_bits.shape) != (nseq, W):
+        raise ValueError(f"mask_bits must be [{nseq}, {W}]")
+    dev = G.device
+    if idx_out is None:
+        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_step_gram(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(mask_bits),
+                                      nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
+    _check(rc, "vs_diversity_step_gram")
     return idx_out, score_out
 
 

@@ -415,6 +415,45 @@ VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t
     return VS_OK;
 }
 
+// ---- diversity from a cached Gram matrix -------------------------------------
+
+VS_API int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ldg,
+                             void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || ldg < n || ldg % 4 != 0) return VS_ERR_SHAPE;
+    if (!C || !G) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(G) & 15) != 0) return VS_ERR_ALIGN;
+    if (!vs::q16_supports(d, C, nullptr)) return VS_ERR_UNSUPPORTED;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    vs::DenseArgs a{};
+    a.Q = C;
+    a.C = C;
+    a.nq = n;
+    a.nc = n;
+    a.d = d;
+    a.S = G;
+    a.ld_s = ldg;
+    VS_TRY_HIP(vs::launch_dense_q16_store(a, reinterpret_cast<hipStream_t>(stream), n_cu));
+    return VS_OK;
+}
+
+VS_API int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg,
+                                  const int32_t *last_pick, uint32_t *mask_bits, int64_t nseq,
+                                  int32_t *idx_out, float *score_out, void *stream) {
+    if (n < 1 || n > kMaxIndex || ldg < n || ldg % 4 != 0 || nseq < 0 || nseq > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nseq == 0) return VS_OK;
+    if (!G || !last_pick || !mask_bits || !idx_out) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(G) & 15) != 0 || !al4(last_pick) || !al4(mask_bits) ||
+        !al4(idx_out) || !al4(score_out))
+        return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_div_gram_step(G, n, ldg, last_pick, mask_bits, nseq, idx_out, score_out,
+                                        reinterpret_cast<hipStream_t>(stream)));
+    return VS_OK;
+}
+
 // ---- norms, tile rule, status ---------------------------------------------
 
 VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t feature_major,

@@ -71,11 +71,17 @@ __device__ __forceinline__ int slab_at(int row, int piece) {
 
 }  // namespace
 
-template <int M, bool GATHER, int NSLAB>
+// MODE: kSearch (arg-reduce over Q's rows), kDiversity (queries gathered
+// as C[pick], masked), kStore (write every dot product to S instead).
+enum : int { kSearch = 0, kDiversity = 1, kStore = 2 };
+
+template <int M, int MODE, int NSLAB>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_q16(const DenseArgs a) {
     constexpr int NCH = NSLAB * kCPS;
-    constexpr bool MASKED = GATHER;  // the gathered form is the diversity step
+    constexpr bool GATHER = MODE == kDiversity;
+    constexpr bool MASKED = MODE == kDiversity;
+    constexpr bool STORE = MODE == kStore;
 
     __shared__ __attribute__((aligned(16))) float sA[3][kBC * kBK];
     __shared__ __attribute__((aligned(16))) float sN[3][kBC];  // candidate norms, by item mod 3
@@ -212,6 +218,25 @@ void k_bmu_q16(const DenseArgs a) {
     // ascending order, so strict "<" keeps the lowest index among ties.
     auto epilogue = [&](int32_t ct, int par) {
         const int32_t base = ct * kBC;  // < nc < 2^31
+        if constexpr (STORE) {
+            // S[q][c] for this lane's query column and its rows 16b+4g..+3
+            // (16-byte stores: ld_s % 4 == 0 and S 16-byte aligned)
+            const int64_t q = (int64_t)qt * kBQ + wave * 16 + i16;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t c = (int64_t)base + 16 * b + 4 * g;
+                if (q < nq && c < nc) {
+                    float *dst = a.S + q * a.ld_s + c;
+                    if (c + 4 <= nc) {
+                        *reinterpret_cast<f32x4 *>(dst) = acc[b];
+                    } else {
+                        for (int r = 0; r < 4 && c + r < nc; ++r) dst[r] = acc[b][r];
+                    }
+                }
+                acc[b] = f32x4{};
+            }
+            return;
+        }
         // rows 16b + r of this lane group are live while 16b + r < lim;
         // mask bits of the group shifted down to bit 0 (constant shifts below)
         const int64_t left = nc - base - 4 * g;
@@ -239,6 +264,7 @@ void k_bmu_q16(const DenseArgs a) {
     // Merge the four lane groups (same query, interleaved candidate rows)
     // and publish each query's best with one packed atomicMin.
     auto flush = [&](int32_t qtile) {
+        if constexpr (STORE) return;
 #pragma unroll
         for (int off = 16; off <= 32; off <<= 1) {
             const float oe = __shfl_xor(best, off);
@@ -351,30 +377,30 @@ void k_bmu_q16(const DenseArgs a) {
     }
 }
 
-template <int M, bool GATHER>
+template <int M, int MODE>
 static void dispatch_slabs(const DenseArgs &a, dim3 grid, hipStream_t st) {
     const int nslab = (a.d + kBK - 1) / kBK;
     static_assert(kMaxSlabs == 6 || kMaxSlabs == 12, "slab count table");
     if constexpr (kMaxSlabs == 6) {
         switch (nslab) {
-        case 1: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 1>), grid, dim3(64 * kW), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 2>), grid, dim3(64 * kW), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 3>), grid, dim3(64 * kW), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 4>), grid, dim3(64 * kW), 0, st, a); break;
-        case 5: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 5>), grid, dim3(64 * kW), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 6>), grid, dim3(64 * kW), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 1>), grid, dim3(64 * kW), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 2>), grid, dim3(64 * kW), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 3>), grid, dim3(64 * kW), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 4>), grid, dim3(64 * kW), 0, st, a); break;
+        case 5: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 5>), grid, dim3(64 * kW), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 6>), grid, dim3(64 * kW), 0, st, a); break;
         }
     } else {
         // 64-feature slabs: slab counts rounded up to an even number above 4
         switch (nslab) {
-        case 1: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 1>), grid, dim3(64 * kW), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 2>), grid, dim3(64 * kW), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 3>), grid, dim3(64 * kW), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 4>), grid, dim3(64 * kW), 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 6>), grid, dim3(64 * kW), 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 8>), grid, dim3(64 * kW), 0, st, a); break;
-        case 9: case 10: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 10>), grid, dim3(64 * kW), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_bmu_q16<M, GATHER, 12>), grid, dim3(64 * kW), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 1>), grid, dim3(64 * kW), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 2>), grid, dim3(64 * kW), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 3>), grid, dim3(64 * kW), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 4>), grid, dim3(64 * kW), 0, st, a); break;
+        case 5: case 6: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 6>), grid, dim3(64 * kW), 0, st, a); break;
+        case 7: case 8: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 8>), grid, dim3(64 * kW), 0, st, a); break;
+        case 9: case 10: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 10>), grid, dim3(64 * kW), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 12>), grid, dim3(64 * kW), 0, st, a); break;
         }
     }
 }
@@ -401,18 +427,35 @@ hipError_t launch_dense_q16(const DenseArgs &a0, int metric, bool gather, hipStr
     const dim3 grid((unsigned)a.grid);
     timing_before(st, gather ? "k_bmu_q16<COS_MIN,gather>" : "k_bmu_q16");
     if (gather) {
-        dispatch_slabs<COS_MIN, true>(a, grid, st);
+        dispatch_slabs<COS_MIN, kDiversity>(a, grid, st);
     } else {
         switch (metric) {
-        case L2SQ_MIN: dispatch_slabs<L2SQ_MIN, false>(a, grid, st); break;
-        case L2SQ_MAX: dispatch_slabs<L2SQ_MAX, false>(a, grid, st); break;
-        case COS_MAX: dispatch_slabs<COS_MAX, false>(a, grid, st); break;
-        default: dispatch_slabs<COS_MIN, false>(a, grid, st); break;
+        case L2SQ_MIN: dispatch_slabs<L2SQ_MIN, kSearch>(a, grid, st); break;
+        case L2SQ_MAX: dispatch_slabs<L2SQ_MAX, kSearch>(a, grid, st); break;
+        case COS_MAX: dispatch_slabs<COS_MAX, kSearch>(a, grid, st); break;
+        default: dispatch_slabs<COS_MIN, kSearch>(a, grid, st); break;
         }
     }
     const hipError_t err = hipGetLastError();
     timing_after(st);
     return err;
+}
+
+// Every dot product Q[q] . C[c] written to S[q * ld_s + c] (ld_s >= nc,
+// ld_s % 4 == 0, S 16-byte aligned) by the same MFMA arithmetic, in the
+// same per-pair order, as the scans above: each stored value equals,
+// bit for bit, the dot product those scans rank.
+hipError_t launch_dense_q16_store(const DenseArgs &a0, hipStream_t st, int n_cu) {
+    DenseArgs a = a0;
+    const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
+    a.n_ctiles = (a.nc + kBC - 1) / kBC;
+    a.n_items = nqt * a.n_ctiles;
+    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256) * (8 / kW);
+    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    a.split = (a.grid % 8 == 0 && a.n_ctiles >= 8 && a.nq < a.nc) ? 8 : 1;
+    const dim3 grid((unsigned)a.grid);
+    dispatch_slabs<COS_MIN, kStore>(a, grid, st);  // not a dominant kernel: no timing events
+    return hipGetLastError();
 }
 
 }  // namespace vs

@@ -1,0 +1,95 @@
+// div_gram.hip -- the diversity step from a cached Gram matrix.
+//
+// "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache Locality",
+// "Current Behavior": every step ranks, for each sequence, all unmasked rows
+// by their cosine to the sequence's reference and picks the most different
+// one.  With the last pick as the reference, every score a run can need is
+// an entry of the table's Gram matrix G = C C^T, so G is computed once (by
+// the same MFMA arithmetic as the per-step scan, so each entry equals, bit
+// for bit, the dot product the scan would rank) and a step becomes a masked
+// arg-min over one row of G per sequence: an HBM-bound read of n floats
+// instead of a d-long dot product per candidate.
+//
+// One wave per sequence: lanes read the reference's row four floats at a
+// time (lane l: columns 256 i + 4 l .. + 3, ascending), skip masked and
+// padded columns, keep the lowest value with strict "<" (so the lowest
+// index among equal values), then the wave merges (value, index) pairs
+// lexicographically.  -0 and +0 compare equal and the score is reported
+// with the sign folded, as the packed-key path does; NaN is never picked.
+#include "vs_internal.h"
+
+namespace vs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_div_gram_step(const float *__restrict__ G, int64_t n,
+                                                      int64_t ldg,
+                                                      const int32_t *__restrict__ pick,
+                                                      uint32_t *__restrict__ mask,
+                                                      int64_t nseq, int32_t *__restrict__ idx_out,
+                                                      float *__restrict__ score_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (s >= nseq) return;
+    const int64_t W = (n + 31) / 32;
+    const int64_t r = pick[s];
+    if (r < 0 || r >= n) {  // no reference: no pick, mask unchanged
+        if (lane == 0) {
+            idx_out[s] = -1;
+            if (score_out) score_out[s] = __builtin_nanf("");
+        }
+        return;
+    }
+    const float *row = G + r * ldg;
+    const uint32_t *mrow = mask + s * W;
+    float best = __builtin_inff();
+    int64_t bidx = -1;
+    for (int64_t j0 = 4 * (int64_t)lane; j0 < n; j0 += 256) {
+        // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
+        // row's padded storage even past n
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
+        const uint32_t mw = mrow[j0 >> 5] >> (j0 & 31);  // j0 % 32 <= 28: 4 bits in one word
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = v[e];
+            const bool live = j0 + e < n && !((mw >> e) & 1u);
+            if (live && x < best) {
+                best = x;
+                bidx = j0 + e;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int64_t oi = __shfl_xor(bidx, off);
+        if (oi >= 0 && (bidx < 0 || ob < best || (ob == best && oi < bidx))) {
+            best = ob;
+            bidx = oi;
+        }
+    }
+    if (lane == 0) {
+        if (bidx < 0) {
+            idx_out[s] = -1;
+            if (score_out) score_out[s] = __builtin_nanf("");
+        } else {
+            idx_out[s] = (int32_t)bidx;
+            if (score_out) score_out[s] = best == 0.0f ? 0.0f : best;
+            mask[s * W + (bidx >> 5)] |= 1u << (bidx & 31);
+        }
+    }
+}
+
+hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
+                                uint32_t *mask, int64_t nseq, int32_t *idx_out,
+                                float *score_out, hipStream_t st) {
+    if (nseq <= 0) return hipSuccess;
+    timing_before(st, "k_div_gram_step");
+    hipLaunchKernelGGL(k_div_gram_step, dim3((unsigned)((nseq + 3) / 4)), dim3(256), 0, st, G, n,
+                       ldg, pick, mask, nseq, idx_out, score_out);
+    const hipError_t err = hipGetLastError();
+    timing_after(st);
+    return err;
+}
+
+}  // namespace vs

@@ -103,6 +103,8 @@ struct DenseArgs {
     int64_t n_ctiles;
     int32_t grid;           // launched workgroups (for the item split)
     int32_t split;          // 1, or 8: candidate tiles split into one range per XCD
+    float *S;               // score block (store mode): S[q * ld_s + c]
+    int64_t ld_s;
 };
 
 struct CsrArgs {
@@ -146,6 +148,12 @@ hipError_t launch_dense_qreg(const DenseArgs &a, int metric, hipStream_t st, int
 bool q16_supports(int32_t d, const float *C, const float *Q);
 hipError_t launch_dense_q16(const DenseArgs &a, int metric, bool gather, hipStream_t st,
                             int n_cu);
+// every dot product Q[q] . C[c] into a.S (same arithmetic as the scans)
+hipError_t launch_dense_q16_store(const DenseArgs &a, hipStream_t st, int n_cu);
+// one diversity step from a cached score block G (G[r * ldg + j] = C[r] . C[j])
+hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
+                                uint32_t *mask, int64_t nseq, int32_t *idx_out,
+                                float *score_out, hipStream_t st);
 // CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
 int32_t csr_groups(int64_t nc);
 hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);

@@ -190,6 +190,30 @@ int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The diversity step from a cached Gram matrix [DIV "Current Behavior"; the
+ * reference of a step is the sequence's last pick, so every score a run can
+ * need is an entry of G = C C^T].
+ *   vs_diversity_gram       writes G[r * ldg + j] = C[r] . C[j] (fp32) for
+ *                           r, j < n, by the same MFMA arithmetic and
+ *                           per-pair order as vs_diversity_step, so each
+ *                           entry equals bit for bit the dot product that
+ *                           call ranks.  C is n x d, unit-norm rows; needs
+ *                           d % 4 == 0, d <= 768 and C 16-byte aligned
+ *                           (else VS_ERR_UNSUPPORTED).  G is caller-owned,
+ *                           n * ldg floats, 16-byte aligned; ldg >= n and
+ *                           ldg % 4 == 0; columns n .. ldg-1 are not written.
+ *   vs_diversity_step_gram  one step for nseq sequences from G: arguments,
+ *                           mask semantics and results as vs_diversity_step
+ *                           (bit-identical picks, scores and masks); reads
+ *                           one row of G per sequence.  No workspace.
+ */
+int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ldg,
+                      void *stream);
+int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg, const int32_t *last_pick,
+                           uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
+                           float *score_out, void *stream);
+
+/*
  * Squared L2 norms of candidates, float32, fixed summation order (the same
  * values the searches use).  feature_major == 0: C is nc x d (row j);
  * otherwise C is d x nc (column j).  norms_out is float32[nc].

@@ -171,6 +171,27 @@ def test_csr_f16_validation(L):
     assert call(ws_bytes=10) == 4
 
 
+def test_diversity_gram_validation(L):
+    gram = lambda C=FAKE, n=100, d=8, G=FAKE, ld=100: L.vs_diversity_gram(_P(C), n, d, _P(G),
+                                                                           ld, None)
+    assert gram(ld=99) == 2
+    assert gram(ld=102) == 2  # not a multiple of 4
+    assert gram(n=0) == 2
+    assert gram(C=0) == 1
+    assert gram(G=FAKE + 4) == 5
+    assert gram(d=770) == 7  # beyond the register-resident kernel
+    assert gram(d=6) == 7
+
+    def step(G=FAKE, n=100, ld=100, pick=FAKE, mask=FAKE, nseq=5, idx=FAKE, score=FAKE):
+        return L.vs_diversity_step_gram(_P(G), n, ld, _P(pick), _P(mask), nseq, _P(idx),
+                                        _P(score), None)
+    assert step(ld=98) == 2
+    assert step(nseq=0, G=0) == 0
+    assert step(mask=0) == 1
+    assert step(G=FAKE + 8) == 5
+    assert step(pick=FAKE + 2) == 5
+
+
 def test_diversity_validation(L):
     def call(C=FAKE, n=100, d=8, pick=FAKE, mask=FAKE, nseq=5, idx=FAKE, score=FAKE, ws=FAKE,
              ws_bytes=1 << 20):

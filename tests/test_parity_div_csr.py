@@ -100,6 +100,71 @@ def div_kernel(request, monkeypatch):
     return request.param
 
 
+def gpu_chain_gram(C, seeds, steps):
+    """The same chain as gpu_chain, from the cached Gram matrix."""
+    Cd = T(C)
+    nseq = len(seeds)
+    mask = T(seed_masks(C.shape[0], seeds).view(np.int32))
+    last = T(np.asarray(seeds, np.int32))
+    picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    scores = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    G = vs.vs_diversity_gram(Cd)
+    for t in range(steps):
+        vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t], score_out=scores[t])
+        last = picks[t]
+    torch.cuda.synchronize()
+    return (picks.cpu().numpy().T.copy(), scores.cpu().numpy().T.copy(),
+            mask.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("n,d,nseq,steps", [(40, 4, 5, 41), (300, 64, 129, 20),
+                                            (129, 768, 70, 6), (3000, 128, 300, 4),
+                                            (700, 500, 520, 5)])
+def test_diversity_gram_matches_step(n, d, nseq, steps, monkeypatch):
+    """Steps from the cached Gram matrix equal the per-step MFMA scan bit for
+    bit (picks, scores, masks): each Gram entry is the dot product the scan
+    ranks, and the masked arg-min rule is the same."""
+    monkeypatch.setenv("VS_DIV_KERNEL", "q16")
+    C = synth.dense_case(1, n, d, "unit", key=7 * n + d)[1]
+    (r,) = synth.rng_children(950 + n, 1)
+    seeds = r.choice(n, nseq, replace=nseq > n).astype(np.int32)
+    a = gpu_chain(C, seeds, steps)
+    b = gpu_chain_gram(C, seeds, steps)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert np.array_equal(a[2], b[2])
+    fails, _ = validate_chain(C, seeds, *b)
+    assert not fails, fails
+
+
+def test_diversity_gram_entries():
+    """The cached Gram matrix against the oracle's fp64 cosine Gram matrix
+    (unit rows), within fp32 rounding of a 768-term dot product."""
+    C = synth.dense_case(1, 500, 768, "unit", key=99)[1]
+    G = vs.vs_diversity_gram(T(C)).cpu().numpy()
+    ref = oracle.gram_cos(C, threads=8)
+    assert np.abs(G.astype(np.float64) - ref).max() <= 2e-6
+
+
+def test_diversity_gram_invalid_reference():
+    """A reference outside [0, n) yields -1, NaN and leaves the mask alone;
+    a sequence with every row masked yields -1 and NaN."""
+    C = synth.dense_case(1, 100, 8, "unit", key=3)[1]
+    G = vs.vs_diversity_gram(T(C))
+    last = T(np.array([5, -1, 100, 7], np.int32))
+    m = seed_masks(100, [5, 0, 0, 7])
+    m[3, :] = 0xFFFFFFFF
+    mask = T(m.view(np.int32))
+    before = mask.cpu().numpy().copy()
+    idx, score = vs.vs_diversity_step_gram(G, last, mask)
+    idx, score = idx.cpu().numpy(), score.cpu().numpy()
+    after = mask.cpu().numpy()
+    assert idx[1] == -1 and idx[2] == -1 and idx[3] == -1
+    assert np.isnan(score[1:]).all()
+    assert idx[0] >= 0
+    assert np.array_equal(after[1:], before[1:])
+
+
 def test_diversity_walk():
     w = diversity_walk()
     picks, scores, masks = gpu_chain(w["C"], [w["seed"]], len(w["picks"]))
@@ -144,6 +209,18 @@ def test_diversity_invalid_reference(div_kernel):
     assert idx[1] == -1 and idx[2] == -1
     assert idx[0] >= 0 and idx[3] >= 0
     assert np.array_equal(after[1:3], before[1:3])
+
+
+@pytest.mark.slow
+def test_workload_3_gram_chain():
+    """The full diversity workload from the cached Gram matrix: bit-identical
+    to the per-step scan for all 64 steps of 3,584 sequences."""
+    w = synth.workload(3)
+    a = gpu_chain(w["C"], w["seeds"], w["steps"])
+    b = gpu_chain_gram(w["C"], w["seeds"], w["steps"])
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert np.array_equal(a[2], b[2])
 
 
 @pytest.mark.slow
