@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-mode", choices=["fused", "unfused"], default="fused",
+                    help="dense workloads: 'unfused' writes the whole score block, then "
+                         "ranks each row in a second pass (the fusion comparator)")
     ap.add_argument("--div-mode", choices=["step", "gram"], default="step",
                     help="diversity workload: 'step' runs the MFMA scan every step, 'gram' "
                          "builds the table's Gram matrix once per run and scans one row of it "
@@ -124,11 +127,21 @@ def setup(k, torch, vs, a):
         ws = torch.empty(vs.lib().vs_bmu_search_workspace(w["nq"], w["nc"], w["d"], 0),
                          dtype=torch.uint8, device=dev)
 
-        def step():
-            vs.vs_bmu_search(Q, C, 0, idx_out=idx, score_out=score, workspace=ws)
+        if a.dense_mode == "unfused":
+            S = torch.empty((w["nq"], (w["nc"] + 63) // 64 * 64), dtype=torch.float32,
+                            device=dev)
+
+            def step():
+                vs.vs_bmu_search_unfused(Q, C, 0, S=S, idx_out=idx, score_out=score,
+                                         workspace=ws)
+        else:
+            def step():
+                vs.vs_bmu_search(Q, C, 0, idx_out=idx, score_out=score, workspace=ws)
         pairs = w["nq"] * w["nc"]
         flops = 2.0 * w["d"] * pairs
         cfg = dict(workload=w["name"], nq=w["nq"], nc=w["nc"], d=w["d"], metric="l2sq_min")
+        if a.dense_mode == "unfused":
+            cfg["mode"] = "unfused"
         return w, step, pairs, flops, 1, cfg
     if w["kind"] == "diversity":
         n, d, nseq, steps = w["n"], w["d"], w["nseq"], w["steps"]
@@ -451,7 +464,7 @@ def main():
     roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
-    roof["traffic"] = (None if (w["kind"] == "diversity" and a.div_mode == "gram") else
+    roof["traffic"] = (None if "mode" in cfg and cfg["mode"] in ("gram", "unfused") else
                        load_traffic(a.traffic_json, DOMINANT[a.workload], cfg["workload"]))
     out = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps,

@@ -8,6 +8,7 @@ calls raise.
 
 Functions (same names as the C entry points):
     vs_bmu_search(Q, C, metric)                        -> (idx, score)
+    vs_bmu_search_unfused(Q, C, metric)                -> (idx, score) via a score block
     vs_bmu_search_csr(indptr, indices, values, CT, metric) -> (idx, score)
     vs_csr_block_codebook(CT)                          -> CB (64-neuron blocked copy)
     vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric) -> (idx, score)
@@ -35,7 +36,8 @@ STATUS = {0: "VS_OK", 1: "VS_ERR_NULL", 2: "VS_ERR_SHAPE", 3: "VS_ERR_METRIC",
           4: "VS_ERR_WORKSPACE", 5: "VS_ERR_ALIGN", 6: "VS_ERR_INDEX",
           7: "VS_ERR_UNSUPPORTED", 8: "VS_ERR_HIP"}
 
-EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_csr_workspace",
+EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
+           "vs_bmu_search_csr_workspace",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
@@ -69,6 +71,7 @@ def lib() -> ctypes.CDLL:
     L.vs_bmu_search_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_workspace.restype = SZ
     L.vs_bmu_search.argtypes = [P, P, I64, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_bmu_search_unfused.argtypes = [P, P, I64, I64, I32, I32, P, P, P, I64, P, SZ, P]
     L.vs_bmu_search_csr_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_csr_workspace.restype = SZ
     L.vs_bmu_search_csr.argtypes = [P, P, P, I64, I64, P, I64, I64, I32, I32, P, P, P, SZ, P]
@@ -95,7 +98,8 @@ def lib() -> ctypes.CDLL:
     L.vs_status_str.argtypes = [ctypes.c_int]
     L.vs_status_str.restype = ctypes.c_char_p
     L.vs_version.restype = ctypes.c_char_p
-    for name in ("vs_bmu_search", "vs_bmu_search_csr", "vs_csr_block_codebook",
+    for name in ("vs_bmu_search", "vs_bmu_search_unfused", "vs_bmu_search_csr",
+                 "vs_csr_block_codebook",
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
                  "vs_diversity_step_gram",
@@ -177,6 +181,39 @@ def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, worksp
         rc = L.vs_bmu_search(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out), _ptr(score_out),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search")
+    return idx_out, score_out
+
+
+def vs_bmu_search_unfused(Q, C, metric=VS_L2SQ_MIN, S=None, idx_out=None, score_out=None,
+                          workspace=None, want_score: bool = True):
+    """vs_bmu_search through a written score block S (nq x ld_s float32, the
+    unfused comparator; allocated here if not given)."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(Q, "Q", torch.float32, 2)
+    _dev(C, "C", torch.float32, 2)
+    nq, d = Q.shape
+    nc = C.shape[0]
+    if C.shape[1] != d:
+        raise ValueError("Q and C must have the same number of columns")
+    dev = Q.device
+    if S is None:
+        S = torch.empty((nq, (nc + 63) // 64 * 64), dtype=torch.float32, device=dev)
+    elif S.dtype != torch.float32 or S.dim() != 2 or S.shape[0] < nq or S.shape[1] < nc \
+            or S.stride(1) != 1 or S.stride(0) % 4:
+        raise ValueError("S must be a float32 nq x ld_s matrix (ld_s >= nc, ld_s % 4 == 0)")
+    if idx_out is None:
+        idx_out = torch.empty(nq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nq, dtype=torch.float32, device=dev)
+    need = L.vs_bmu_search_workspace(nq, nc, d, m)
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search_unfused(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out),
+                                     _ptr(score_out), _ptr(S), S.stride(0), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_bmu_search_unfused")
     return idx_out, score_out
 
 

@@ -223,6 +223,51 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     return VS_OK;
 }
 
+// ---- unfused comparator: score block, then a per-row pass -------------------
+
+VS_API int vs_bmu_search_unfused(const float *Q, const float *C, int64_t nq, int64_t nc,
+                                 int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
+                                 float *S, int64_t ld_s, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (nq < 0 || nq > kMaxIndex || nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxDim ||
+        ld_s < nc || ld_s % 4 != 0)
+        return VS_ERR_SHAPE;
+    if (nq == 0) return VS_OK;
+    if (!Q || !C || !idx_out || !S || !workspace) return VS_ERR_NULL;
+    if (!al4(Q) || !al4(C) || !al4(idx_out) || !al4(score_out) || !al256(workspace) ||
+        (reinterpret_cast<uintptr_t>(S) & 15) != 0)
+        return VS_ERR_ALIGN;
+    const bool q32 = vs::qreg_supports(d);
+    if (!q32 && !vs::q16_supports(d, C, Q)) return VS_ERR_UNSUPPORTED;
+    const Layout L = search_layout(nq, nc, metric);
+    if (workspace_bytes < L.total) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(ws + L.keys);
+    float *qn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.qn) : nullptr;
+    float *cn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.cn) : nullptr;
+    if (cn) VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, cn, st));
+    if (qn && score_out) VS_TRY_HIP(vs::launch_row_sqnorms(Q, nq, d, qn, st));
+
+    vs::DenseArgs a{};
+    a.Q = Q;
+    a.C = C;
+    a.nq = nq;
+    a.nc = nc;
+    a.d = d;
+    a.S = S;
+    a.ld_s = ld_s;
+    if (q32) VS_TRY_HIP(vs::launch_dense_qreg_store(a, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense_q16_store(a, st, n_cu));
+    VS_TRY_HIP(vs::launch_row_argbest(S, nq, nc, ld_s, cn, keys, metric, st));
+    VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
+    return VS_OK;
+}
+
 // ---- sparse-query search ---------------------------------------------------
 
 // Workspace of the CSR search: keys[nq] | qn[nq] | cn[nc] | partial keys

@@ -70,6 +70,10 @@ __device__ __forceinline__ f32x4 ld4(const float *p, int32_t k, int32_t d) {
 
 }  // namespace
 
+// M is a metric, or kStoreDots: write every dot product to a.S instead of
+// ranking (the score block of the unfused comparator).
+constexpr int kStoreDots = 4;
+
 template <int M, bool VEC, int NSLAB>
 __global__ __launch_bounds__(64 * kQW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_qreg(const DenseArgs a) {
@@ -178,6 +182,30 @@ void k_bmu_qreg(const DenseArgs a) {
     // visited in ascending order, so strict "<" keeps the lowest index.
     auto epilogue = [&](int64_t item, int par) {
         const int64_t base = (item % nct) * kBC;
+        if constexpr (M == kStoreDots) {
+            // S[q][c] for this lane's query column; register quad r4 holds
+            // rows 8 r4 + 4h .. + 3 of each 32-row block
+            const int64_t q = (item / nct) * kBQ + wave * 32 + l32;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int64_t c = base + cb * 32 + 8 * r4 + 4 * h;
+                    if (q < nq && c < nc) {
+                        float *dst = a.S + q * a.ld_s + c;
+                        const f32x4 v = {acc[cb][4 * r4], acc[cb][4 * r4 + 1],
+                                         acc[cb][4 * r4 + 2], acc[cb][4 * r4 + 3]};
+                        if (c + 4 <= nc) {
+                            *reinterpret_cast<f32x4 *>(dst) = v;
+                        } else {
+                            for (int e = 0; e < 4 && c + e < nc; ++e) dst[e] = v[e];
+                        }
+                    }
+                }
+                acc[cb] = f32x16{};
+            }
+            return;
+        }
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
@@ -200,6 +228,7 @@ void k_bmu_qreg(const DenseArgs a) {
         }
     };
     auto flush = [&](int64_t qt) {
+        if constexpr (M == kStoreDots) return;
         const float oe = __shfl_xor(best, 32);
         const int32_t oi = __shfl_xor(bidx, 32);
         if (oi >= 0 && (bidx < 0 || oe < best || (oe == best && oi < bidx))) {
@@ -321,6 +350,25 @@ hipError_t launch_dense_qreg(const DenseArgs &a0, int metric, hipStream_t st, in
     case COS_MAX: dispatch_slabs<COS_MAX>(a, vec, grid, st); break;
     default: dispatch_slabs<COS_MIN>(a, vec, grid, st); break;
     }
+    const hipError_t err = hipGetLastError();
+    timing_after(st);
+    return err;
+}
+
+// Every dot product Q[q] . C[c] (d <= 256) written to S[q * ld_s + c]
+// (ld_s % 4 == 0, S 16-byte aligned) by the arithmetic of the scan above, so
+// each value equals, bit for bit, the dot product that scan ranks.
+hipError_t launch_dense_qreg_store(const DenseArgs &a0, hipStream_t st, int n_cu) {
+    DenseArgs a = a0;
+    const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
+    a.n_ctiles = (a.nc + kBC - 1) / kBC;
+    a.n_items = nqt * a.n_ctiles;
+    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256);
+    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    const bool vec = (a.d % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a.Q) & 15) == 0);
+    timing_before(st, "k_bmu_qreg<store>");
+    dispatch_slabs<kStoreDots>(a, vec, dim3((unsigned)a.grid), st);
     const hipError_t err = hipGetLastError();
     timing_after(st);
     return err;

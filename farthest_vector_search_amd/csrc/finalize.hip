@@ -82,4 +82,57 @@ hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mas
     return hipGetLastError();
 }
 
+// Second pass of the unfused comparator: one wave per query reads its row
+// of the score block (16-byte loads, lane l: columns 256 i + 4 l .. + 3),
+// ranks each dot product with the metric's rule (the fused epilogue's own
+// rank_value), keeps the lowest value with the lowest index, and writes the
+// query's packed key; k_finalize then produces (index, score) as for the
+// fused scan.  The keys equal the fused scan's bit for bit.
+template <int M>
+__global__ __launch_bounds__(256) void k_row_argbest(const float *__restrict__ S, int64_t nq,
+                                                    int64_t nc, int64_t ld_s,
+                                                    const float *__restrict__ cn,
+                                                    uint64_t *__restrict__ keys) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
+    const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (q >= nq) return;
+    const float *row = S + q * ld_s;
+    float best = __builtin_inff();
+    int64_t bidx = -1;
+    for (int64_t j0 = 4 * (int64_t)lane; j0 < nc; j0 += 256) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);  // ld_s % 4 == 0
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (j0 + e < nc) {
+                const float r = rank_value<M>(v[e], metric_is_l2(M) ? cn[j0 + e] : 0.0f);
+                if (r < best) {
+                    best = r;
+                    bidx = j0 + e;
+                }
+            }
+        }
+    }
+    uint64_t k = bidx >= 0 ? pack_key(best, (uint32_t)bidx) : kNoKey;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(k, off);
+        k = o < k ? o : k;
+    }
+    if (lane == 0) keys[q] = k;
+}
+
+hipError_t launch_row_argbest(const float *S, int64_t nq, int64_t nc, int64_t ld_s,
+                              const float *cn, uint64_t *keys, int metric, hipStream_t st) {
+    if (nq <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((nq + 3) / 4)), block(256);
+    switch (metric) {
+    case L2SQ_MIN: hipLaunchKernelGGL(k_row_argbest<L2SQ_MIN>, grid, block, 0, st, S, nq, nc, ld_s, cn, keys); break;
+    case L2SQ_MAX: hipLaunchKernelGGL(k_row_argbest<L2SQ_MAX>, grid, block, 0, st, S, nq, nc, ld_s, cn, keys); break;
+    case COS_MAX: hipLaunchKernelGGL(k_row_argbest<COS_MAX>, grid, block, 0, st, S, nq, nc, ld_s, cn, keys); break;
+    default: hipLaunchKernelGGL(k_row_argbest<COS_MIN>, grid, block, 0, st, S, nq, nc, ld_s, cn, keys); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace vs

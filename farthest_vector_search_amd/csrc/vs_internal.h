@@ -150,6 +150,10 @@ hipError_t launch_dense_q16(const DenseArgs &a, int metric, bool gather, hipStre
                             int n_cu);
 // every dot product Q[q] . C[c] into a.S (same arithmetic as the scans)
 hipError_t launch_dense_q16_store(const DenseArgs &a, hipStream_t st, int n_cu);
+hipError_t launch_dense_qreg_store(const DenseArgs &a, hipStream_t st, int n_cu);
+// per-row best of a score block into packed keys (the unfused comparator)
+hipError_t launch_row_argbest(const float *S, int64_t nq, int64_t nc, int64_t ld_s,
+                              const float *cn, uint64_t *keys, int metric, hipStream_t st);
 // one diversity step from a cached score block G (G[r * ldg + j] = C[r] . C[j])
 hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
                                 uint32_t *mask, int64_t nseq, int32_t *idx_out,

@@ -92,6 +92,21 @@ int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_
                   size_t workspace_bytes, void *stream);
 
 /*
+ * Unfused comparator for the dense search [BMU, section 3 (the unfused
+ * GEMM-then-argmin path the fused search is measured against) and section 4]:
+ * the same MFMA arithmetic writes the whole score block S[q * ld_s + c] =
+ * Q[q] . C[c], then one pass per query ranks its row with the metric's rule.
+ * Results equal vs_bmu_search's bit for bit.  Exists to measure what fusion
+ * saves; S is caller-owned scratch of nq * ld_s floats (ld_s >= nc,
+ * ld_s % 4 == 0, 16-byte aligned), overwritten.  Other arguments and the
+ * workspace as for vs_bmu_search.  Needs d <= 256, or d <= 768 with d % 4 == 0
+ * and 16-byte aligned Q and C (else VS_ERR_UNSUPPORTED).
+ */
+int vs_bmu_search_unfused(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                          int32_t metric, int32_t *idx_out, float *score_out, float *S,
+                          int64_t ld_s, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Sparse-query search over a feature-major codebook [BMU, section 3 and
  * section 4 "The levers"].
  *   indptr     int32[nq+1], indices int32[nnz], values float32[nnz]: CSR

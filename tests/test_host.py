@@ -95,6 +95,21 @@ def test_dense_validation(L):
     assert dense_call(L, ws_bytes=need - 1) == 4
 
 
+def test_unfused_validation(L):
+    def call(Q=FAKE, C=FAKE, nq=4, nc=8, d=4, metric=0, idx=FAKE, score=FAKE, S=FAKE, ld=8,
+             ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_bmu_search_unfused(_P(Q), _P(C), nq, nc, d, metric, _P(idx), _P(score),
+                                       _P(S), ld, _P(ws), ws_bytes, None)
+    assert call(metric=4) == 3
+    assert call(ld=7) == 2
+    assert call(ld=10) == 2  # not a multiple of 4
+    assert call(nq=0, Q=0) == 0
+    assert call(S=0) == 1
+    assert call(S=FAKE + 4) == 5
+    assert call(d=1000) == 7
+    assert call(ws_bytes=8) == 4
+
+
 def test_workspace_sizes(L):
     # keys (8 B per query) always; squared L2 adds query and candidate norms
     assert L.vs_bmu_search_workspace(1000, 500, 64, 2) == 8192

@@ -148,6 +148,24 @@ def test_candidate_ranges_per_xcd(d, metric, monkeypatch):
     assert np.array_equal(full[1][:7].view(np.uint32), part[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("nq,nc,d", [(1, 1, 4), (65, 300, 64), (300, 1000, 200),
+                                     (129, 777, 256), (200, 500, 384), (70, 260, 768)])
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+def test_unfused_matches_fused(nq, nc, d, metric):
+    """The unfused comparator (score block, then a per-row pass) ranks the
+    same dot products with the same rule: bit-identical to the fused search,
+    which the oracle checks."""
+    dist = "unit" if metric in (2, 3) else "normal"
+    Q, C = synth.dense_case(nq, nc, d, dist, key=800 + d + metric)
+    Qd, Cd = to_dev(Q), to_dev(C)
+    a = vs.vs_bmu_search(Qd, Cd, metric)
+    b = vs.vs_bmu_search_unfused(Qd, Cd, metric)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0].cpu().numpy(), b[0].cpu().numpy())
+    assert np.array_equal(a[1].cpu().numpy().view(np.uint32), b[1].cpu().numpy().view(np.uint32))
+    assert_parity(Q, C, metric)
+
+
 def test_determinism(kernel):
     Q, C = synth.dense_case(1000, 3000, 96, "normal", key=8)
     outs = [run_dense(Q, C, 0) for _ in range(5)]
