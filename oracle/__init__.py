@@ -61,9 +61,13 @@ def _load(mutant: int = 0) -> ctypes.CDLL:
     lib.orc_div_run.argtypes = [P, I64, I64, I64, INT, P, P, P, P]
     lib.orc_gram_cos.argtypes = [P, I64, I64, I64, I64, P]
     lib.orc_div_replay.argtypes = [P, I64, I64, INT, P, P, P, P, P, P, P, P]
+    lib.orc_som_update.argtypes = [P, P, P, I64, INT, P, INT, INT, ctypes.c_double, INT, P,
+                                   I64, P, P, P, P]
+    lib.orc_mean_sqrt.argtypes = [P, I64]
+    lib.orc_mean_sqrt.restype = ctypes.c_double
     lib.orc_mutant.restype = INT
     for f in (lib.orc_dense, lib.orc_pair_values, lib.orc_sqnorms, lib.orc_csr,
-              lib.orc_div_run, lib.orc_gram_cos, lib.orc_div_replay):
+              lib.orc_div_run, lib.orc_gram_cos, lib.orc_div_replay, lib.orc_som_update):
         f.restype = None
     _libs[mutant] = lib
     return lib
@@ -275,6 +279,61 @@ def div_replay(G, seeds, picks, threads: int = 1, mutant: int = 0):
         with ThreadPoolExecutor(len(shards)) as ex:
             list(ex.map(run, shards))
     return out
+
+
+def dense_as_csr(X):
+    """A dense matrix as the CSR matrix holding every entry (row-major)."""
+    X = _c(X, np.float32)
+    n, d = X.shape
+    indptr = np.arange(n + 1, dtype=np.int64) * d
+    indices = np.tile(np.arange(d, dtype=np.int32), n)
+    return indptr, indices, X.reshape(-1)
+
+
+def som_update(indptr, indices, values, d: int, bmu, C_old, rows: int, cols: int,
+               sigma: float, radius: int, neurons=None, threads: int = 1, mutant: int = 0):
+    """Batch SOM update of the requested neurons (all by default).
+
+    Inputs are CSR rows (see :func:`dense_as_csr` for a dense matrix);
+    ``C_old`` is the neuron-major codebook (rows*cols x d) before the update.
+    Returns (w float64[m, d], mass float64[m, d], den float64[m]) for the
+    neurons in ``neurons`` order.
+    """
+    lib = _load(mutant)
+    indptr = _c(indptr, np.int64)
+    indices = _c(indices, np.int32)
+    values = _c(values, np.float32)
+    bmu = _c(bmu, np.int32)
+    C_old = np.asarray(C_old, np.float32)
+    nc = rows * cols
+    assert C_old.shape == (nc, d) and bmu.shape[0] == indptr.shape[0] - 1
+    neurons = np.arange(nc, dtype=np.int32) if neurons is None else _c(neurons, np.int32)
+    m = neurons.shape[0]
+    old = np.ascontiguousarray(C_old[neurons])
+    w = np.empty((m, d), np.float64)
+    mass = np.empty((m, d), np.float64)
+    den = np.empty(m, np.float64)
+
+    def run(lo_hi):
+        lo, hi = lo_hi
+        lib.orc_som_update(_p(indptr), _p(indices), _p(values), bmu.shape[0], d, _p(bmu),
+                           rows, cols, float(sigma), radius, _p(neurons[lo:hi]), hi - lo,
+                           _p(old[lo:hi]), _p(w[lo:hi]), _p(mass[lo:hi]), _p(den[lo:hi]))
+
+    shards = _shards(m, threads)
+    if len(shards) <= 1:
+        for s in shards:
+            run(s)
+    else:
+        with ThreadPoolExecutor(len(shards)) as ex:
+            list(ex.map(run, shards))
+    return w, mass, den
+
+
+def mean_sqrt(d2, mutant: int = 0) -> float:
+    """Quantisation error from each input's exact squared distance to its BMU."""
+    d2 = _c(d2, np.float64)
+    return float(_load(mutant).orc_mean_sqrt(_p(d2), d2.shape[0]))
 
 
 def mutant_id(mutant: int = 0) -> int:

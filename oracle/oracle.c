@@ -21,6 +21,8 @@
  *    Shader Inner Loop For L2 Cache Locality", sections "Current Behavior" and
  *    "Intended Behavior".  Largest cosine distance == smallest cosine, so the
  *    same scan with the order reversed covers it (metric COS_MIN).
+ *  - SOM batch update and quantisation error around the BMU search (the
+ *    same paper, section 3); see the notes at orc_som_update below.
  *  - The running best across the whole candidate range is a plain max/min:
  *    the same issue, "Intended Behavior" (associativity of max) and
  *    "Suggested Implementation Steps" (per-thread running best that is never
@@ -367,4 +369,118 @@ void orc_div_replay(const double *G, int64_t n, int64_t nseq, int T,
             last = p;
         }
     }
+}
+
+/* ------------------------------------------------------ SOM batch update -- */
+/*
+ * One batch update of a self-organizing map around the BMU search.  "From
+ * 80x to 385x ...", section 3 (workload): each article's closest neuron is
+ * found first, then that neuron and its neighbours on the map are updated.
+ * The pages name no update rule; the readings taken here (all listed in the
+ * design notes) are the batch map of the SOM literature:
+ *  - the map is rows x cols, planar (no wrap-around); neuron m sits at grid
+ *    row m / cols, column m % cols;
+ *  - the neighbourhood weight of a BMU b on a neuron m is the Gaussian
+ *    h(b, m) = exp(-(dy^2 + dx^2) / (2 sigma^2)) of their grid offset
+ *    (dy, dx), taken as 0 outside the square window max(|dy|, |dx|) <= R;
+ *  - every input pulls with weight h(bmu_i, m) at once:
+ *        w_m <- sum_i h(bmu_i, m) x_i / sum_i h(bmu_i, m),
+ *    and a neuron whose denominator is 0 keeps its weights;
+ *  - an input whose BMU index lies outside [0, rows*cols) pulls nothing.
+ * Inputs are CSR rows (a dense matrix is the CSR matrix holding every
+ * entry); a column repeated within a row adds its values.  The definition is
+ * evaluated directly, one requested neuron at a time, inputs in ascending
+ * order, in double.  For each neuron the function also returns its
+ * denominator and, per feature, sum_i h |x_ik| / den (the magnitude the
+ * floating-point error of any summation order scales with; 0 when den = 0).
+ *
+ * MUTANT 10: window one step too narrow;  MUTANT 11: exp(-r^2 / sigma^2);
+ * MUTANT 12: grid row taken as m / rows;   MUTANT 13: weights not normalised
+ * by the Gaussian (den counts inputs).
+ */
+void orc_som_update(const int64_t *indptr, const int32_t *indices, const float *values,
+                    int64_t n_in, int32_t d, const int32_t *bmu, int32_t rows, int32_t cols,
+                    double sigma, int32_t radius, const int32_t *neurons, int64_t m,
+                    const float *old_rows, double *w_out, double *mass_out, double *den_out)
+{
+    const int64_t nc = (int64_t)rows * cols;
+#if ORC_MUTANT == 10
+    const int64_t R = (int64_t)radius - 1;
+#else
+    const int64_t R = radius;
+#endif
+    for (int64_t t = 0; t < m; ++t) {
+        const int64_t nm = neurons[t];
+#if ORC_MUTANT == 12
+        const int64_t ym = nm / rows, xm = nm % cols;
+#else
+        const int64_t ym = nm / cols, xm = nm % cols;
+#endif
+        double *num = w_out + t * d;
+        double *mass = mass_out + t * d;
+        for (int32_t k = 0; k < d; ++k)
+            num[k] = mass[k] = 0.0;
+        double den = 0.0;
+        for (int64_t i = 0; i < n_in; ++i) {
+            const int64_t b = bmu[i];
+            if (b < 0 || b >= nc)
+                continue;
+#if ORC_MUTANT == 12
+            const int64_t dy = b / rows - ym, dx = b % cols - xm;
+#else
+            const int64_t dy = b / cols - ym, dx = b % cols - xm;
+#endif
+            if (llabs(dy) > R || llabs(dx) > R)
+                continue;
+            const double r2 = (double)(dy * dy + dx * dx);
+#if ORC_MUTANT == 11
+            const double h = exp(-r2 / (sigma * sigma));
+#else
+            const double h = exp(-r2 / (2.0 * sigma * sigma));
+#endif
+#if ORC_MUTANT == 13
+            den += 1.0;
+#else
+            den += h;
+#endif
+            for (int64_t p = indptr[i]; p < indptr[i + 1]; ++p) {
+                const double v = (double)values[p];
+                num[indices[p]] += h * v;
+                mass[indices[p]] += h * fabs(v);
+            }
+        }
+        den_out[t] = den;
+        for (int32_t k = 0; k < d; ++k) {
+            if (den > 0.0) {
+                num[k] /= den;
+                mass[k] /= den;
+            } else {
+                num[k] = (double)old_rows[t * d + k];
+                mass[k] = 0.0;
+            }
+        }
+    }
+}
+
+/*
+ * Quantisation error of a map: the mean, over the inputs, of the Euclidean
+ * distance from each input to its BMU's weight vector, measured before the
+ * update ("From 80x to 385x ...", section 3 records it as the map's quality
+ * figure; the mean Euclidean distance is the usual SOM definition, a
+ * reading).  d2 holds each input's exact squared distance to its BMU (the
+ * value the scans above return for squared L2); n = 0 gives NaN.
+ * MUTANT 14: averages the squared distances.
+ */
+double orc_mean_sqrt(const double *d2, int64_t n)
+{
+    if (n <= 0)
+        return NAN;
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+#if ORC_MUTANT == 14
+        s += d2[i];
+#else
+        s += sqrt(d2[i] > 0.0 ? d2[i] : 0.0);
+#endif
+    return s / (double)n;
 }

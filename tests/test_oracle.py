@@ -26,7 +26,7 @@ import oracle
 import synth
 from goldens import csr_cases, diversity_walk, hand_cases
 
-MUTANTS = list(range(1, 10))
+MUTANTS = list(range(1, 15))
 
 
 def _close(a, b, rel=1e-12, abs_=1e-12):
@@ -256,9 +256,153 @@ def pin_sqnorms(m=0):
     return [] if np.allclose(a, ref, rtol=1e-13) and np.allclose(b, ref, rtol=1e-13) else ["sqnorms"]
 
 
+# ---- SOM batch update and quantisation error --------------------------------
+# Pinned against: group means (np.add.at), a single input (closed form), a
+# separable Gaussian window from scipy.signal.windows.gaussian correlated over
+# the map by scipy.ndimage.correlate (zero outside the map), the global mean
+# when the window is the whole map and sigma is huge, mirror/transpose
+# symmetry of the map, a hand-worked 1x3 map, and distances with known roots.
+
+def _som_inputs(n, d, nc, key, dense=True):
+    rng = np.random.default_rng(key)
+    X = rng.normal(size=(n, d)).astype(np.float32)
+    if not dense:
+        X[rng.random(X.shape) < 0.7] = 0.0
+    bmu = rng.integers(0, nc, n).astype(np.int32)
+    C = rng.normal(size=(nc, d)).astype(np.float32)
+    return X, bmu, C
+
+
+def _som(X, bmu, C, rows, cols, sigma, R, m=0, **kw):
+    ip, ix, v = oracle.dense_as_csr(X)
+    return oracle.som_update(ip, ix, v, X.shape[1], bmu, C, rows, cols, sigma, R, mutant=m, **kw)
+
+
+def _group_sums(X, bmu, nc):
+    S = np.zeros((nc, X.shape[1]))
+    np.add.at(S, bmu, X.astype(np.float64))
+    return S, np.bincount(bmu, minlength=nc).astype(np.float64)
+
+
+def pin_som_group_mean(m=0):
+    bad = []
+    rows, cols = 3, 5
+    X, bmu, C = _som_inputs(40, 6, rows * cols, key=70)
+    bmu[bmu == 7] = 8  # leave neuron 7 without inputs
+    S, N = _group_sums(X, bmu, rows * cols)
+    ref = np.where(N[:, None] > 0, S / np.maximum(N, 1)[:, None], C)
+    for sigma, R in ((1.0, 0), (1e-3, 2)):
+        w, _, _ = _som(X, bmu, C, rows, cols, sigma, R, m)
+        if not np.allclose(w, ref, rtol=1e-12, atol=1e-12):
+            bad.append(f"som: sigma {sigma} R {R} is not the per-neuron mean")
+    return bad
+
+
+def pin_som_single_input(m=0):
+    rows, cols, R = 6, 9, 2
+    X, _, C = _som_inputs(1, 5, rows * cols, key=71)
+    b = 3 * cols + 7  # (3, 7): the window is clipped by the right edge
+    w, _, den = _som(X, np.array([b], np.int32), C, rows, cols, 1.3, R, m)
+    y, x = np.divmod(np.arange(rows * cols), cols)
+    inside = (np.abs(y - 3) <= R) & (np.abs(x - 7) <= R)
+    ref = np.where(inside[:, None], X[0].astype(np.float64), C)
+    ok = np.allclose(w, ref, rtol=1e-12, atol=1e-12) and np.array_equal(den > 0, inside)
+    return [] if ok else ["som: one input must move exactly its window onto itself"]
+
+
+def pin_som_scipy(m=0):
+    from scipy.ndimage import correlate
+    from scipy.signal.windows import gaussian
+    bad = []
+    for rows, cols, sigma, R, key in ((7, 11, 1.5, 3, 72), (10, 4, 0.8, 2, 73), (5, 5, 2.5, 6, 74)):
+        nc = rows * cols
+        X, bmu, C = _som_inputs(60, 4, nc, key)
+        bmu[::7] = 0  # a crowded corner neuron
+        S, N = _group_sums(X, bmu, nc)
+        g = gaussian(2 * R + 1, std=sigma)
+        K = np.outer(g, g)
+        den = correlate(N.reshape(rows, cols), K, mode="constant", cval=0.0).reshape(-1)
+        num = np.stack([correlate(S[:, k].reshape(rows, cols), K, mode="constant", cval=0.0)
+                        .reshape(-1) for k in range(S.shape[1])], axis=1)
+        ref = np.where(den[:, None] > 0, num / np.where(den > 0, den, 1)[:, None], C)
+        w, mass, d = _som(X, bmu, C, rows, cols, sigma, R, m)
+        if not (np.allclose(w, ref, rtol=1e-10, atol=1e-10) and np.allclose(d, den, rtol=1e-12)):
+            bad.append(f"som differs from the scipy window on {rows}x{cols} R {R}")
+        A, _ = _group_sums(np.abs(X), bmu, nc)
+        lin = np.stack([correlate(A[:, k].reshape(rows, cols), K, mode="constant")
+                        .reshape(-1) for k in range(A.shape[1])], axis=1)
+        ref_mass = np.where(den[:, None] > 0, lin / np.where(den > 0, den, 1)[:, None], 0.0)
+        if not np.allclose(mass, ref_mass, rtol=1e-10, atol=1e-12):
+            bad.append("som mass is not the smoothed |x|")
+    return bad
+
+
+def pin_som_global_mean(m=0):
+    rows, cols = 4, 6
+    X, bmu, C = _som_inputs(30, 5, rows * cols, key=75)
+    w, _, _ = _som(X, bmu, C, rows, cols, 1e6, max(rows, cols), m)
+    ref = X.astype(np.float64).mean(axis=0)
+    return [] if np.allclose(w, ref[None, :], rtol=1e-9, atol=1e-9) else ["som: huge window is not the mean"]
+
+
+def pin_som_symmetry(m=0):
+    rows, cols = 4, 7
+    X, bmu, C = _som_inputs(50, 3, rows * cols, key=76)
+    y, x = np.divmod(np.arange(rows * cols), cols)
+    w0, _, _ = _som(X, bmu, C, rows, cols, 1.1, 2, m)
+    mir = y * cols + (cols - 1 - x)          # mirror left-right
+    w1, _, _ = _som(X, mir[bmu].astype(np.int32), C[np.argsort(mir)], rows, cols, 1.1, 2, m)
+    tr = x * rows + y                         # transpose: the map becomes cols x rows
+    w2, _, _ = _som(X, tr[bmu].astype(np.int32), C[np.argsort(tr)], cols, rows, 1.1, 2, m)
+    bad = []
+    if not np.allclose(w1[mir], w0, rtol=1e-12, atol=1e-12):
+        bad.append("som not mirror-symmetric")
+    if not np.allclose(w2[tr], w0, rtol=1e-12, atol=1e-12):
+        bad.append("som not transpose-symmetric")
+    return bad
+
+
+def pin_som_hand(m=0):
+    # 1 x 3 map, sigma 1, R 1; x = 1 at neuron 0 and x = 4 at neuron 2.  Neuron 0
+    # sees only its own input (neuron 2 is two steps away), neuron 1 sees both
+    # with the same weight (midpoint 2.5), neuron 2 only its own.
+    X = np.array([[1.0], [4.0]], np.float32)
+    w, _, _ = _som(X, np.array([0, 2], np.int32), np.zeros((3, 1), np.float32), 1, 3, 1.0, 1, m)
+    return [] if np.allclose(w[:, 0], [1.0, 2.5, 4.0], rtol=0, atol=1e-15) else [f"som hand {w[:, 0]}"]
+
+
+def pin_som_csr_duplicates(m=0):
+    # a column repeated within a row adds its values: [2 + 3] at column 1
+    ip = np.array([0, 2, 3], np.int64)
+    a = oracle.som_update(ip, np.array([1, 1, 0], np.int32), np.array([2, 3, 7], np.float32), 2,
+                          np.array([0, 0], np.int32), np.zeros((1, 2), np.float32), 1, 1, 1.0, 0,
+                          mutant=m)[0]
+    return [] if np.allclose(a, [[3.5, 2.5]], atol=1e-15) else ["som csr duplicates"]
+
+
+def pin_qe(m=0):
+    bad = []
+    # distances 5, 1, 10 from the origin neuron (3-4-5 and 6-8-10 triangles)
+    X = np.array([[3, 4], [0, 1], [6, 8]], np.float32)
+    C = np.array([[0, 0], [100, 100]], np.float32)
+    _, v, _ = oracle.dense(X, C, 0, mutant=m)
+    if not _close(oracle.mean_sqrt(v, mutant=m), 16.0 / 3.0, 1e-14, 1e-14):
+        bad.append("qe of 5, 1, 10")
+    # inputs sitting on neurons have zero error
+    _, C2 = synth.dense_case(1, 9, 4, "normal", key=77)
+    _, v2, _ = oracle.dense(C2[[3, 5, 3]], C2, 0, mutant=m)
+    if oracle.mean_sqrt(v2, mutant=m) != 0.0:
+        bad.append("qe of inputs equal to neurons")
+    if not math.isnan(oracle.mean_sqrt(np.zeros(0), mutant=m)):
+        bad.append("qe of no inputs must be NaN")
+    return bad
+
+
 PINS = [pin_hand_cases, pin_csr_cases, pin_walk, pin_library, pin_sklearn, pin_closed_forms,
         pin_split_invariance, pin_permutation, pin_translation, pin_duplicates,
-        pin_csr_vs_dense, pin_replay, pin_gram, pin_sqnorms]
+        pin_csr_vs_dense, pin_replay, pin_gram, pin_sqnorms, pin_som_group_mean,
+        pin_som_single_input, pin_som_scipy, pin_som_global_mean, pin_som_symmetry,
+        pin_som_hand, pin_som_csr_duplicates, pin_qe]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
