@@ -42,6 +42,9 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
            "vs_diversity_gram", "vs_diversity_step_gram",
+           "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
+           "vs_som_epoch_workspace", "vs_som_epoch", "vs_som_epoch_csr_workspace",
+           "vs_som_epoch_csr",
            "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
            "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
 
@@ -89,6 +92,19 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
     L.vs_diversity_gram.argtypes = [P, I64, I32, P, I64, P]
     L.vs_diversity_step_gram.argtypes = [P, I64, I64, P, P, I64, P, P, P]
+    F = ctypes.c_float
+    L.vs_som_update_workspace.argtypes = [I32, I32, I32]
+    L.vs_som_update_workspace.restype = SZ
+    L.vs_som_update.argtypes = [P, I64, I32, P, P, I32, I32, F, I32, P, SZ, P]
+    L.vs_som_update_csr.argtypes = [P, P, P, I64, I64, P, P, I32, I32, I32, F, I32, P, SZ, P]
+    L.vs_som_qe.argtypes = [P, I64, P, P]
+    L.vs_som_epoch_workspace.argtypes = [I64, I32, I32, I32]
+    L.vs_som_epoch_workspace.restype = SZ
+    L.vs_som_epoch.argtypes = [P, I64, I32, P, I32, I32, F, I32, P, P, P, P, SZ, P]
+    L.vs_som_epoch_csr_workspace.argtypes = [I64, I32, I32, I32]
+    L.vs_som_epoch_csr_workspace.restype = SZ
+    L.vs_som_epoch_csr.argtypes = [P, P, P, I64, I64, P, I32, I32, I32, F, I32, P, P, P, P, SZ,
+                                   P]
     L.vs_candidate_norms.argtypes = [P, I64, I32, I32, P, P]
     L.vs_tile_rows.argtypes = [I64, I32, I32]
     L.vs_tile_rows.restype = I64
@@ -102,7 +118,8 @@ def lib() -> ctypes.CDLL:
                  "vs_csr_block_codebook",
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
-                 "vs_diversity_step_gram",
+                 "vs_diversity_step_gram", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
+                 "vs_som_epoch", "vs_som_epoch_csr",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
         getattr(L, name).restype = ctypes.c_int
@@ -451,6 +468,141 @@ def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None
                                       nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
     _check(rc, "vs_diversity_step_gram")
     return idx_out, score_out
+
+
+def _map_shape(nc, map_shape):
+    rows, cols = (int(v) for v in map_shape)
+    if rows * cols != nc:
+        raise ValueError(f"map {rows}x{cols} does not hold {nc} neurons")
+    return rows, cols
+
+
+def _csr_args(indptr, indices, values):
+    torch = _torch()
+    _dev(indptr, "indptr", torch.int32, 1)
+    _dev(indices, "indices", torch.int32, 1)
+    _dev(values, "values", torch.float32, 1)
+    n = indptr.numel() - 1
+    nnz = indices.numel()
+    if values.numel() != nnz:
+        raise ValueError("indices and values differ in length")
+    return n, nnz
+
+
+def vs_som_update(X, bmu, C, map_shape, sigma: float, radius: int, workspace=None):
+    """Batch SOM update of the neuron-major codebook C (rows*cols x d) in
+    place from the dense rows X and their BMU indices (see include/vs.h)."""
+    torch = _torch()
+    L = lib()
+    _dev(X, "X", torch.float32, 2)
+    _dev(bmu, "bmu", torch.int32, 1)
+    _dev(C, "C", torch.float32, 2)
+    n, d = X.shape
+    nc = C.shape[0]
+    if C.shape[1] != d or bmu.numel() != n:
+        raise ValueError("X, bmu and C disagree in shape")
+    rows, cols = _map_shape(nc, map_shape)
+    dev = C.device
+    ws = _workspace(L.vs_som_update_workspace(rows, cols, d), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_update(_ptr(X), n, d, _ptr(bmu), _ptr(C), rows, cols, float(sigma),
+                             int(radius), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_som_update")
+    return C
+
+
+def vs_som_update_csr(indptr, indices, values, bmu, CB, map_shape, d: int, sigma: float,
+                      radius: int, workspace=None):
+    """Batch SOM update, CSR rows, of the 64-neuron blocked codebook CB (the
+    layout vs_csr_block_codebook writes) in place."""
+    torch = _torch()
+    L = lib()
+    n, nnz = _csr_args(indptr, indices, values)
+    _dev(bmu, "bmu", torch.int32, 1)
+    _dev(CB, "CB", torch.float32, 1)
+    rows, cols = (int(v) for v in map_shape)
+    nc = rows * cols
+    if bmu.numel() != n:
+        raise ValueError("bmu must hold one index per row")
+    if CB.numel() < ((nc + 63) // 64) * 64 * d:
+        raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
+    dev = CB.device
+    ws = _workspace(L.vs_som_update_workspace(rows, cols, d), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_update_csr(_ptr(indptr), _ptr(indices) if nnz else None,
+                                 _ptr(values) if nnz else None, n, nnz, _ptr(bmu), _ptr(CB),
+                                 rows, cols, d, float(sigma), int(radius), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_som_update_csr")
+    return CB
+
+
+def vs_som_qe(score, qe_out=None):
+    """Quantisation error (float64 tensor of one element) from BMU scores."""
+    torch = _torch()
+    L = lib()
+    _dev(score, "score", torch.float32, 1)
+    dev = score.device
+    if qe_out is None:
+        qe_out = torch.empty(1, dtype=torch.float64, device=dev)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_qe(_ptr(score), score.numel(), _ptr(qe_out), _stream(dev))
+    _check(rc, "vs_som_qe")
+    return qe_out
+
+
+def vs_som_epoch(X, C, map_shape, sigma: float, radius: int, bmu_out=None, score_out=None,
+                 qe_out=None, workspace=None):
+    """One SOM epoch on dense rows: BMU search, quantisation error, batch
+    update of C in place.  Returns (bmu, score, qe)."""
+    torch = _torch()
+    L = lib()
+    _dev(X, "X", torch.float32, 2)
+    _dev(C, "C", torch.float32, 2)
+    n, d = X.shape
+    nc = C.shape[0]
+    if C.shape[1] != d:
+        raise ValueError("X and C must have the same number of columns")
+    rows, cols = _map_shape(nc, map_shape)
+    dev = C.device
+    bmu_out = torch.empty(n, dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
+    score_out = torch.empty(n, dtype=torch.float32, device=dev) if score_out is None else score_out
+    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    ws = _workspace(L.vs_som_epoch_workspace(n, rows, cols, d), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_epoch(_ptr(X), n, d, _ptr(C), rows, cols, float(sigma), int(radius),
+                            _ptr(bmu_out), _ptr(score_out), _ptr(qe_out), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_som_epoch")
+    return bmu_out, score_out, qe_out
+
+
+def vs_som_epoch_csr(indptr, indices, values, CB, map_shape, d: int, sigma: float, radius: int,
+                     bmu_out=None, score_out=None, qe_out=None, workspace=None):
+    """One SOM epoch on CSR rows over the blocked codebook CB: BMU search,
+    quantisation error, batch update of CB in place.  Returns (bmu, score, qe)."""
+    torch = _torch()
+    L = lib()
+    n, nnz = _csr_args(indptr, indices, values)
+    _dev(CB, "CB", torch.float32, 1)
+    rows, cols = (int(v) for v in map_shape)
+    nc = rows * cols
+    if CB.numel() < ((nc + 63) // 64) * 64 * d:
+        raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
+    dev = CB.device
+    bmu_out = torch.empty(max(n, 0), dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
+    score_out = (torch.empty(max(n, 0), dtype=torch.float32, device=dev) if score_out is None
+                 else score_out)
+    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_epoch_csr(_ptr(indptr), _ptr(indices) if nnz else None,
+                                _ptr(values) if nnz else None, n, nnz, _ptr(CB), rows, cols, d,
+                                float(sigma), int(radius), _ptr(bmu_out), _ptr(score_out),
+                                _ptr(qe_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(dev))
+    _check(rc, "vs_som_epoch_csr")
+    return bmu_out, score_out, qe_out
 
 
 def vs_candidate_norms(C, feature_major: bool = False, out=None):

@@ -515,6 +515,185 @@ VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t fea
     return VS_OK;
 }
 
+// ---- SOM batch update, quantisation error, epoch ----------------------------
+
+struct SomLayout {
+    size_t S = 0, T = 0, cnt = 0, den_t = 0, den = 0, g = 0, total = 0;
+};
+
+SomLayout som_layout(int64_t nc, int32_t d, int32_t gmax) {
+    SomLayout L;
+    const size_t elems = (size_t)((nc + 63) / 64) * 64u * (size_t)d;
+    L.T = up256(elems * 4);
+    L.cnt = L.T + up256(elems * 4);
+    L.den_t = L.cnt + up256((size_t)nc * 4);
+    L.den = L.den_t + up256((size_t)nc * 4);
+    L.g = L.den + up256((size_t)nc * 4);
+    L.total = L.g + up256((size_t)gmax * 4);
+    return L;
+}
+
+// map, sigma and radius checks; *R_eff = radius clipped to the map
+static int som_params(int32_t rows, int32_t cols, int32_t d, float sigma, int32_t radius,
+                      int32_t *R_eff) {
+    if (rows < 1 || cols < 1 || (int64_t)rows * cols > kMaxIndex || d < 1 || d > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (!(sigma > 0.0f) || !(sigma < 3.0e38f) || radius < 0) return VS_ERR_SHAPE;
+    // every weight inside the window stays a normal fp32 number (>= e^-64)
+    if (radius > 0 && (double)radius > 8.0 * (double)sigma) return VS_ERR_SHAPE;
+    const int32_t ext = rows > cols ? rows : cols;
+    *R_eff = radius < ext - 1 ? radius : ext - 1;
+    return VS_OK;
+}
+
+static int som_update(vs::SomArgs &a, void *workspace, size_t workspace_bytes, void *stream) {
+    const int64_t nc = (int64_t)a.rows * a.cols;
+    const SomLayout L = som_layout(nc, a.d, a.rows > a.cols ? a.rows : a.cols);
+    if (workspace_bytes < L.total) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    char *ws = static_cast<char *>(workspace);
+    a.S = reinterpret_cast<float *>(ws + L.S);
+    a.T = reinterpret_cast<float *>(ws + L.T);
+    a.cnt = reinterpret_cast<int32_t *>(ws + L.cnt);
+    a.den_t = reinterpret_cast<float *>(ws + L.den_t);
+    a.den = reinterpret_cast<float *>(ws + L.den);
+    a.g = reinterpret_cast<float *>(ws + L.g);
+    VS_TRY_HIP(vs::launch_som_update(a, reinterpret_cast<hipStream_t>(stream), n_cu));
+    return VS_OK;
+}
+
+VS_API size_t vs_som_update_workspace(int32_t map_rows, int32_t map_cols, int32_t d) {
+    int32_t R = 0;
+    if (som_params(map_rows, map_cols, d, 1.0f, 0, &R)) return 0;
+    return som_layout((int64_t)map_rows * map_cols, d, map_rows > map_cols ? map_rows : map_cols)
+        .total;
+}
+
+VS_API int vs_som_update(const float *X, int64_t n, int32_t d, const int32_t *bmu, float *C,
+                         int32_t map_rows, int32_t map_cols, float sigma, int32_t radius,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    int32_t R = 0;
+    if (const int s = som_params(map_rows, map_cols, d, sigma, radius, &R)) return s;
+    if (n < 0 || n > kMaxIndex) return VS_ERR_SHAPE;
+    if (n == 0) return VS_OK;
+    if (!X || !bmu || !C || !workspace) return VS_ERR_NULL;
+    if (!al4(X) || !al4(bmu) || !al4(C) || !al256(workspace)) return VS_ERR_ALIGN;
+    vs::SomArgs a{};
+    a.csr = false;
+    a.X = X;
+    a.n = n;
+    a.d = d;
+    a.bmu = bmu;
+    a.C = C;
+    a.rows = map_rows;
+    a.cols = map_cols;
+    a.R = R;
+    a.sigma = sigma;
+    return som_update(a, workspace, workspace_bytes, stream);
+}
+
+VS_API int vs_som_update_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                             int64_t n, int64_t nnz, const int32_t *bmu, float *CB,
+                             int32_t map_rows, int32_t map_cols, int32_t d, float sigma,
+                             int32_t radius, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    int32_t R = 0;
+    if (const int s = som_params(map_rows, map_cols, d, sigma, radius, &R)) return s;
+    if (n < 0 || n > kMaxIndex || nnz < 0 || nnz > kMaxIndex) return VS_ERR_SHAPE;
+    if (n == 0) return VS_OK;
+    if (!indptr || !bmu || !CB || !workspace || (nnz > 0 && (!indices || !values)))
+        return VS_ERR_NULL;
+    if (!al4(indptr) || !al4(indices) || !al4(values) || !al4(bmu) || !al4(CB) ||
+        !al256(workspace))
+        return VS_ERR_ALIGN;
+    vs::SomArgs a{};
+    a.csr = true;
+    a.indptr = indptr;
+    a.indices = indices;
+    a.values = values;
+    a.n = n;
+    a.d = d;
+    a.bmu = bmu;
+    a.C = CB;
+    a.rows = map_rows;
+    a.cols = map_cols;
+    a.R = R;
+    a.sigma = sigma;
+    return som_update(a, workspace, workspace_bytes, stream);
+}
+
+VS_API int vs_som_qe(const float *score, int64_t n, double *qe_out, void *stream) {
+    if (n < 0 || n > kMaxIndex) return VS_ERR_SHAPE;
+    if (!qe_out || (n > 0 && !score)) return VS_ERR_NULL;
+    if (!al4(score) || (reinterpret_cast<uintptr_t>(qe_out) & 7) != 0) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_som_qe(score, n, qe_out, reinterpret_cast<hipStream_t>(stream)));
+    return VS_OK;
+}
+
+VS_API size_t vs_som_epoch_workspace(int64_t n, int32_t map_rows, int32_t map_cols, int32_t d) {
+    const size_t u = vs_som_update_workspace(map_rows, map_cols, d);
+    if (!u || n < 0) return 0;
+    return up256(search_layout(n, (int64_t)map_rows * map_cols, vs::L2SQ_MIN).total) + u;
+}
+
+VS_API int vs_som_epoch(const float *X, int64_t n, int32_t d, float *C, int32_t map_rows,
+                        int32_t map_cols, float sigma, int32_t radius, int32_t *bmu_out,
+                        float *score_out, double *qe_out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    int32_t R = 0;
+    if (const int s = som_params(map_rows, map_cols, d, sigma, radius, &R)) return s;
+    if (n < 0 || n > kMaxIndex || d > kMaxDim) return VS_ERR_SHAPE;
+    if (!C || !workspace || (n > 0 && (!X || !bmu_out || !score_out))) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(qe_out) & 7) != 0) return VS_ERR_ALIGN;
+    const size_t need = vs_som_epoch_workspace(n, map_rows, map_cols, d);
+    if (workspace_bytes < need) return VS_ERR_WORKSPACE;
+    const int64_t nc = (int64_t)map_rows * map_cols;
+    const size_t ws1 = up256(search_layout(n, nc, vs::L2SQ_MIN).total);
+    char *ws = static_cast<char *>(workspace);
+    if (const int s = vs_bmu_search(X, C, n, nc, d, vs::L2SQ_MIN, bmu_out, score_out, ws, ws1,
+                                    stream))
+        return s;
+    if (qe_out)
+        if (const int s = vs_som_qe(score_out, n, qe_out, stream)) return s;
+    return vs_som_update(X, n, d, bmu_out, C, map_rows, map_cols, sigma, radius, ws + ws1,
+                         workspace_bytes - ws1, stream);
+}
+
+VS_API size_t vs_som_epoch_csr_workspace(int64_t n, int32_t map_rows, int32_t map_cols,
+                                         int32_t d) {
+    const size_t u = vs_som_update_workspace(map_rows, map_cols, d);
+    if (!u || n < 0) return 0;
+    return up256(csr_layout(n, (int64_t)map_rows * map_cols).total) + u;
+}
+
+VS_API int vs_som_epoch_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                            int64_t n, int64_t nnz, float *CB, int32_t map_rows,
+                            int32_t map_cols, int32_t d, float sigma, int32_t radius,
+                            int32_t *bmu_out, float *score_out, double *qe_out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    int32_t R = 0;
+    if (const int s = som_params(map_rows, map_cols, d, sigma, radius, &R)) return s;
+    if (n < 0 || n > kMaxIndex || nnz < 0 || nnz > kMaxIndex) return VS_ERR_SHAPE;
+    if (!CB || !workspace || (n > 0 && (!bmu_out || !score_out))) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(qe_out) & 7) != 0) return VS_ERR_ALIGN;
+    const size_t need = vs_som_epoch_csr_workspace(n, map_rows, map_cols, d);
+    if (workspace_bytes < need) return VS_ERR_WORKSPACE;
+    const int64_t nc = (int64_t)map_rows * map_cols;
+    const size_t ws1 = up256(csr_layout(n, nc).total);
+    char *ws = static_cast<char *>(workspace);
+    if (const int s = vs_bmu_search_csr_blocked(indptr, indices, values, n, nnz, CB, nc, d,
+                                                vs::L2SQ_MIN, bmu_out, score_out, ws, ws1,
+                                                stream))
+        return s;
+    if (qe_out)
+        if (const int s = vs_som_qe(score_out, n, qe_out, stream)) return s;
+    return vs_som_update_csr(indptr, indices, values, n, nnz, bmu_out, CB, map_rows, map_cols, d,
+                             sigma, radius, ws + ws1, workspace_bytes - ws1, stream);
+}
+
 VS_API int64_t vs_tile_rows(int64_t cache_bytes, int32_t d, int32_t bytes_per_value) {
     if (cache_bytes <= 0 || d < 1 || bytes_per_value < 1) return 0;
     // floor(cache * 0.85 / (d * b)) in exact integer arithmetic: 0.85 = 17/20

@@ -1,0 +1,247 @@
+// som.hip -- batch SOM update and quantisation error around the BMU search.
+//
+// "From 80x to 385x: A Best-Matching-Unit Search at the L2 Roof", section 3
+// (workload): each input's closest neuron is found first, then that neuron
+// and its neighbours on the map are updated.  The update here is the batch
+// map: neuron m at grid (m / cols, m % cols) of a planar rows x cols map
+// becomes sum_i h(bmu_i, m) x_i / sum_i h(bmu_i, m) with the Gaussian
+// h = exp(-(dy^2 + dx^2) / (2 sigma^2)) of the grid offset inside the square
+// window max(|dy|, |dx|) <= R (0 outside); a neuron with zero denominator
+// keeps its weights.
+//
+// The Gaussian of a square window factorises, h = g(dy) g(dx) with
+// g(t) = exp(-t^2 / (2 sigma^2)), so the update runs as
+//   1. S[b] = sum of the inputs whose BMU is b, N[b] = their count
+//      (fp32 / int32 atomics; the float sums' last bits depend on the order
+//      in which the atomics land);
+//   2. a pass along the map's columns:  T(m) = sum_t g(t) S(m + t)
+//      and the same over N;
+//   3. a pass along the map's rows:     num(m) = sum_t g(t) T(m + t cols),
+//      fused with the division num / den into the codebook.
+// Both passes only sum over offsets that stay on the map (the planar edge).
+//
+// Element (neuron m, feature k) of the codebook and of the S / T buffers:
+//   neuron-major (dense rows):  m * d + k
+//   blocked feature-major (the sparse search's layout, 64-neuron blocks):
+//                               (m / 64) * 64 d + k * 64 + m % 64
+// Threads run along the contiguous axis (k, resp. m within a block), so every
+// load and store of a pass is coalesced; the window's other taps are re-reads
+// of lines the neighbouring waves just fetched (L1 / L2 hits).
+#include "vs_internal.h"
+
+namespace vs {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BLOCKED>
+__device__ __forceinline__ int64_t at(int64_t m, int64_t k, int32_t d) {
+    if constexpr (BLOCKED) return (m >> 6) * 64 * (int64_t)d + k * 64 + (m & 63);
+    else return m * d + k;
+}
+
+// element e of the buffer (in storage order) -> (neuron, feature)
+template <bool BLOCKED>
+__device__ __forceinline__ void coords(int64_t e, int32_t d, int64_t &m, int64_t &k) {
+    if constexpr (BLOCKED) {
+        const int64_t blk = e / (64 * (int64_t)d);
+        const int64_t r = e - blk * 64 * (int64_t)d;
+        k = r >> 6;
+        m = blk * 64 + (r & 63);
+    } else {
+        m = e / d;
+        k = e - m * d;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_som_zero(float *p, int64_t n4, int32_t *cnt,
+                                                       int64_t nc) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride)
+        reinterpret_cast<f32x4 *>(p)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nc; i += stride) cnt[i] = 0;
+}
+
+// g[t] = exp(-t^2 / (2 sigma^2)), t = 0 .. count-1, evaluated in double and
+// rounded once.
+__global__ void k_som_gauss(float *g, int32_t count, double sigma) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < count) g[t] = (float)exp(-((double)t * (double)t) / (2.0 * sigma * sigma));
+}
+
+// Dense rows: one wave per input, lanes along the features.
+__global__ __launch_bounds__(kThreads) void k_som_scatter_rows(const float *__restrict__ X,
+                                                               int64_t n, int32_t d,
+                                                               const int32_t *__restrict__ bmu,
+                                                               int64_t nc, float *S,
+                                                               int32_t *cnt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); i < n;
+         i += waves) {
+        const int64_t b = bmu[i];
+        if (b < 0 || b >= nc) continue;
+        const float *x = X + i * d;
+        float *s = S + b * d;
+        for (int k = lane; k < d; k += 64) unsafeAtomicAdd(s + k, x[k]);
+        if (lane == 0) atomicAdd(cnt + b, 1);
+    }
+}
+
+// CSR rows: one wave per input, lanes along its stored entries; entries with
+// a column outside [0, d) are skipped.
+__global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
+    const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
+    const float *__restrict__ values, int64_t n, int32_t d, const int32_t *__restrict__ bmu,
+    int64_t nc, float *S, int32_t *cnt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); i < n;
+         i += waves) {
+        const int64_t b = bmu[i];
+        if (b < 0 || b >= nc) continue;
+        const int64_t lo = indptr[i], hi = indptr[i + 1];
+        for (int64_t p = lo + lane; p < hi; p += 64) {
+            const int32_t k = indices[p];
+            if (k >= 0 && k < d) unsafeAtomicAdd(S + at<true>(b, k, d), values[p]);
+        }
+        if (lane == 0) atomicAdd(cnt + b, 1);
+    }
+}
+
+// One separable pass over (neuron, feature) elements.  ALONG_X: offsets
+// m + t on the same map row; else m + t cols on the same map column.  FINAL:
+// out(m, k) = acc / den[m] written to the codebook where den[m] > 0.
+template <bool BLOCKED, bool ALONG_X, bool FINAL>
+__global__ __launch_bounds__(kThreads) void k_som_pass(const float *__restrict__ in,
+                                                       float *__restrict__ out, int64_t nc,
+                                                       int32_t d, int32_t rows, int32_t cols,
+                                                       int32_t R, const float *__restrict__ g,
+                                                       const float *__restrict__ den) {
+    const int64_t total = BLOCKED ? ((nc + 63) >> 6) * 64 * (int64_t)d : nc * (int64_t)d;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+        int64_t m, k;
+        coords<BLOCKED>(e, d, m, k);
+        if (m >= nc) continue;
+        const int64_t y = m / cols, x = m - y * cols;
+        const int64_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
+        const int64_t step = ALONG_X ? 1 : cols;
+        const int lo = (int)(pos < R ? -pos : -R);
+        const int hi = (int)(ext - 1 - pos < R ? ext - 1 - pos : R);
+        float acc = 0.0f;
+        for (int t = lo; t <= hi; ++t) acc = __builtin_fmaf(g[t < 0 ? -t : t],
+                                                           in[at<BLOCKED>(m + t * step, k, d)], acc);
+        if constexpr (FINAL) {
+            const float dv = den[m];
+            if (dv > 0.0f) out[e] = acc / dv;
+        } else {
+            out[e] = acc;
+        }
+    }
+}
+
+// The same two passes over the counts (one "feature", int32 input first).
+template <bool ALONG_X, typename TIn>
+__global__ __launch_bounds__(kThreads) void k_som_den_pass(const TIn *__restrict__ in,
+                                                           float *__restrict__ out, int64_t nc,
+                                                           int32_t rows, int32_t cols, int32_t R,
+                                                           const float *__restrict__ g) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t m = (int64_t)blockIdx.x * kThreads + threadIdx.x; m < nc; m += stride) {
+        const int64_t y = m / cols, x = m - y * cols;
+        const int64_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
+        const int64_t step = ALONG_X ? 1 : cols;
+        const int lo = (int)(pos < R ? -pos : -R);
+        const int hi = (int)(ext - 1 - pos < R ? ext - 1 - pos : R);
+        float acc = 0.0f;
+        for (int t = lo; t <= hi; ++t)
+            acc = __builtin_fmaf(g[t < 0 ? -t : t], (float)in[m + t * step], acc);
+        out[m] = acc;
+    }
+}
+
+// Quantisation error: mean over the inputs of sqrt(max(score, 0)), summed in
+// double by one workgroup in a fixed order (so the result is reproducible).
+__global__ __launch_bounds__(1024) void k_som_qe(const float *__restrict__ score, int64_t n,
+                                                 double *out) {
+    __shared__ double part[1024];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+        const double v = (double)score[i];
+        s += sqrt(v > 0.0 ? v : 0.0);
+    }
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 512; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = n > 0 ? part[0] / (double)n : __builtin_nan("");
+}
+
+unsigned grid_for(int64_t work, int n_cu) {
+    const int64_t want = (work + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)n_cu * 32;
+    return (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
+}
+
+}  // namespace
+
+hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
+    const bool blocked = a.csr;
+    const int64_t nc = (int64_t)a.rows * a.cols;
+    const int64_t elems = blocked ? ((nc + 63) / 64) * 64 * (int64_t)a.d : nc * (int64_t)a.d;
+    const int32_t R = a.R;
+    hipError_t err;
+
+    // S is allocated in whole 256-byte units, so rounding up to float4 stays inside it
+    const int64_t n4 = (elems + 3) / 4;
+    hipLaunchKernelGGL(k_som_zero, dim3(grid_for(n4 > nc ? n4 : nc, n_cu)), dim3(kThreads), 0,
+                       st, a.S, n4, a.cnt, nc);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_som_gauss, dim3((R + 1 + 255) / 256), dim3(256), 0, st, a.g, R + 1,
+                       a.sigma);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.n > 0) {
+        const dim3 gs(grid_for(a.n * 64, n_cu));  // one wave per input
+        if (blocked)
+            hipLaunchKernelGGL(k_som_scatter_csr, gs, dim3(kThreads), 0, st, a.indptr, a.indices,
+                               a.values, a.n, a.d, a.bmu, nc, a.S, a.cnt);
+        else
+            hipLaunchKernelGGL(k_som_scatter_rows, gs, dim3(kThreads), 0, st, a.X, a.n, a.d,
+                               a.bmu, nc, a.S, a.cnt);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const dim3 gd(grid_for(nc, n_cu));
+    hipLaunchKernelGGL((k_som_den_pass<true, int32_t>), gd, dim3(kThreads), 0, st, a.cnt, a.den_t,
+                       nc, a.rows, a.cols, R, a.g);
+    hipLaunchKernelGGL((k_som_den_pass<false, float>), gd, dim3(kThreads), 0, st, a.den_t, a.den,
+                       nc, a.rows, a.cols, R, a.g);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const dim3 ge(grid_for(elems, n_cu));
+    timing_before(st, "k_som_pass");
+    if (blocked) {
+        hipLaunchKernelGGL((k_som_pass<true, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
+                           nc, a.d, a.rows, a.cols, R, a.g, nullptr);
+        hipLaunchKernelGGL((k_som_pass<true, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
+                           nc, a.d, a.rows, a.cols, R, a.g, a.den);
+    } else {
+        hipLaunchKernelGGL((k_som_pass<false, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
+                           nc, a.d, a.rows, a.cols, R, a.g, nullptr);
+        hipLaunchKernelGGL((k_som_pass<false, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
+                           nc, a.d, a.rows, a.cols, R, a.g, a.den);
+    }
+    err = hipGetLastError();
+    timing_after(st);
+    return err;
+}
+
+hipError_t launch_som_qe(const float *score, int64_t n, double *out, hipStream_t st) {
+    hipLaunchKernelGGL(k_som_qe, dim3(1), dim3(1024), 0, st, score, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace vs

@@ -170,6 +170,26 @@ hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mas
                                int64_t mask_words, int32_t *idx_out, float *score_out,
                                hipStream_t st);
 
+// Batch SOM update (som.hip).  The codebook and the S / T buffers are
+// neuron-major (m * d + k) for dense rows, blocked feature-major
+// ((m / 64) * 64 d + k * 64 + m % 64) for CSR rows.
+struct SomArgs {
+    bool csr;
+    const float *X;                       // dense rows, n x d
+    const int32_t *indptr, *indices;      // CSR rows
+    const float *values;
+    int64_t n;
+    int32_t d;
+    const int32_t *bmu;                   // n
+    float *C;                             // codebook, updated in place
+    int32_t rows, cols, R;                // map and window radius (R < max(rows, cols))
+    double sigma;
+    float *S, *T, *den_t, *den, *g;       // workspace
+    int32_t *cnt;
+};
+hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu);
+hipError_t launch_som_qe(const float *score, int64_t n, double *out, hipStream_t st);
+
 // Timing hook (api.hip).
 void timing_before(hipStream_t st, const char *name);
 void timing_after(hipStream_t st);

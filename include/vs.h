@@ -229,6 +229,64 @@ int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg, const int32_t
                            float *score_out, void *stream);
 
 /*
+ * SOM epoch around the BMU search [BMU section 3: each input's closest
+ * neuron is found first, then that neuron and its neighbours are updated;
+ * the update rule is not given there, these calls take the batch map].
+ * The map is rows x cols neurons, planar; neuron m sits at grid row m / cols,
+ * column m % cols.  The neighbourhood weight of a BMU b on neuron m is
+ * h = exp(-(dy^2 + dx^2) / (2 sigma^2)) of their grid offset inside the
+ * square window max(|dy|, |dx|) <= radius, 0 outside, and the update is
+ *     w_m <- sum_i h(bmu_i, m) x_i / sum_i h(bmu_i, m)
+ * for every neuron whose denominator is > 0 (the others keep their weights).
+ * Inputs whose BMU lies outside [0, rows*cols) pull nothing.  sigma > 0 and
+ * finite; radius >= 0 and, unless 0, <= 8 sigma (so every weight in the
+ * window stays a normal fp32 number); else VS_ERR_SHAPE.  Arithmetic is
+ * fp32 with float atomics for the per-neuron sums: results agree with the
+ * exact update to a few units of fp32 rounding per summed term, and their
+ * last bits can differ from run to run.
+ *   vs_som_update      dense rows X (n x d) and bmu int32[n]; C (rows*cols x
+ *                      d, neuron-major) is updated in place.
+ *   vs_som_update_csr  CSR rows (as vs_bmu_search_csr; entries with a
+ *                      column outside [0, d) are skipped); CB is the
+ *                      64-neuron blocked codebook of vs_csr_block_codebook,
+ *                      updated in place.
+ *   vs_som_qe          quantisation error: mean over the n inputs of
+ *                      sqrt(max(score, 0)), score = squared distance to the
+ *                      BMU as the searches return it; summed in double in a
+ *                      fixed order; NaN for n = 0.  qe_out: one double in
+ *                      device memory (8-byte aligned).
+ *   vs_som_epoch       dense rows: vs_bmu_search (squared L2) into bmu_out /
+ *                      score_out (caller-owned int32[n] / float32[n], may be
+ *                      NULL when n = 0), then
+ *                      vs_som_qe into qe_out (may be NULL), then
+ *                      vs_som_update of C.
+ *   vs_som_epoch_csr   the same for CSR rows over the blocked codebook CB
+ *                      (vs_bmu_search_csr_blocked, vs_som_update_csr).
+ * Workspace: 256-byte aligned, at least the matching *_workspace() bytes
+ * (two rows*cols x d float buffers plus O(rows*cols); the epochs add the
+ * search's).  The workspace functions return 0 for invalid sizes.
+ */
+size_t vs_som_update_workspace(int32_t map_rows, int32_t map_cols, int32_t d);
+int vs_som_update(const float *X, int64_t n, int32_t d, const int32_t *bmu, float *C,
+                  int32_t map_rows, int32_t map_cols, float sigma, int32_t radius,
+                  void *workspace, size_t workspace_bytes, void *stream);
+int vs_som_update_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                      int64_t n, int64_t nnz, const int32_t *bmu, float *CB, int32_t map_rows,
+                      int32_t map_cols, int32_t d, float sigma, int32_t radius, void *workspace,
+                      size_t workspace_bytes, void *stream);
+int vs_som_qe(const float *score, int64_t n, double *qe_out, void *stream);
+size_t vs_som_epoch_workspace(int64_t n, int32_t map_rows, int32_t map_cols, int32_t d);
+int vs_som_epoch(const float *X, int64_t n, int32_t d, float *C, int32_t map_rows,
+                 int32_t map_cols, float sigma, int32_t radius, int32_t *bmu_out,
+                 float *score_out, double *qe_out, void *workspace, size_t workspace_bytes,
+                 void *stream);
+size_t vs_som_epoch_csr_workspace(int64_t n, int32_t map_rows, int32_t map_cols, int32_t d);
+int vs_som_epoch_csr(const int32_t *indptr, const int32_t *indices, const float *values,
+                     int64_t n, int64_t nnz, float *CB, int32_t map_rows, int32_t map_cols,
+                     int32_t d, float sigma, int32_t radius, int32_t *bmu_out, float *score_out,
+                     double *qe_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Squared L2 norms of candidates, float32, fixed summation order (the same
  * values the searches use).  feature_major == 0: C is nc x d (row j);
  * otherwise C is d x nc (column j).  norms_out is float32[nc].

@@ -291,11 +291,13 @@ def dense_as_csr(X):
 
 
 def som_update(indptr, indices, values, d: int, bmu, C_old, rows: int, cols: int,
-               sigma: float, radius: int, neurons=None, threads: int = 1, mutant: int = 0):
+               sigma: float, radius: int, neurons=None, threads: int = 1, mutant: int = 0,
+               old_rows=None):
     """Batch SOM update of the requested neurons (all by default).
 
     Inputs are CSR rows (see :func:`dense_as_csr` for a dense matrix);
-    ``C_old`` is the neuron-major codebook (rows*cols x d) before the update.
+    ``C_old`` is the neuron-major codebook (rows*cols x d) before the update,
+    or None when ``old_rows`` holds just the requested neurons' old weights.
     Returns (w float64[m, d], mass float64[m, d], den float64[m]) for the
     neurons in ``neurons`` order.
     """
@@ -304,12 +306,17 @@ def som_update(indptr, indices, values, d: int, bmu, C_old, rows: int, cols: int
     indices = _c(indices, np.int32)
     values = _c(values, np.float32)
     bmu = _c(bmu, np.int32)
-    C_old = np.asarray(C_old, np.float32)
     nc = rows * cols
-    assert C_old.shape == (nc, d) and bmu.shape[0] == indptr.shape[0] - 1
+    assert bmu.shape[0] == indptr.shape[0] - 1
     neurons = np.arange(nc, dtype=np.int32) if neurons is None else _c(neurons, np.int32)
     m = neurons.shape[0]
-    old = np.ascontiguousarray(C_old[neurons])
+    if old_rows is None:
+        C_old = np.asarray(C_old, np.float32)
+        assert C_old.shape == (nc, d)
+        old = np.ascontiguousarray(C_old[neurons])
+    else:
+        old = _c(old_rows, np.float32)
+        assert old.shape == (m, d)
     w = np.empty((m, d), np.float64)
     mass = np.empty((m, d), np.float64)
     den = np.empty(m, np.float64)

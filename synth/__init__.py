@@ -166,6 +166,12 @@ def dense_case(nq: int, nc: int, d: int, dist: str = "normal", key: int = 0):
     return normal(rq, (nq, d)), normal(rc, (nc, d))
 
 
+def random_indices(n: int, hi: int, key: int = 0) -> np.ndarray:
+    """int32[n] uniform in [0, hi) (e.g. a BMU assignment handed to an update)."""
+    (r,) = rng_children(8000 + key, 1)
+    return r.integers(0, hi, n).astype(np.int32)
+
+
 def random_mask(nq: int, nc: int, frac: float, key: int = 0) -> np.ndarray:
     """uint32 mask words [nq, ceil(nc/32)], each candidate excluded with
     probability ``frac``; bits at or above nc are left clear."""

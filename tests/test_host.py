@@ -221,6 +221,74 @@ def test_diversity_validation(L):
     assert call(ws_bytes=8) == 4
 
 
+def test_som_validation(L):
+    F = ctypes.c_float
+    assert L.vs_som_update_workspace(0, 4, 8) == 0
+    assert L.vs_som_update_workspace(4, 0, 8) == 0
+    assert L.vs_som_update_workspace(4, 4, 0) == 0
+    # two 64-neuron-rounded float buffers, three count/denominator arrays, the 1-D weights
+    assert L.vs_som_update_workspace(4, 4, 8) == 2 * 64 * 8 * 4 + 3 * 256 + 256
+    assert L.vs_som_epoch_workspace(-1, 4, 4, 8) == 0
+    assert L.vs_som_epoch_workspace(10, 4, 4, 8) > L.vs_som_update_workspace(4, 4, 8)
+    assert L.vs_som_epoch_csr_workspace(10, 4, 4, 8) > L.vs_som_update_workspace(4, 4, 8)
+
+    def upd(X=FAKE, n=10, d=8, bmu=FAKE, C=FAKE, rows=4, cols=4, sigma=1.0, R=2, ws=FAKE,
+            ws_bytes=1 << 20):
+        return L.vs_som_update(_P(X), n, d, _P(bmu), _P(C), rows, cols, F(sigma), R, _P(ws),
+                               ws_bytes, None)
+    assert upd(sigma=0.0) == 2
+    assert upd(sigma=-1.0) == 2
+    assert upd(sigma=float("nan")) == 2
+    assert upd(sigma=float("inf")) == 2
+    assert upd(R=-1) == 2
+    assert upd(sigma=0.25, R=3) == 2      # window beyond 8 sigma
+    assert upd(sigma=0.01, R=0, ws_bytes=100) == 4  # R = 0 is the per-neuron mean at any sigma
+    assert upd(rows=0) == 2
+    assert upd(n=-1) == 2
+    assert upd(n=0, X=0) == 0             # nothing to do
+    assert upd(X=0) == 1
+    assert upd(bmu=0) == 1
+    assert upd(C=FAKE + 2) == 5
+    assert upd(ws=FAKE + 16) == 5
+    assert upd(ws_bytes=100) == 4
+
+    def upd_csr(indptr=FAKE, indices=FAKE, values=FAKE, n=10, nnz=30, bmu=FAKE, CB=FAKE,
+                rows=4, cols=4, d=8, sigma=1.0, R=2, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_som_update_csr(_P(indptr), _P(indices), _P(values), n, nnz, _P(bmu), _P(CB),
+                                   rows, cols, d, F(sigma), R, _P(ws), ws_bytes, None)
+    assert upd_csr(d=0) == 2
+    assert upd_csr(nnz=-1) == 2
+    assert upd_csr(indices=0) == 1
+    assert upd_csr(nnz=0, indices=0, values=0, ws_bytes=10) == 4
+    assert upd_csr(values=FAKE + 1) == 5
+    assert upd_csr(ws_bytes=10) == 4
+
+    assert L.vs_som_qe(_P(FAKE), -1, _P(FAKE), None) == 2
+    assert L.vs_som_qe(_P(FAKE), 5, None, None) == 1
+    assert L.vs_som_qe(None, 5, _P(FAKE), None) == 1
+    assert L.vs_som_qe(_P(FAKE), 5, _P(FAKE + 4), None) == 5
+
+    def ep(X=FAKE, n=10, d=8, C=FAKE, rows=4, cols=4, sigma=1.0, R=2, bmu=FAKE, score=FAKE,
+           qe=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_som_epoch(_P(X), n, d, _P(C), rows, cols, F(sigma), R, _P(bmu), _P(score),
+                              _P(qe), _P(ws), ws_bytes, None)
+    assert ep(sigma=0.0) == 2
+    assert ep(cols=0) == 2
+    assert ep(bmu=0) == 1
+    assert ep(score=0) == 1
+    assert ep(qe=FAKE + 4) == 5
+    assert ep(ws_bytes=10) == 4
+
+    def ep_csr(indptr=FAKE, indices=FAKE, values=FAKE, n=10, nnz=30, CB=FAKE, rows=4, cols=4,
+               d=8, sigma=1.0, R=2, bmu=FAKE, score=FAKE, qe=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_som_epoch_csr(_P(indptr), _P(indices), _P(values), n, nnz, _P(CB), rows, cols,
+                                  d, F(sigma), R, _P(bmu), _P(score), _P(qe), _P(ws), ws_bytes,
+                                  None)
+    assert ep_csr(R=-2) == 2
+    assert ep_csr(CB=0) == 1
+    assert ep_csr(ws_bytes=10) == 4
+
+
 def test_norms_validation(L):
     assert L.vs_candidate_norms(_P(FAKE), 10, 0, 0, _P(FAKE), None) == 2
     assert L.vs_candidate_norms(_P(0), 10, 4, 0, _P(FAKE), None) == 1
