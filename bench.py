@@ -15,6 +15,12 @@ same workload on the host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
                     [--no-cpu-baseline] [--traffic-json FILE]
+                    [--som [--som-sigma S --som-radius R]]
+
+--som turns a BMU workload (1, 2, 4, 5) into SOM training: one step = one
+epoch (vs_som_epoch / vs_som_epoch_csr: search, quantisation error, batch
+update of the codebook in place) on the workload's map; the line adds the
+epoch's per-phase times.
 """
 from __future__ import annotations
 
@@ -59,6 +65,12 @@ def parse():
                     help="sparse workload: 'blocked' times the 64-neuron blocked copy of the "
                          "codebook plus the search over it, 'plain' the search over the "
                          "row-padded feature-major codebook")
+    ap.add_argument("--som", action="store_true",
+                    help="one step = one SOM epoch around the search (workloads 1, 2, 4, 5)")
+    ap.add_argument("--som-sigma", type=float, default=2.0,
+                    help="Gaussian neighbourhood width in map cells")
+    ap.add_argument("--som-radius", type=int, default=6,
+                    help="square window radius in map cells (default 3 sigma)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -236,6 +248,166 @@ def setup(k, torch, vs, a):
     chunks = (nc + (127 if a.csr_storage == "f16" else 63)) // (128 if a.csr_storage == "f16" else 64)
     rounds = (chunks + min(8, chunks) - 1) // min(8, chunks)  # one scan launch per round
     return w, step, pairs, flops, rounds, cfg
+
+
+SOM_MAPS = {1: (32, 32), 2: (128, 128), 4: (256, 256), 5: (512, 512)}
+
+
+def setup_som(k, torch, vs, a):
+    """One step = one SOM epoch on workload k's inputs and codebook (the map
+    trains on from step to step, as successive epochs do)."""
+    import synth
+    if k not in SOM_MAPS:
+        raise SystemExit(f"--som needs a BMU workload ({sorted(SOM_MAPS)})")
+    dev = torch.device("cuda:0")
+    w = synth.workload(k)
+    rows, cols = SOM_MAPS[k]
+    sig, R = a.som_sigma, a.som_radius
+    nq, nc, d = w["nq"], w["nc"], w["d"]
+    L = vs.lib()
+    bmu = torch.empty(nq, dtype=torch.int32, device=dev)
+    score = torch.empty(nq, dtype=torch.float32, device=dev)
+    qe = torch.empty(1, dtype=torch.float64, device=dev)
+    phases = {}
+    if w["kind"] == "dense":
+        X = torch.from_numpy(w["Q"]).to(dev)
+        C = torch.from_numpy(w["C"]).to(dev)
+        ws = torch.empty(L.vs_som_epoch_workspace(nq, rows, cols, d), dtype=torch.uint8,
+                         device=dev)
+        ws_s = torch.empty(L.vs_bmu_search_workspace(nq, nc, d, 0), dtype=torch.uint8, device=dev)
+        ws_u = torch.empty(L.vs_som_update_workspace(rows, cols, d), dtype=torch.uint8,
+                           device=dev)
+
+        def step():
+            vs.vs_som_epoch(X, C, (rows, cols), sig, R, bmu_out=bmu, score_out=score, qe_out=qe,
+                            workspace=ws)
+        phases["search"] = lambda: vs.vs_bmu_search(X, C, 0, idx_out=bmu, score_out=score,
+                                                    workspace=ws_s)
+        phases["update"] = lambda: vs.vs_som_update(X, bmu, C, (rows, cols), sig, R,
+                                                    workspace=ws_u)
+        in_bytes = nq * d * 4
+        flops = 2.0 * d * nq * nc
+        launches = 1
+    else:
+        indptr = torch.from_numpy(w["indptr"]).to(dev)
+        indices = torch.from_numpy(w["indices"]).to(dev)
+        values = torch.from_numpy(w["values"]).to(dev)
+        CB = vs.vs_csr_block_codebook(torch.from_numpy(w["CT"]).to(dev))
+        torch.cuda.synchronize()
+        ws = torch.empty(L.vs_som_epoch_csr_workspace(nq, rows, cols, d), dtype=torch.uint8,
+                         device=dev)
+        ws_s = torch.empty(L.vs_bmu_search_csr_workspace(nq, nc, d, 0), dtype=torch.uint8,
+                           device=dev)
+        ws_u = torch.empty(L.vs_som_update_workspace(rows, cols, d), dtype=torch.uint8,
+                           device=dev)
+
+        def step():
+            vs.vs_som_epoch_csr(indptr, indices, values, CB, (rows, cols), d, sig, R,
+                                bmu_out=bmu, score_out=score, qe_out=qe, workspace=ws)
+        phases["search"] = lambda: vs.vs_bmu_search_csr_blocked(
+            indptr, indices, values, CB, nc, 0, d=d, idx_out=bmu, score_out=score,
+            workspace=ws_s)
+        phases["update"] = lambda: vs.vs_som_update_csr(indptr, indices, values, bmu, CB,
+                                                        (rows, cols), d, sig, R, workspace=ws_u)
+        w["nnz"] = int(w["indices"].shape[0])
+        w["value_bytes"] = 4
+        in_bytes = w["nnz"] * 8 + (nq + 1) * 4
+        flops = 2.0 * w["nnz"] * nc
+        chunks = (nc + 63) // 64
+        launches = (chunks + min(8, chunks) - 1) // min(8, chunks)
+    phases["qe"] = lambda: vs.vs_som_qe(score, qe_out=qe)
+    # the update's algorithmic HBM bytes: read the inputs and their BMUs once,
+    # write every neuron's new weights once
+    w["update_bytes"] = in_bytes + nq * 4 + nc * d * 4
+    w["som_phases"] = phases
+    w["som_qe"] = qe
+    cfg = dict(workload=w["name"] + "+som_epoch", nq=nq, nc=nc, d=d, map=f"{rows}x{cols}",
+               sigma=sig, radius=R, metric="l2sq_min",
+               update="batch map, Gaussian in a square window, separable passes")
+    if w["kind"] == "csr":
+        cfg.update(nnz=w["nnz"], codebook_layout="blocked")
+    return w, step, nq * nc, flops, launches, cfg
+
+
+def som_phase_times(w, torch, reps=3):
+    """Mean ms of each phase of the epoch, run as the separate entry points
+    the epoch calls, bracketed by events on the current stream."""
+    out = {}
+    for name in ("search", "qe", "update"):
+        fn = w["som_phases"][name]
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+    ub = w["update_bytes"]
+    out["update_algorithmic_bytes"] = ub
+    out["update_GBps"] = round(ub / (out["update_ms"] * 1e-3) / 1e9, 1)
+    out["update_frac_hbm"] = round(out["update_GBps"] / PEAK_HBM_GBS, 4)
+    return out
+
+
+def cpu_baseline_som(k, w, target_s):
+    """Oracle epoch on a bounded sample: the exact search on a sample of
+    inputs plus the update of a sample of neurons (BMUs drawn uniformly),
+    scaled to the whole epoch."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = oracle.default_threads()
+    rows, cols = SOM_MAPS[k]
+    nq, nc, d = w["nq"], w["nc"], w["d"]
+    half = target_s / 2
+    if w["kind"] == "dense":
+        t0 = time.perf_counter()
+        oracle.dense(w["Q"][:threads], w["C"], 0, threads=threads)
+        per_q = (time.perf_counter() - t0) / threads
+        ns = int(max(threads, min(nq, half / max(per_q, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.dense(w["Q"][:ns], w["C"], 0, threads=threads)
+        search_s = (time.perf_counter() - t0) * nq / ns
+        ip, ix, vv = oracle.dense_as_csr(w["Q"])
+        C_old = w["C"]
+        old = None
+    else:
+        col_sq = oracle.sqnorms(w["CT"], feature_major=True, threads=threads)
+        ptr = w["indptr"]
+        t0 = time.perf_counter()
+        oracle.csr(ptr[:threads + 1], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq,
+                   threads=threads)
+        per_q = (time.perf_counter() - t0) / threads
+        ns = int(max(threads, min(nq, half / max(per_q, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.csr(ptr[:ns + 1], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq,
+                   threads=threads)
+        search_s = (time.perf_counter() - t0) * nq / ns
+        ip, ix, vv = w["indptr"], w["indices"], w["values"]
+        C_old = None
+    bmu = synth.random_indices(nq, nc, key=k)
+    probe = np.arange(threads, dtype=np.int32)
+    kw = {} if C_old is not None else {"old_rows": np.ascontiguousarray(w["CT"][:, probe].T)}
+    t0 = time.perf_counter()
+    oracle.som_update(ip, ix, vv, d, bmu, C_old, rows, cols, 2.0, 6, neurons=probe,
+                      threads=threads, **kw)
+    per_n = (time.perf_counter() - t0) / threads
+    nn = int(max(threads, min(nc, half / max(per_n, 1e-9))))
+    sel = synth.sample_queries(nc, nn, key=k).astype(np.int32)
+    kw = {} if C_old is not None else {"old_rows": np.ascontiguousarray(w["CT"][:, sel].T)}
+    t0 = time.perf_counter()
+    oracle.som_update(ip, ix, vv, d, bmu, C_old, rows, cols, 2.0, 6, neurons=sel,
+                      threads=threads, **kw)
+    dt_u = time.perf_counter() - t0
+    update_s = dt_u * nc / nn
+    epoch_s = search_s + update_s
+    return dict(value=nq * nc / epoch_s, unit="pairs/s", cores=threads, kind="oracle",
+                sample=(f"search of {ns} of {nq} inputs x all {nc} neurons and update of {nn} "
+                        f"of {nc} neurons, scaled to one epoch"),
+                epoch_s=round(epoch_s, 2), search_s=round(search_s, 2),
+                update_s=round(update_s, 2))
 
 
 # ------------------------------------------------------------ cpu leg --
@@ -422,7 +594,10 @@ def main():
         measure_l2_roof(a, torch)
         return
     log(f"workload {a.workload}: generating inputs")
-    w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs, a)
+    if a.som:
+        w, step, pairs, flops, launches_per_step, cfg = setup_som(a.workload, torch, vs, a)
+    else:
+        w, step, pairs, flops, launches_per_step, cfg = setup(a.workload, torch, vs, a)
     torch.cuda.synchronize()
     log(f"warmup {a.warmup} steps")
     for _ in range(a.warmup):
@@ -465,16 +640,23 @@ def main():
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
     roof["traffic"] = (None if "mode" in cfg and cfg["mode"] in ("gram", "unfused") else
-                       load_traffic(a.traffic_json, DOMINANT[a.workload], cfg["workload"]))
+                       load_traffic(a.traffic_json, DOMINANT[a.workload],
+                                    cfg["workload"].replace("+som_epoch", "")))
     out = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": cfg, "roofline": roof,
     }
+    if a.som:
+        qe_final = float(w["som_qe"].cpu()[0])
+        log("epoch phases")
+        out["som_epoch"] = som_phase_times(w, torch)
+        out["som_epoch"]["qe_last_epoch"] = qe_final
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(a.workload, w, a.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_som(a.workload, w, a.cpu_seconds) if a.som else
+                               cpu_baseline(a.workload, w, a.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

@@ -541,6 +541,9 @@ static int som_params(int32_t rows, int32_t cols, int32_t d, float sigma, int32_
     if (!(sigma > 0.0f) || !(sigma < 3.0e38f) || radius < 0) return VS_ERR_SHAPE;
     // every weight inside the window stays a normal fp32 number (>= e^-64)
     if (radius > 0 && (double)radius > 8.0 * (double)sigma) return VS_ERR_SHAPE;
+    // one pass launch covers 64 neurons x 32 features per workgroup and stays
+    // under 2^32 threads (each of the two buffers is then < 128 GiB)
+    if (((int64_t)rows * cols + 63) / 64 * 64 * (int64_t)d > (int64_t(1) << 35)) return VS_ERR_SHAPE;
     const int32_t ext = rows > cols ? rows : cols;
     *R_eff = radius < ext - 1 ? radius : ext - 1;
     return VS_OK;

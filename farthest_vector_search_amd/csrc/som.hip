@@ -27,6 +27,8 @@
 // Threads run along the contiguous axis (k, resp. m within a block), so every
 // load and store of a pass is coalesced; the window's other taps are re-reads
 // of lines the neighbouring waves just fetched (L1 / L2 hits).
+#include <type_traits>
+
 #include "vs_internal.h"
 
 namespace vs {
@@ -143,6 +145,185 @@ __global__ __launch_bounds__(kThreads) void k_som_pass(const float *__restrict__
     }
 }
 
+// The blocked layout's passes.  A workgroup owns one 64-neuron block (lane =
+// neuron) and 4 x kKV features (kKV per wave); each thread works out its
+// neuron's grid position and window once, then for every tap reads kKV
+// features of the tap neuron -- kKV loads, each a coalesced 256-byte row of a
+// block.  Workgroups are numbered XCD by XCD: workgroup i runs on XCD i % 8
+// and XCD x owns a contiguous eighth of the blocks, sweeping all of its blocks
+// at one feature chunk before the next, so the neighbouring blocks a window
+// reaches are (mostly) fetched into the same XCD's L2.
+constexpr int kKV = 8;
+
+template <bool ALONG_X, bool FINAL>
+__global__ __launch_bounds__(kThreads) void k_som_pass_blk(const float *__restrict__ in,
+                                                           float *__restrict__ out, int32_t nc,
+                                                           int32_t d, int32_t rows, int32_t cols,
+                                                           int32_t R, int32_t per_xcd,
+                                                           const float *__restrict__ g,
+                                                           const float *__restrict__ den) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t lin = blockIdx.x, r = lin >> 3;
+    const int32_t blk = (lin & 7) * per_xcd + r % per_xcd;
+    const int32_t kbase = ((r / per_xcd) * 4 + wave) * kKV;
+    const int64_t m64 = (int64_t)blk * 64 + lane;
+    if (m64 >= nc || kbase >= d) return;
+    const int32_t m = (int32_t)m64;
+    float dv = 1.0f;
+    if constexpr (FINAL) {
+        dv = den[m];
+        if (!(dv > 0.0f)) return;  // no input in the window: the neuron keeps its weights
+    }
+    const int32_t y = m / cols, x = m - y * cols;
+    const int32_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
+    const int32_t step = ALONG_X ? 1 : cols;
+    const int lo = pos < R ? -pos : -R;
+    const int hi = ext - 1 - pos < R ? ext - 1 - pos : R;
+    const int64_t D64 = 64 * (int64_t)d;
+    const int nk = d - kbase < kKV ? d - kbase : kKV;
+    float acc[kKV];
+#pragma unroll
+    for (int i = 0; i < kKV; ++i) acc[i] = 0.0f;
+    for (int t = lo; t <= hi; ++t) {
+        const int32_t n2 = m + t * step;
+        const float *p = in + (int64_t)(n2 >> 6) * D64 + (n2 & 63) + (int64_t)kbase * 64;
+        const float gt = g[t < 0 ? -t : t];
+        if (nk == kKV) {
+#pragma unroll
+            for (int i = 0; i < kKV; ++i) acc[i] = __builtin_fmaf(gt, p[i * 64], acc[i]);
+        } else {
+            for (int i = 0; i < nk; ++i) acc[i] = __builtin_fmaf(gt, p[i * 64], acc[i]);
+        }
+    }
+    float *o = out + (int64_t)blk * D64 + lane + (int64_t)kbase * 64;
+#pragma unroll
+    for (int i = 0; i < kKV; ++i)
+        if (i < nk) o[i * 64] = FINAL ? acc[i] / dv : acc[i];
+}
+
+// Both passes in one sweep (blocked layout, window radius R <= 8 known at
+// compile time).  A wave owns one feature k and a strip of 64 map columns
+// x0 .. x0+63 and walks down the map one row at a time:
+//   - the row's 64 values plus R halo columns on each side (0 off the map)
+//     go to a per-wave LDS row, from which each lane sums its column's
+//     window along the row: X(y', x) = sum_t g(t) S(y', x + t);
+//   - X(y', x) is added, weighted g(s), to the pending outputs of rows
+//     y' - s, s = -R .. R, held in a ring of 2R+1 registers (the row loop is
+//     unrolled by 2R+1 so every ring slot is a fixed register);
+//   - once row y' is in, output row y' - R has all its terms: it is divided
+//     by its denominator and stored (or left alone when that is 0).
+// S is read once (plus the halo columns) and the codebook written once; no
+// intermediate buffer.  The next row's loads are issued before the current
+// row is summed.
+// Calls f(integral_constant<int, U>) for U = B .. E-1 (compile-time unrolling).
+template <int B, int E>
+struct Unroll {
+    template <class F>
+    __device__ __forceinline__ static void run(F &f) {
+        f(std::integral_constant<int, B>{});
+        Unroll<B + 1, E>::run(f);
+    }
+};
+template <int E>
+struct Unroll<E, E> {
+    template <class F>
+    __device__ __forceinline__ static void run(F &) {}
+};
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
+    const float *__restrict__ S, float *__restrict__ C, int32_t d, int32_t rows, int32_t cols,
+    int32_t ntx, int64_t n_items, const float *__restrict__ g, const float *__restrict__ den) {
+    constexpr int P = 2 * R + 1;
+    constexpr int W = 64 + 2 * R;
+    __shared__ float buf[kThreads / 64][W];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+    if (item >= n_items) return;
+    const int32_t k = (int32_t)(item / ntx);
+    const int32_t x0 = (int32_t)(item - (int64_t)k * ntx) * 64;
+    const int64_t D64 = 64 * (int64_t)d;
+    const float *Sk = S + (int64_t)k * 64;
+    float *Ck = C + (int64_t)k * 64;
+    float *row = buf[wave];
+
+    // each lane loads its own column and, lanes < 2R, one halo column:
+    // left halo x0-R+lane (slot lane), right halo x0+64+lane-R (slot 64+lane)
+    const int32_t xc = x0 + lane;
+    const bool c_ok = xc < cols;
+    const int32_t xh = lane < R ? x0 - R + lane : x0 + 64 + (lane - R);
+    const bool h_ok = lane < 2 * R && xh >= 0 && xh < cols;
+    const int hslot = lane < R ? lane : 64 + lane;
+    // clamped (always in-bounds) columns, so every load is unconditional
+    const int32_t xcl = c_ok ? xc : cols - 1;
+    const int32_t xhl = h_ok ? xh : (xh < 0 ? 0 : cols - 1);
+    auto at_rc = [&](int32_t y, int32_t x) -> int64_t {
+        const int32_t n = y * cols + x;
+        return (int64_t)(n >> 6) * D64 + (n & 63);
+    };
+
+    float gw[R + 1];
+#pragma unroll
+    for (int i = 0; i <= R; ++i) gw[i] = g[i];
+    float acc[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) acc[i] = 0.0f;
+
+    float vc = Sk[at_rc(0, xcl)], vh = Sk[at_rc(0, xhl)];
+    // denominator of the output row finished after the current input row
+    // (row yy - R; none for yy < R)
+    float dnext = 0.0f;
+    int32_t base = 0;
+    // one input row; u = yy mod P is a compile-time constant
+    auto step = [&](auto U) {
+        constexpr int u = decltype(U)::value;
+        const int32_t yy = base + u;
+        if (yy < rows) {
+            const float cc = c_ok ? vc : 0.0f;
+            const float hh = h_ok ? vh : 0.0f;
+            const float dv = dnext;
+            {
+                const int32_t yn = yy + 1 < rows ? yy + 1 : rows - 1;
+                vc = Sk[at_rc(yn, xcl)];
+                vh = Sk[at_rc(yn, xhl)];
+                int32_t yd1 = yy + 1 - R;
+                yd1 = yd1 < 0 ? 0 : (yd1 >= rows ? rows - 1 : yd1);
+                dnext = den[(int64_t)yd1 * cols + xcl];
+            }
+            asm volatile("" ::: "memory");
+            row[R + lane] = cc;
+            if (lane < 2 * R) row[hslot] = hh;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            float X = gw[0] * row[R + lane];
+#pragma unroll
+            for (int t = 1; t <= R; ++t)
+                X = __builtin_fmaf(gw[t], row[R + lane - t] + row[R + lane + t], X);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int sft = -R; sft <= R; ++sft) {
+                const int q = (u + sft + 2 * P) % P;  // constant once unrolled
+                acc[q] = __builtin_fmaf(gw[sft < 0 ? -sft : sft], X, acc[q]);
+            }
+            constexpr int qd = (u - R + 2 * P) % P;
+            const int32_t yd = yy - R;
+            if (yd >= 0 && c_ok && dv > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] / dv;
+            acc[qd] = 0.0f;
+        }
+    };
+    for (; base < rows; base += P) Unroll<0, P>::run(step);
+    // the last R output rows have no further input rows
+    for (int j = 0; j < R; ++j) {
+        const int32_t y = rows - R + j;
+        if (y < 0 || !c_ok) continue;
+        const int q = y % P;
+        float v = 0.0f;
+#pragma unroll
+        for (int qq = 0; qq < P; ++qq) v = qq == q ? acc[qq] : v;
+        const float dv = den[(int64_t)y * cols + xc];
+        if (dv > 0.0f) Ck[at_rc(y, xc)] = v / dv;
+    }
+}
+
 // The same two passes over the counts (one "feature", int32 input first).
 template <bool ALONG_X, typename TIn>
 __global__ __launch_bounds__(kThreads) void k_som_den_pass(const TIn *__restrict__ in,
@@ -222,21 +403,36 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
                        nc, a.rows, a.cols, R, a.g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const dim3 ge(grid_for(elems, n_cu));
-    timing_before(st, "k_som_pass");
-    if (blocked) {
-        hipLaunchKernelGGL((k_som_pass<true, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
-                           nc, a.d, a.rows, a.cols, R, a.g, nullptr);
-        hipLaunchKernelGGL((k_som_pass<true, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
-                           nc, a.d, a.rows, a.cols, R, a.g, a.den);
+    if (blocked && R >= 1 && R <= 8) {
+        const int32_t ntx = (a.cols + 63) / 64;
+        const int64_t items = (int64_t)a.d * ntx;
+        const dim3 gw((unsigned)((items + 3) / 4));
+#define VS_SMOOTH(RR)                                                                          \
+    case RR:                                                                                   \
+        hipLaunchKernelGGL((k_som_smooth_blk<RR>), gw, dim3(kThreads), 0, st, a.S, a.C, a.d,    \
+                           a.rows, a.cols, ntx, items, a.g, a.den);                            \
+        break;
+        switch (R) {
+            VS_SMOOTH(1) VS_SMOOTH(2) VS_SMOOTH(3) VS_SMOOTH(4)
+            VS_SMOOTH(5) VS_SMOOTH(6) VS_SMOOTH(7) VS_SMOOTH(8)
+        }
+#undef VS_SMOOTH
+    } else if (blocked) {
+        const int32_t nblk = (int32_t)((nc + 63) / 64);
+        const int32_t per = (nblk + 7) / 8;
+        const int64_t nkc = (a.d + 4 * kKV - 1) / (4 * kKV);
+        const dim3 gb((unsigned)(8 * (int64_t)per * nkc));
+        hipLaunchKernelGGL((k_som_pass_blk<true, false>), gb, dim3(kThreads), 0, st, a.S, a.T,
+                           (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, nullptr);
+        hipLaunchKernelGGL((k_som_pass_blk<false, true>), gb, dim3(kThreads), 0, st, a.T, a.C,
+                           (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, a.den);
     } else {
         hipLaunchKernelGGL((k_som_pass<false, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
                            nc, a.d, a.rows, a.cols, R, a.g, nullptr);
         hipLaunchKernelGGL((k_som_pass<false, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
                            nc, a.d, a.rows, a.cols, R, a.g, a.den);
     }
-    err = hipGetLastError();
-    timing_after(st);
-    return err;
+    return hipGetLastError();
 }
 
 hipError_t launch_som_qe(const float *score, int64_t n, double *out, hipStream_t st) {

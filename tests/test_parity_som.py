@@ -128,9 +128,18 @@ def test_som_update_no_inputs_in_window_keeps_codebook():
     assert not np.array_equal(w[0], C[0])
 
 
+# R 1..8 runs the one-sweep kernel (every radius once, with maps narrower and
+# wider than its 64-column strips, fewer rows than R, one row, one column);
+# R 0 and R > 8 run the two-pass kernels
 @pytest.mark.parametrize("rows,cols,d,n,sigma,R,density", [
     (8, 8, 300, 200, 1.5, 3, 0.05),
     (5, 27, 129, 400, 1.0, 2, 0.1),    # nc not a multiple of 64, ragged d
+    (9, 64, 16, 200, 0.5, 1, 0.2),
+    (12, 200, 24, 500, 1.0, 7, 0.1),   # four strips, the last one partial
+    (3, 130, 20, 300, 1.0, 8, 0.1),    # fewer rows than R
+    (1, 70, 40, 100, 1.0, 4, 0.2),     # one row
+    (70, 1, 40, 100, 2.0, 5, 0.2),     # one column
+    (4, 5, 9, 30, 1.0, 6, 0.3),        # window beyond both edges
     (16, 16, 64, 900, 2.0, 16, 0.2),
     (3, 3, 17, 40, 1.0, 0, 0.3),
 ])
