@@ -65,6 +65,10 @@ def _load(mutant: int = 0) -> ctypes.CDLL:
                                    I64, P, P, P, P]
     lib.orc_mean_sqrt.argtypes = [P, I64]
     lib.orc_mean_sqrt.restype = ctypes.c_double
+    lib.orc_div_run_centroid.argtypes = [P, I64, I64, I64, INT, P, P, P, P, P]
+    lib.orc_div_replay_centroid.argtypes = [P, I64, I64, I64, INT, P, P, P, P, P, P, P, P, P]
+    lib.orc_div_run_centroid.restype = None
+    lib.orc_div_replay_centroid.restype = None
     lib.orc_mutant.restype = INT
     for f in (lib.orc_dense, lib.orc_pair_values, lib.orc_sqnorms, lib.orc_csr,
               lib.orc_div_run, lib.orc_gram_cos, lib.orc_div_replay, lib.orc_som_update):
@@ -270,6 +274,67 @@ def div_replay(G, seeds, picks, threads: int = 1, mutant: int = 0):
                            _p(out["bidx"][lo:hi]), _p(out["best"][lo:hi]),
                            _p(out["gap"][lo:hi]), _p(out["pick_value"][lo:hi]),
                            _p(out["pick_ok"][lo:hi]), _p(scratch))
+
+    shards = _shards(nseq, threads)
+    if len(shards) <= 1:
+        for s in shards:
+            run(s)
+    else:
+        with ThreadPoolExecutor(len(shards)) as ex:
+            list(ex.map(run, shards))
+    return out
+
+
+def div_run_centroid(C, seeds, T: int, threads: int = 1, mutant: int = 0):
+    """Diversity sequences with the centroid of the sequence so far as the
+    reference.  Returns (picks, cosines to the centroid), both [nseq, T]."""
+    lib = _load(mutant)
+    C = _c(C, np.float32)
+    seeds = _c(seeds, np.int32)
+    n, d = C.shape
+    nseq = seeds.shape[0]
+    picks = np.empty((nseq, T), np.int32)
+    vals = np.empty((nseq, T), np.float64)
+
+    def run(lo_hi):
+        lo, hi = lo_hi
+        scratch = np.empty((n + 31) // 32, np.uint32)
+        cent = np.empty(d, np.float64)
+        lib.orc_div_run_centroid(_p(C), n, d, hi - lo, T, _p(seeds[lo:hi]), _p(picks[lo:hi]),
+                                 _p(vals[lo:hi]), _p(scratch), _p(cent))
+
+    shards = _shards(nseq, threads)
+    if len(shards) <= 1:
+        for s in shards:
+            run(s)
+    else:
+        with ThreadPoolExecutor(len(shards)) as ex:
+            list(ex.map(run, shards))
+    return picks, vals
+
+
+def div_replay_centroid(C, seeds, picks, threads: int = 1, mutant: int = 0):
+    """Replay recorded centroid-reference picks [nseq, T] from the table C;
+    returns the same dict as :func:`div_replay`."""
+    lib = _load(mutant)
+    C = _c(C, np.float32)
+    seeds = _c(seeds, np.int32)
+    picks = _c(picks, np.int32)
+    n, d = C.shape
+    nseq, T = picks.shape
+    out = {k: np.empty((nseq, T), dt) for k, dt in
+           (("bidx", np.int32), ("best", np.float64), ("gap", np.float64),
+            ("pick_value", np.float64), ("pick_ok", np.int32))}
+
+    def run(lo_hi):
+        lo, hi = lo_hi
+        scratch = np.empty((n + 31) // 32, np.uint32)
+        cent = np.empty(d, np.float64)
+        lib.orc_div_replay_centroid(_p(C), n, d, hi - lo, T, _p(seeds[lo:hi]),
+                                    _p(picks[lo:hi]), _p(out["bidx"][lo:hi]),
+                                    _p(out["best"][lo:hi]), _p(out["gap"][lo:hi]),
+                                    _p(out["pick_value"][lo:hi]), _p(out["pick_ok"][lo:hi]),
+                                    _p(scratch), _p(cent))
 
     shards = _shards(nseq, threads)
     if len(shards) <= 1:

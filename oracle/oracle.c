@@ -484,3 +484,143 @@ double orc_mean_sqrt(const double *d2, int64_t n)
 #endif
     return s / (double)n;
 }
+
+/* ------------------------------------------- centroid-reference diversity -- */
+/*
+ * The diversity run with the sequence's centroid as the reference: "Issue
+ * 9-014 ...", "FP16 storage (compounding optimization)" speaks of the
+ * candidate most different from the centroid.  Reading: after the seed and t
+ * picks, the reference is the mean of those t+1 rows; each step takes the
+ * unmasked row with the smallest true cosine to it (lowest index on ties) and
+ * masks it.  A zero centroid has no direction: every candidate then scores 0
+ * (so the lowest unmasked index wins).  Everything in double.
+ *
+ * MUTANT 15: the centroid leaves out the seed;  MUTANT 16: the centroid is
+ * not accumulated (only the last pick is kept).
+ */
+static double cosine_ref(const float *c, const double *ref, int64_t d)
+{
+    double rr = 0.0, cc = 0.0, rc = 0.0;
+    for (int64_t k = 0; k < d; ++k) {
+        const double b = (double)c[k];
+        rr += ref[k] * ref[k];
+        cc += b * b;
+        rc += ref[k] * b;
+    }
+    if (rr == 0.0 || cc == 0.0)
+        return 0.0;
+    return rc / (sqrt(rr) * sqrt(cc));
+}
+
+/* sum <- sum + row (double), or sum <- row when `reset` */
+static void acc_row(double *sum, const float *row, int64_t d, int reset)
+{
+    for (int64_t k = 0; k < d; ++k)
+        sum[k] = (reset ? 0.0 : sum[k]) + (double)row[k];
+}
+
+/* centroid of the seed and the first t picks of a prefix (invalid picks skipped) */
+static void prefix_centroid(const float *C, int64_t n, int64_t d, int32_t seed,
+                            const int32_t *picks, int t, double *cent)
+{
+    int64_t cnt = 0;
+    for (int64_t k = 0; k < d; ++k)
+        cent[k] = 0.0;
+#if ORC_MUTANT != 15
+    if (seed >= 0 && seed < n) {
+        acc_row(cent, C + (int64_t)seed * d, d, 0);
+        ++cnt;
+    }
+#endif
+    for (int i = 0; i < t; ++i) {
+        const int32_t p = picks[i];
+        if (p < 0 || p >= n)
+            continue;
+#if ORC_MUTANT == 16
+        acc_row(cent, C + (int64_t)p * d, d, 1);
+        cnt = 1;
+#else
+        acc_row(cent, C + (int64_t)p * d, d, 0);
+        ++cnt;
+#endif
+    }
+    if (cnt > 0)
+        for (int64_t k = 0; k < d; ++k)
+            cent[k] /= (double)cnt;
+}
+
+/* nseq x T picks and cosines (to the centroid at that step) of the centroid run */
+void orc_div_run_centroid(const float *C, int64_t n, int64_t d, int64_t nseq, int T,
+                          const int32_t *seeds, int32_t *picks, double *values,
+                          uint32_t *mask_scratch, double *cent)
+{
+    const int64_t W = (n + 31) / 32;
+    for (int64_t s = 0; s < nseq; ++s) {
+        memset(mask_scratch, 0, (size_t)W * sizeof(uint32_t));
+        const int32_t seed = seeds[s];
+        if (seed >= 0 && seed < n)
+            mask_scratch[seed >> 5] |= 1u << (seed & 31);
+        int32_t *ps = picks + s * T;
+        for (int t = 0; t < T; ++t) {
+            run_best r;
+            rb_init(&r);
+            prefix_centroid(C, n, d, seed, ps, t, cent);
+            if (seed >= 0 && seed < n) {
+                for (int64_t j = 0; j < n; ++j) {
+                    if (is_masked(mask_scratch, j))
+                        continue;
+                    const double v = cosine_ref(C + j * d, cent, d);
+                    rb_offer(&r, order_key(v, ORC_COS_MIN), v, j);
+                }
+            }
+            ps[t] = r.idx;
+            values[s * T + t] = r.value;
+            if (r.idx >= 0)
+                mask_scratch[r.idx >> 5] |= 1u << (r.idx & 31);
+        }
+    }
+}
+
+/*
+ * Replay of a recorded centroid run: as orc_div_replay, with the reference of
+ * step t the centroid of the recorded prefix (seed and recorded picks before
+ * t).  Outputs per (sequence, step): the exact best index, its cosine, the
+ * top-two gap, the recorded pick's cosine and whether that pick was legal.
+ */
+void orc_div_replay_centroid(const float *C, int64_t n, int64_t d, int64_t nseq, int T,
+                             const int32_t *seeds, const int32_t *picks, int32_t *bidx,
+                             double *best_value, double *gap, double *pick_value,
+                             int32_t *pick_ok, uint32_t *seen_scratch, double *cent)
+{
+    const int64_t W = (n + 31) / 32;
+    for (int64_t s = 0; s < nseq; ++s) {
+        memset(seen_scratch, 0, (size_t)W * sizeof(uint32_t));
+        const int32_t seed = seeds[s];
+        const int seed_ok = seed >= 0 && seed < n;
+        if (seed_ok)
+            seen_scratch[seed >> 5] |= 1u << (seed & 31);
+        const int32_t *ps = picks + s * T;
+        for (int t = 0; t < T; ++t) {
+            const int64_t o = s * T + t;
+            run_best r;
+            rb_init(&r);
+            prefix_centroid(C, n, d, seed, ps, t, cent);
+            if (seed_ok) {
+                for (int64_t j = 0; j < n; ++j) {
+                    if (is_masked(seen_scratch, j))
+                        continue;
+                    const double v = cosine_ref(C + j * d, cent, d);
+                    rb_offer(&r, order_key(v, ORC_COS_MIN), v, j);
+                }
+            }
+            rb_emit(&r, bidx + o, best_value + o, gap + o);
+            const int32_t p = ps[t];
+            const int ok = seed_ok && p >= 0 && p < n &&
+                           !((seen_scratch[p >> 5] >> (p & 31)) & 1u);
+            pick_ok[o] = ok;
+            pick_value[o] = ok ? cosine_ref(C + (int64_t)p * d, cent, d) : NAN;
+            if (p >= 0 && p < n)
+                seen_scratch[p >> 5] |= 1u << (p & 31);
+        }
+    }
+}

@@ -68,6 +68,24 @@ def diversity_walk():
     return out
 
 
+def diversity_centroid():
+    """The centroid-reference walk; vectors given by their angle in degrees."""
+    out = dict(angles=[])
+    for line in _lines("diversity_centroid.txt"):
+        key, *rest = line.split()
+        if key == "angle":
+            out["angles"].append(float(rest[0]))
+        elif key == "seed":
+            out["seed"] = int(rest[0])
+        elif key == "expect_picks":
+            out["picks"] = [int(x) for x in rest]
+        elif key == "expect_values":
+            out["values"] = [_num(x) for x in rest]
+    a = np.deg2rad(np.array(out["angles"]))
+    out["C"] = np.stack([np.cos(a), np.sin(a)], axis=1).astype(np.float32)
+    return out
+
+
 def csr_cases():
     ct, rows = [], []
     for line in _lines("csr_cases.txt"):

@@ -24,9 +24,9 @@ from scipy.spatial.distance import cdist
 
 import oracle
 import synth
-from goldens import csr_cases, diversity_walk, hand_cases
+from goldens import csr_cases, diversity_centroid, diversity_walk, hand_cases
 
-MUTANTS = list(range(1, 15))
+MUTANTS = list(range(1, 17))
 
 
 def _close(a, b, rel=1e-12, abs_=1e-12):
@@ -398,11 +398,75 @@ def pin_qe(m=0):
     return bad
 
 
+# ---- centroid-reference diversity -------------------------------------------
+# Pinned against: the hand-worked plane walk (tests/golden/diversity_centroid.txt);
+# the first step equals the last-pick step (the centroid of one row is that
+# row); the replay of the oracle's own run accepts every pick; relabelling
+# the table's rows relabels the picks; scaling every row by a positive
+# constant changes no pick (cosines are scale-free).
+
+def pin_centroid_walk(m=0):
+    w = diversity_centroid()
+    picks, vals = oracle.div_run_centroid(w["C"], np.array([w["seed"]]), len(w["picks"]),
+                                          mutant=m)
+    bad = []
+    if list(picks[0]) != w["picks"]:
+        bad.append(f"centroid walk picks {list(picks[0])}")
+    for v, e in zip(vals[0], w["values"]):
+        if not _close(v, e, 1e-6, 1e-6):
+            bad.append(f"centroid walk value {v} != {e}")
+    return bad
+
+
+def _div_table(n, d, key):
+    _, C = synth.dense_case(1, n, d, "unit", key=key)
+    (r,) = synth.rng_children(9000 + key, 1)
+    return C, r.choice(n, 6, replace=False).astype(np.int32)
+
+
+def pin_centroid_first_step(m=0):
+    C, seeds = _div_table(90, 12, 80)
+    a, va = oracle.div_run_centroid(C, seeds, 1, mutant=m)
+    b, vb = oracle.div_run(C, seeds, 1, mutant=m)
+    ok = np.array_equal(a, b) and np.allclose(va, vb, rtol=1e-12, atol=1e-12)
+    return [] if ok else ["centroid step 1 differs from the last-pick step"]
+
+
+def pin_centroid_replay(m=0):
+    C, seeds = _div_table(70, 9, 81)
+    picks, vals = oracle.div_run_centroid(C, seeds, 30, mutant=m)
+    rep = oracle.div_replay_centroid(C, seeds, picks, mutant=m)
+    ok = (rep["pick_ok"].all() and np.array_equal(rep["bidx"], picks)
+          and np.allclose(rep["pick_value"], vals, rtol=1e-12, atol=1e-12))
+    bad = [] if ok else ["centroid replay rejects the oracle's own run"]
+    seen = [set([s]) | set(p) for s, p in zip(seeds, picks)]
+    if any(len(sv) != 31 for sv in seen):
+        bad.append("centroid run repeats a pick or the seed")
+    return bad
+
+
+def pin_centroid_relabel_and_scale(m=0):
+    C, seeds = _div_table(60, 7, 82)
+    picks, _ = oracle.div_run_centroid(C, seeds, 20, mutant=m)
+    (r,) = synth.rng_children(9100, 1)
+    perm = r.permutation(C.shape[0])            # new row i = old row perm[i]
+    inv = np.argsort(perm)
+    p2, _ = oracle.div_run_centroid(C[perm], inv[seeds].astype(np.int32), 20, mutant=m)
+    p3, _ = oracle.div_run_centroid(C * np.float32(4.0), seeds, 20, mutant=m)
+    bad = []
+    if not np.array_equal(perm[p2], picks):
+        bad.append("centroid run not relabelling-invariant")
+    if not np.array_equal(p3, picks):
+        bad.append("centroid run depends on the rows' scale")
+    return bad
+
+
 PINS = [pin_hand_cases, pin_csr_cases, pin_walk, pin_library, pin_sklearn, pin_closed_forms,
         pin_split_invariance, pin_permutation, pin_translation, pin_duplicates,
         pin_csr_vs_dense, pin_replay, pin_gram, pin_sqnorms, pin_som_group_mean,
         pin_som_single_input, pin_som_scipy, pin_som_global_mean, pin_som_symmetry,
-        pin_som_hand, pin_som_csr_duplicates, pin_qe]
+        pin_som_hand, pin_som_csr_duplicates, pin_qe, pin_centroid_walk,
+        pin_centroid_first_step, pin_centroid_replay, pin_centroid_relabel_and_scale]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
