@@ -41,6 +41,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_diversity_step_ref", "vs_diversity_accumulate",
            "vs_diversity_gram", "vs_diversity_step_gram",
            "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
            "vs_som_epoch_workspace", "vs_som_epoch", "vs_som_epoch_csr_workspace",
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_step_workspace.argtypes = [I64, I32, I64]
     L.vs_diversity_step_workspace.restype = SZ
     L.vs_diversity_step.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
+    L.vs_diversity_step_ref.argtypes = [P, I64, I32, P, P, I64, P, P, P, SZ, P]
+    L.vs_diversity_accumulate.argtypes = [P, I64, I32, P, P, I64, P]
     L.vs_diversity_gram.argtypes = [P, I64, I32, P, I64, P]
     L.vs_diversity_step_gram.argtypes = [P, I64, I64, P, P, I64, P, P, P]
     F = ctypes.c_float
@@ -118,7 +121,8 @@ def lib() -> ctypes.CDLL:
                  "vs_csr_block_codebook",
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
-                 "vs_diversity_step_gram", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
+                 "vs_diversity_step_gram", "vs_diversity_step_ref", "vs_diversity_accumulate",
+                 "vs_som_update", "vs_som_update_csr", "vs_som_qe",
                  "vs_som_epoch", "vs_som_epoch_csr",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
@@ -418,6 +422,51 @@ def vs_diversity_step(C, last_pick, mask_bits, idx_out=None, score_out=None, wor
                                  ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_diversity_step")
     return idx_out, score_out
+
+
+def vs_diversity_step_ref(C, Q, mask_bits, idx_out=None, score_out=None, workspace=None,
+                          want_score: bool = True):
+    """One diversity step against explicit reference rows Q (nseq x d)."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    _dev(Q, "Q", torch.float32, 2)
+    if mask_bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask_bits must be int32 or uint32 words")
+    _dev(mask_bits, "mask_bits", mask_bits.dtype, 2)
+    n, d = C.shape
+    nseq = Q.shape[0]
+    if Q.shape[1] != d or tuple(mask_bits.shape) != (nseq, mask_words(n)):
+        raise ValueError("Q or mask_bits disagree with C")
+    dev = C.device
+    if idx_out is None:
+        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_step_ref(_ptr(C), n, d, _ptr(Q), _ptr(mask_bits), nseq,
+                                     _ptr(idx_out), _ptr(score_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_diversity_step_ref")
+    return idx_out, score_out
+
+
+def vs_diversity_accumulate(C, pick, Q):
+    """Q[s] += C[pick[s]] where the pick is valid (in place)."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    _dev(pick, "pick", torch.int32, 1)
+    _dev(Q, "Q", torch.float32, 2)
+    n, d = C.shape
+    if Q.shape != (pick.numel(), d):
+        raise ValueError("Q must be (len(pick), d)")
+    with torch.cuda.device(C.device):
+        rc = L.vs_diversity_accumulate(_ptr(C), n, d, _ptr(pick), _ptr(Q), pick.numel(),
+                                       _stream(C.device))
+    _check(rc, "vs_diversity_accumulate")
+    return Q
 
 
 def vs_diversity_gram(C, out=None):

@@ -20,7 +20,7 @@ ROOF_LIB = os.path.join(HERE, "libvs_roofs.so")  # measurement kernels, not the 
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "prep.hip", "bmu_mfma.hip", "bmu_qreg.hip", "bmu_q16.hip", "bmu_csr.hip", "finalize.hip",
-           "div_gram.hip", "som.hip"]
+           "div_gram.hip", "div_ref.hip", "som.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -216,8 +216,8 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     a.d = d;
     switch (dense_kernel(d, C, Q)) {
     case DenseKernel::QREG: VS_TRY_HIP(vs::launch_dense_qreg(a, metric, st, n_cu)); break;
-    case DenseKernel::Q16: VS_TRY_HIP(vs::launch_dense_q16(a, metric, false, st, n_cu)); break;
-    default: VS_TRY_HIP(vs::launch_dense(a, metric, false, st, n_cu)); break;
+    case DenseKernel::Q16: VS_TRY_HIP(vs::launch_dense_q16(a, metric, vs::kQRows, st, n_cu)); break;
+    default: VS_TRY_HIP(vs::launch_dense(a, metric, vs::kQRows, st, n_cu)); break;
     }
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
@@ -454,13 +454,63 @@ VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t
     a.nc = n;
     a.d = d;
     a.mask_words = W;
-    if (div_use_q16(d, C)) VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, true, st, n_cu));
-    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, true, st, n_cu));
+    if (div_use_q16(d, C))
+        VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, vs::kQGatherMasked, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, vs::kQGatherMasked, st, n_cu));
     VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
     return VS_OK;
 }
 
 // ---- diversity from a cached Gram matrix -------------------------------------
+
+VS_API int vs_diversity_step_ref(const float *C, int64_t n, int32_t d, const float *Q,
+                                 uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
+                                 float *score_out, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || d > kMaxDim || nseq < 0 || nseq > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nseq == 0) return VS_OK;
+    if (!C || !Q || !mask_bits || !idx_out || !workspace) return VS_ERR_NULL;
+    if (!al4(C) || !al4(Q) || !al4(mask_bits) || !al4(idx_out) || !al4(score_out) ||
+        !al256(workspace))
+        return VS_ERR_ALIGN;
+    if (workspace_bytes < vs_diversity_step_workspace(n, d, nseq)) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    uint64_t *keys = static_cast<uint64_t *>(workspace);
+    const int64_t W = (n + 31) / 32;
+    VS_TRY_HIP(vs::launch_fill_keys(keys, nseq, st));
+    vs::DenseArgs a{};
+    a.Q = Q;
+    a.C = C;
+    a.mask = mask_bits;
+    a.keys = keys;
+    a.nq = nseq;
+    a.nc = n;
+    a.d = d;
+    a.mask_words = W;
+    if (div_use_q16(d, C) && vs::q16_supports(d, C, Q))
+        VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, vs::kQRowsMasked, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, vs::kQRowsMasked, st, n_cu));
+    VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
+    return VS_OK;
+}
+
+VS_API int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick,
+                                   float *Q, int64_t nseq, void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || d > kMaxDim || nseq < 0 || nseq > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nseq == 0) return VS_OK;
+    if (!C || !pick || !Q) return VS_ERR_NULL;
+    if (!al4(C) || !al4(pick) || !al4(Q)) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_div_accumulate(C, n, d, pick, Q, nseq,
+                                         reinterpret_cast<hipStream_t>(stream)));
+    return VS_OK;
+}
 
 VS_API int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ldg,
                              void *stream) {

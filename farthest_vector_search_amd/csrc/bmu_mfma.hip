@@ -75,15 +75,16 @@ __device__ __forceinline__ f32x4 load4(const float *p, int32_t k, int32_t d) {
     return v;
 }
 
-template <int M, bool GATHER, bool VEC, int WQ, int WC>
+template <int M, int QM, bool VEC, int WQ, int WC>
 __global__ __launch_bounds__(64 * WQ * WC) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_mfma(const DenseArgs a) {
+    constexpr bool GATHER = QM == kQGatherMasked;
     constexpr int NT = 64 * WQ * WC;
     constexpr int BQ = 64 * WQ, BC = 64 * WC;
     constexpr int RPP = NT / 8;  // rows per loader pass
     constexpr int AP = BC / RPP, BP = BQ / RPP;
     static_assert(BC % RPP == 0 && BQ % RPP == 0, "tile/loader mismatch");
-    constexpr bool MASKED = GATHER;  // the gathered form is the diversity step
+    constexpr bool MASKED = QM != kQRows;  // the diversity step, gathered or explicit
 
     __shared__ __attribute__((aligned(16))) float sA[2][BC * kBK];
     __shared__ __attribute__((aligned(16))) float sB[2][BQ * kBK];
@@ -278,15 +279,16 @@ void k_bmu_mfma(const DenseArgs a) {
     }
 }
 
-template <int M, bool GATHER>
+template <int M, int QM>
 static void dispatch_vec(const DenseArgs &a, bool vec, dim3 grid, dim3 block, hipStream_t st) {
     if (vec)
-        hipLaunchKernelGGL((k_bmu_mfma<M, GATHER, true, 2, 2>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_bmu_mfma<M, QM, true, 2, 2>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_bmu_mfma<M, GATHER, false, 2, 2>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_bmu_mfma<M, QM, false, 2, 2>), grid, block, 0, st, a);
 }
 
-hipError_t launch_dense(const DenseArgs &a0, int metric, bool gather, hipStream_t st, int n_cu) {
+hipError_t launch_dense(const DenseArgs &a0, int metric, int qmode, hipStream_t st, int n_cu) {
+    const bool gather = qmode == kQGatherMasked;
     constexpr int BQ = 128, BC = 128, OCC = 2;
     DenseArgs a = a0;
     const int64_t nqt = (a.nq + BQ - 1) / BQ;
@@ -297,15 +299,18 @@ hipError_t launch_dense(const DenseArgs &a0, int metric, bool gather, hipStream_
     const bool vec = (a.d % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) &&
                      (gather || (reinterpret_cast<uintptr_t>(a.Q) & 15) == 0);
     const dim3 grid((unsigned)a.grid), block(256);
-    timing_before(st, gather ? "k_bmu_mfma<COS_MIN,gather>" : "k_bmu_mfma");
+    timing_before(st, gather ? "k_bmu_mfma<COS_MIN,gather>"
+                             : (qmode == kQRowsMasked ? "k_bmu_mfma<COS_MIN,ref>" : "k_bmu_mfma"));
     if (gather) {
-        dispatch_vec<COS_MIN, true>(a, vec, grid, block, st);
+        dispatch_vec<COS_MIN, kQGatherMasked>(a, vec, grid, block, st);
+    } else if (qmode == kQRowsMasked) {
+        dispatch_vec<COS_MIN, kQRowsMasked>(a, vec, grid, block, st);
     } else {
         switch (metric) {
-        case L2SQ_MIN: dispatch_vec<L2SQ_MIN, false>(a, vec, grid, block, st); break;
-        case L2SQ_MAX: dispatch_vec<L2SQ_MAX, false>(a, vec, grid, block, st); break;
-        case COS_MAX: dispatch_vec<COS_MAX, false>(a, vec, grid, block, st); break;
-        default: dispatch_vec<COS_MIN, false>(a, vec, grid, block, st); break;
+        case L2SQ_MIN: dispatch_vec<L2SQ_MIN, kQRows>(a, vec, grid, block, st); break;
+        case L2SQ_MAX: dispatch_vec<L2SQ_MAX, kQRows>(a, vec, grid, block, st); break;
+        case COS_MAX: dispatch_vec<COS_MAX, kQRows>(a, vec, grid, block, st); break;
+        default: dispatch_vec<COS_MIN, kQRows>(a, vec, grid, block, st); break;
         }
     }
     const hipError_t err = hipGetLastError();

@@ -72,15 +72,16 @@ __device__ __forceinline__ int slab_at(int row, int piece) {
 }  // namespace
 
 // MODE: kSearch (arg-reduce over Q's rows), kDiversity (queries gathered
-// as C[pick], masked), kStore (write every dot product to S instead).
-enum : int { kSearch = 0, kDiversity = 1, kStore = 2 };
+// as C[pick], masked), kStore (write every dot product to S instead),
+// kRef (Q's rows, masked: a diversity step against explicit references).
+enum : int { kSearch = 0, kDiversity = 1, kStore = 2, kRef = 3 };
 
 template <int M, int MODE, int NSLAB>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_q16(const DenseArgs a) {
     constexpr int NCH = NSLAB * kCPS;
     constexpr bool GATHER = MODE == kDiversity;
-    constexpr bool MASKED = MODE == kDiversity;
+    constexpr bool MASKED = MODE == kDiversity || MODE == kRef;
     constexpr bool STORE = MODE == kStore;
 
     __shared__ __attribute__((aligned(16))) float sA[3][kBC * kBK];
@@ -411,8 +412,9 @@ bool q16_supports(int32_t d, const float *C, const float *Q) {
     return d >= 1 && d <= kMaxD && d % 4 == 0 && al;
 }
 
-hipError_t launch_dense_q16(const DenseArgs &a0, int metric, bool gather, hipStream_t st,
+hipError_t launch_dense_q16(const DenseArgs &a0, int metric, int qmode, hipStream_t st,
                             int n_cu) {
+    const bool gather = qmode == kQGatherMasked;
     DenseArgs a = a0;
     const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
     a.n_ctiles = (a.nc + kBC - 1) / kBC;
@@ -425,9 +427,12 @@ hipError_t launch_dense_q16(const DenseArgs &a0, int metric, bool gather, hipStr
     // query set eight times, instead of the whole candidate set eight times.
     a.split = (a.grid % 8 == 0 && a.n_ctiles >= 8 && a.nq < a.nc) ? 8 : 1;
     const dim3 grid((unsigned)a.grid);
-    timing_before(st, gather ? "k_bmu_q16<COS_MIN,gather>" : "k_bmu_q16");
+    timing_before(st, gather ? "k_bmu_q16<COS_MIN,gather>"
+                             : (qmode == kQRowsMasked ? "k_bmu_q16<COS_MIN,ref>" : "k_bmu_q16"));
     if (gather) {
         dispatch_slabs<COS_MIN, kDiversity>(a, grid, st);
+    } else if (qmode == kQRowsMasked) {
+        dispatch_slabs<COS_MIN, kRef>(a, grid, st);
     } else {
         switch (metric) {
         case L2SQ_MIN: dispatch_slabs<L2SQ_MIN, kSearch>(a, grid, st); break;

@@ -16,6 +16,9 @@
 // index among equal values), then the wave merges (value, index) pairs
 // lexicographically.  -0 and +0 compare equal and the score is reported
 // with the sign folded, as the packed-key path does; NaN is never picked.
+// A lane whose four columns are all masked does not load them, so as a run
+// fills its masks (a full-length run ends with every bit set) the HBM bytes
+// of a step fall with the number of candidates left.
 #include "vs_internal.h"
 
 namespace vs {
@@ -45,15 +48,18 @@ __global__ __launch_bounds__(256) void k_div_gram_step(const float *__restrict__
     float best = __builtin_inff();
     int64_t bidx = -1;
     for (int64_t j0 = 4 * (int64_t)lane; j0 < n; j0 += 256) {
+        // j0 % 32 <= 28: the four columns' bits sit in one mask word
+        const int64_t left = n - j0;
+        uint32_t live4 = ~(mrow[j0 >> 5] >> (j0 & 31)) & 0xFu;
+        if (left < 4) live4 &= (1u << left) - 1u;
+        if (live4 == 0) continue;
         // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
         // row's padded storage even past n
         const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
-        const uint32_t mw = mrow[j0 >> 5] >> (j0 & 31);  // j0 % 32 <= 28: 4 bits in one word
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = v[e];
-            const bool live = j0 + e < n && !((mw >> e) & 1u);
-            if (live && x < best) {
+            if (((live4 >> e) & 1u) && x < best) {
                 best = x;
                 bidx = j0 + e;
             }

@@ -138,15 +138,20 @@ hipError_t launch_col_sqnorms_f16(const uint16_t *X, int64_t cols, int32_t d, fl
                                   hipStream_t st);
 hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,
                                   int64_t nnz, float *out, hipStream_t st);
-hipError_t launch_dense(const DenseArgs &a, int metric, bool gather, hipStream_t st,
-                        int n_cu);
+// Where a dense scan takes its queries from: the rows of a.Q; rows
+// a.C[a.pick[i]] with the mask (the diversity step); the rows of a.Q with
+// the mask (a step against explicit reference rows).  The masked forms rank
+// by COS_MIN.
+enum QueryMode : int { kQRows = 0, kQGatherMasked = 1, kQRowsMasked = 2 };
+
+hipError_t launch_dense(const DenseArgs &a, int metric, int qmode, hipStream_t st, int n_cu);
 // Queries-in-registers variant of the dense scan (d <= 256, no gather).
 bool qreg_supports(int32_t d);
 hipError_t launch_dense_qreg(const DenseArgs &a, int metric, hipStream_t st, int n_cu);
 // 16-queries-per-wave variant (d <= 768, d % 4 == 0, 16-byte aligned rows);
 // also runs the gathered, masked diversity step.
 bool q16_supports(int32_t d, const float *C, const float *Q);
-hipError_t launch_dense_q16(const DenseArgs &a, int metric, bool gather, hipStream_t st,
+hipError_t launch_dense_q16(const DenseArgs &a, int metric, int qmode, hipStream_t st,
                             int n_cu);
 // every dot product Q[q] . C[c] into a.S (same arithmetic as the scans)
 hipError_t launch_dense_q16_store(const DenseArgs &a, hipStream_t st, int n_cu);
@@ -154,6 +159,9 @@ hipError_t launch_dense_qreg_store(const DenseArgs &a, hipStream_t st, int n_cu)
 // per-row best of a score block into packed keys (the unfused comparator)
 hipError_t launch_row_argbest(const float *S, int64_t nq, int64_t nc, int64_t ld_s,
                               const float *cn, uint64_t *keys, int metric, hipStream_t st);
+// Q[s] += C[pick[s]] for every sequence whose pick is in [0, n)
+hipError_t launch_div_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick,
+                                 float *Q, int64_t nseq, hipStream_t st);
 // one diversity step from a cached score block G (G[r * ldg + j] = C[r] . C[j])
 hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
                                 uint32_t *mask, int64_t nseq, int32_t *idx_out,

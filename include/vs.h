@@ -205,6 +205,31 @@ int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The diversity step against explicit reference rows [DIV "Current
+ * Behavior"; "FP16 storage (compounding optimization)" ranks candidates
+ * against the sequence's centroid].
+ *   vs_diversity_step_ref    as vs_diversity_step, with sequence s ranked
+ *                            against Q[s] (nseq x d, float32, row-major)
+ *                            instead of C[last_pick[s]]: the unmasked row j
+ *                            of C with the smallest C[j] . Q[s] (lowest index
+ *                            on ties) is picked and its bit set.  C's rows
+ *                            unit-norm: that is the smallest cosine to Q[s],
+ *                            for any positive scale of Q[s].  score_out =
+ *                            C[pick] . Q[s].  Workspace as vs_diversity_step.
+ *   vs_diversity_accumulate  Q[s] += C[pick[s]] for every s whose pick is in
+ *                            [0, n) (others unchanged): with Q[s] started at
+ *                            the seed's row it holds the sum of the sequence
+ *                            so far, i.e. its centroid times a positive count,
+ *                            so a chain step_ref / accumulate is the centroid
+ *                            reading.  No workspace.
+ */
+int vs_diversity_step_ref(const float *C, int64_t n, int32_t d, const float *Q,
+                          uint32_t *mask_bits, int64_t nseq, int32_t *idx_out, float *score_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick, float *Q,
+                            int64_t nseq, void *stream);
+
+/*
  * The diversity step from a cached Gram matrix [DIV "Current Behavior"; the
  * reference of a step is the sequence's last pick, so every score a run can
  * need is an entry of G = C C^T].
