@@ -58,6 +58,12 @@ def parse():
                     help="diversity workload: 'step' runs the MFMA scan every step, 'gram' "
                          "builds the table's Gram matrix once per run and scans one row of it "
                          "per sequence and step")
+    ap.add_argument("--div-ref", choices=["last", "centroid"], default="last",
+                    help="diversity reference: the last pick, or the centroid of the "
+                         "sequence so far (per-step scan against explicit reference rows)")
+    ap.add_argument("--div-steps", default=None,
+                    help="diversity steps per run: a number, or 'full' (every row of the "
+                         "table, n - 1 picks); default the workload's 64")
     ap.add_argument("--csr-storage", choices=["f32", "f16"], default="f32",
                     help="sparse workload: codebook storage type ('f16': the 128-neuron "
                          "blocked fp16 copy, fp32 arithmetic)")
@@ -157,6 +163,10 @@ def setup(k, torch, vs, a):
         return w, step, pairs, flops, 1, cfg
     if w["kind"] == "diversity":
         n, d, nseq, steps = w["n"], w["d"], w["nseq"], w["steps"]
+        if a.div_steps is not None:
+            steps = n - 1 if a.div_steps == "full" else int(a.div_steps)
+        if a.div_ref == "centroid" and a.div_mode != "step":
+            raise SystemExit("--div-ref centroid runs the per-step scan (--div-mode step)")
         C = torch.from_numpy(w["C"]).to(dev)
         seeds = torch.from_numpy(w["seeds"]).to(dev)
         W = (n + 31) // 32
@@ -182,9 +192,24 @@ def setup(k, torch, vs, a):
                     vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t],
                                               want_score=False)
                     last = picks[t]
-            # algorithmic bytes of one scan: a row of n fp32 per sequence, its
-            # mask row read and written, the pick read and written
-            w["scan_bytes"] = nseq * (4 * n + 8 * W + 8)
+            # algorithmic bytes of one scan, averaged over the run: the live
+            # (unmasked) entries of one Gram row per sequence -- n - 1 - t at
+            # step t -- its mask row read and written, the pick read and written
+            live = sum(max(n - 1 - t, 0) for t in range(steps)) / steps
+            w["scan_bytes"] = nseq * (4 * live + 8 * W + 8)
+        elif a.div_ref == "centroid":
+            # the reference of each sequence is the running sum of its rows
+            # (the centroid times a positive count): start at the seed's row
+            Q = torch.empty((nseq, d), dtype=torch.float32, device=dev)
+
+            def step():
+                mask.copy_(mask0)
+                Q.zero_()
+                vs.vs_diversity_accumulate(C, seeds, Q)
+                for t in range(steps):
+                    vs.vs_diversity_step_ref(C, Q, mask, idx_out=picks[t], workspace=ws,
+                                             want_score=False)
+                    vs.vs_diversity_accumulate(C, picks[t], Q)
         else:
             def step():
                 mask.copy_(mask0)
@@ -196,7 +221,7 @@ def setup(k, torch, vs, a):
         pairs = nseq * n * steps
         flops = 2.0 * d * pairs
         cfg = dict(workload=w["name"], n=n, d=d, nseq=nseq, steps_per_run=steps,
-                   metric="cos_min_masked", mode=a.div_mode)
+                   metric="cos_min_masked", mode=a.div_mode, reference=a.div_ref)
         return w, step, pairs, flops, steps, cfg
     # sparse
     indptr = torch.from_numpy(w["indptr"]).to(dev)
@@ -639,7 +664,10 @@ def main():
     roof["launches_per_step"] = launches // a.steps
     roof["kernel"] = kt.name
     roof["kernel_ms"] = round(kernel_ms, 5)
-    roof["traffic"] = (None if "mode" in cfg and cfg["mode"] in ("gram", "unfused") else
+    # counters were taken for the default forms only
+    other_form = (cfg.get("mode") in ("gram", "unfused") or cfg.get("reference") == "centroid"
+                  or cfg.get("steps_per_run", w.get("steps")) != w.get("steps"))
+    roof["traffic"] = (None if other_form else
                        load_traffic(a.traffic_json, DOMINANT[a.workload],
                                     cfg["workload"].replace("+som_epoch", "")))
     out = {

@@ -47,10 +47,19 @@ __global__ __launch_bounds__(256) void k_div_gram_step(const float *__restrict__
     const uint32_t *mrow = mask + s * W;
     float best = __builtin_inff();
     int64_t bidx = -1;
-    for (int64_t j0 = 4 * (int64_t)lane; j0 < n; j0 += 256) {
+    // the mask word of the next segment is fetched one iteration ahead, so
+    // a segment's row load never waits for its own mask load
+    // (unconditionally, at a clamped in-range column, so that the compiler's
+    // wait before the row load does not also wait for it)
+    int64_t j0 = 4 * (int64_t)lane;
+    uint32_t mw = mrow[(j0 < n ? j0 : n - 1) >> 5];
+    for (; j0 < n; j0 += 256) {
+        const int64_t jn = j0 + 256;
+        const uint32_t mw_next = mrow[(jn < n ? jn : n - 1) >> 5];
         // j0 % 32 <= 28: the four columns' bits sit in one mask word
         const int64_t left = n - j0;
-        uint32_t live4 = ~(mrow[j0 >> 5] >> (j0 & 31)) & 0xFu;
+        uint32_t live4 = ~(mw >> (j0 & 31)) & 0xFu;
+        mw = mw_next;
         if (left < 4) live4 &= (1u << left) - 1u;
         if (live4 == 0) continue;
         // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
