@@ -10,10 +10,10 @@
 // arg-min over one row of G per sequence: an HBM-bound read of n floats
 // instead of a d-long dot product per candidate.
 //
-// One wave per sequence: lanes read the reference's row four floats at a
-// time (lane l: columns 256 i + 4 l .. + 3, ascending), skip masked and
-// padded columns, keep the lowest value with strict "<" (so the lowest
-// index among equal values), then the wave merges (value, index) pairs
+// Lanes read the reference's row four floats at a time (lane l of a wave:
+// columns 4 l .. 4 l + 3 of each 256-column segment the wave owns), skip
+// masked and padded columns, keep the lowest value with strict "<" (so the
+// lowest index among equal values), then (value, index) pairs are merged
 // lexicographically.  -0 and +0 compare equal and the score is reported
 // with the sign folded, as the packed-key path does; NaN is never picked.
 // A lane whose four columns are all masked does not load them, so as a run
@@ -25,73 +25,100 @@ namespace vs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void k_div_gram_step(const float *__restrict__ G, int64_t n,
-                                                      int64_t ldg,
-                                                      const int32_t *__restrict__ pick,
-                                                      uint32_t *__restrict__ mask,
-                                                      int64_t nseq, int32_t *__restrict__ idx_out,
-                                                      float *__restrict__ score_out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= nseq) return;
+// One workgroup of kWPS waves per sequence: wave w scans the 256-column
+// segments w, w + kWPS, ... (so a step has kWPS x nseq waves in flight to
+// hide the row loads' latency), then the waves' (value, index) pairs are
+// merged through LDS; the order of a lexicographic minimum is immaterial, so
+// the pick equals the one-wave scan's.
+constexpr int kWPS = 4;
+
+__global__ __launch_bounds__(64 * kWPS) void k_div_gram_step(const float *__restrict__ G,
+                                                            int64_t n, int64_t ldg,
+                                                            const int32_t *__restrict__ pick,
+                                                            uint32_t *__restrict__ mask,
+                                                            int64_t nseq,
+                                                            int32_t *__restrict__ idx_out,
+                                                            float *__restrict__ score_out) {
+    __shared__ float s_best[kWPS];
+    __shared__ int64_t s_idx[kWPS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t W = (n + 31) / 32;
-    const int64_t r = pick[s];
-    if (r < 0 || r >= n) {  // no reference: no pick, mask unchanged
-        if (lane == 0) {
-            idx_out[s] = -1;
-            if (score_out) score_out[s] = __builtin_nanf("");
+    // sequences s = blockIdx.x, + gridDim.x, ...: every branch below is
+    // uniform over the workgroup, so all its waves meet every barrier
+    for (int64_t s = blockIdx.x; s < nseq; s += gridDim.x) {
+        const int64_t r = pick[s];
+        if (r < 0 || r >= n) {  // no reference: no pick, mask unchanged
+            if (threadIdx.x == 0) {
+                idx_out[s] = -1;
+                if (score_out) score_out[s] = __builtin_nanf("");
+            }
+            continue;
         }
-        return;
-    }
-    const float *row = G + r * ldg;
-    const uint32_t *mrow = mask + s * W;
-    float best = __builtin_inff();
-    int64_t bidx = -1;
-    // the mask word of the next segment is fetched one iteration ahead, so
-    // a segment's row load never waits for its own mask load
-    // (unconditionally, at a clamped in-range column, so that the compiler's
-    // wait before the row load does not also wait for it)
-    int64_t j0 = 4 * (int64_t)lane;
-    uint32_t mw = mrow[(j0 < n ? j0 : n - 1) >> 5];
-    for (; j0 < n; j0 += 256) {
-        const int64_t jn = j0 + 256;
-        const uint32_t mw_next = mrow[(jn < n ? jn : n - 1) >> 5];
-        // j0 % 32 <= 28: the four columns' bits sit in one mask word
-        const int64_t left = n - j0;
-        uint32_t live4 = ~(mw >> (j0 & 31)) & 0xFu;
-        mw = mw_next;
-        if (left < 4) live4 &= (1u << left) - 1u;
-        if (live4 == 0) continue;
-        // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
-        // row's padded storage even past n
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x = v[e];
-            if (((live4 >> e) & 1u) && x < best) {
-                best = x;
-                bidx = j0 + e;
+        const float *row = G + r * ldg;
+        const uint32_t *mrow = mask + s * W;
+        float best = __builtin_inff();
+        int64_t bidx = -1;
+        // the mask word of the next segment is fetched one iteration ahead
+        // (unconditionally, at a clamped in-range column, so that the compiler's
+        // wait before the row load does not also wait for it): a segment's row
+        // load never waits for its own mask load
+        constexpr int64_t kStep = 256 * kWPS;
+        int64_t j0 = 256 * (int64_t)wave + 4 * (int64_t)lane;
+        uint32_t mw = mrow[(j0 < n ? j0 : n - 1) >> 5];
+        for (; j0 < n; j0 += kStep) {
+            const int64_t jn = j0 + kStep;
+            const uint32_t mw_next = mrow[(jn < n ? jn : n - 1) >> 5];
+            // j0 % 32 <= 28: the four columns' bits sit in one mask word
+            const int64_t left = n - j0;
+            uint32_t live4 = ~(mw >> (j0 & 31)) & 0xFu;
+            mw = mw_next;
+            if (left < 4) live4 &= (1u << left) - 1u;
+            if (live4 == 0) continue;
+            // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
+            // row's padded storage even past n
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = v[e];
+                if (((live4 >> e) & 1u) && x < best) {
+                    best = x;
+                    bidx = j0 + e;
+                }
             }
         }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int64_t oi = __shfl_xor(bidx, off);
-        if (oi >= 0 && (bidx < 0 || ob < best || (ob == best && oi < bidx))) {
-            best = ob;
-            bidx = oi;
+        auto better = [](float ob, int64_t oi, float b, int64_t i) {
+            return oi >= 0 && (i < 0 || ob < b || (ob == b && oi < i));
+        };
+    #pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ob = __shfl_xor(best, off);
+            const int64_t oi = __shfl_xor(bidx, off);
+            if (better(ob, oi, best, bidx)) {
+                best = ob;
+                bidx = oi;
+            }
         }
-    }
-    if (lane == 0) {
-        if (bidx < 0) {
-            idx_out[s] = -1;
-            if (score_out) score_out[s] = __builtin_nanf("");
-        } else {
-            idx_out[s] = (int32_t)bidx;
-            if (score_out) score_out[s] = best == 0.0f ? 0.0f : best;
-            mask[s * W + (bidx >> 5)] |= 1u << (bidx & 31);
+        if (lane == 0) {
+            s_best[wave] = best;
+            s_idx[wave] = bidx;
         }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kWPS; ++w)
+                if (better(s_best[w], s_idx[w], best, bidx)) {
+                    best = s_best[w];
+                    bidx = s_idx[w];
+                }
+            if (bidx < 0) {
+                idx_out[s] = -1;
+                if (score_out) score_out[s] = __builtin_nanf("");
+            } else {
+                idx_out[s] = (int32_t)bidx;
+                if (score_out) score_out[s] = best == 0.0f ? 0.0f : best;
+                mask[s * W + (bidx >> 5)] |= 1u << (bidx & 31);
+            }
+        }
+        __syncthreads();  // s_best / s_idx are rewritten by the next sequence
     }
 }
 
@@ -100,8 +127,9 @@ hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const in
                                 float *score_out, hipStream_t st) {
     if (nseq <= 0) return hipSuccess;
     timing_before(st, "k_div_gram_step");
-    hipLaunchKernelGGL(k_div_gram_step, dim3((unsigned)((nseq + 3) / 4)), dim3(256), 0, st, G, n,
-                       ldg, pick, mask, nseq, idx_out, score_out);
+    const unsigned grid = (unsigned)(nseq < (1 << 20) ? nseq : (1 << 20));
+    hipLaunchKernelGGL(k_div_gram_step, dim3(grid), dim3(64 * kWPS), 0, st, G, n, ldg, pick, mask,
+                       nseq, idx_out, score_out);
     const hipError_t err = hipGetLastError();
     timing_after(st);
     return err;
