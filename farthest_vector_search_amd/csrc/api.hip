@@ -610,7 +610,7 @@ static int som_update(vs::SomArgs &a, void *workspace, size_t workspace_bytes, v
     a.T = reinterpret_cast<float *>(ws + L.T);
     a.cnt = reinterpret_cast<int32_t *>(ws + L.cnt);
     a.den_t = reinterpret_cast<float *>(ws + L.den_t);
-    a.den = reinterpret_cast<float *>(ws + L.den);
+    a.rden = reinterpret_cast<float *>(ws + L.den);
     a.g = reinterpret_cast<float *>(ws + L.g);
     VS_TRY_HIP(vs::launch_som_update(a, reinterpret_cast<hipStream_t>(stream), n_cu));
     return VS_OK;

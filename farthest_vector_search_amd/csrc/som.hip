@@ -17,7 +17,9 @@
 //   2. a pass along the map's columns:  T(m) = sum_t g(t) S(m + t)
 //      and the same over N;
 //   3. a pass along the map's rows:     num(m) = sum_t g(t) T(m + t cols),
-//      fused with the division num / den into the codebook.
+//      fused with the division into the codebook: num * (1 / den), the
+//      reciprocal taken once per neuron by the denominator's second pass
+//      (0 where den = 0: those neurons keep their weights).
 // Both passes only sum over offsets that stay on the map (the planar edge).
 //
 // Element (neuron m, feature k) of the codebook and of the S / T buffers:
@@ -115,13 +117,13 @@ __global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
 
 // One separable pass over (neuron, feature) elements.  ALONG_X: offsets
 // m + t on the same map row; else m + t cols on the same map column.  FINAL:
-// out(m, k) = acc / den[m] written to the codebook where den[m] > 0.
+// out(m, k) = acc * rden[m] written to the codebook where rden[m] > 0.
 template <bool BLOCKED, bool ALONG_X, bool FINAL>
 __global__ __launch_bounds__(kThreads) void k_som_pass(const float *__restrict__ in,
                                                        float *__restrict__ out, int64_t nc,
                                                        int32_t d, int32_t rows, int32_t cols,
                                                        int32_t R, const float *__restrict__ g,
-                                                       const float *__restrict__ den) {
+                                                       const float *__restrict__ rden) {
     const int64_t total = BLOCKED ? ((nc + 63) >> 6) * 64 * (int64_t)d : nc * (int64_t)d;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void k_som_pass(const float *__restrict__
         for (int t = lo; t <= hi; ++t) acc = __builtin_fmaf(g[t < 0 ? -t : t],
                                                            in[at<BLOCKED>(m + t * step, k, d)], acc);
         if constexpr (FINAL) {
-            const float dv = den[m];
-            if (dv > 0.0f) out[e] = acc / dv;
+            const float rd = rden[m];
+            if (rd > 0.0f) out[e] = acc * rd;
         } else {
             out[e] = acc;
         }
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_som_pass_blk(const float *__restri
                                                            int32_t d, int32_t rows, int32_t cols,
                                                            int32_t R, int32_t per_xcd,
                                                            const float *__restrict__ g,
-                                                           const float *__restrict__ den) {
+                                                           const float *__restrict__ rden) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int32_t lin = blockIdx.x, r = lin >> 3;
     const int32_t blk = (lin & 7) * per_xcd + r % per_xcd;
@@ -169,10 +171,10 @@ __global__ __launch_bounds__(kThreads) void k_som_pass_blk(const float *__restri
     const int64_t m64 = (int64_t)blk * 64 + lane;
     if (m64 >= nc || kbase >= d) return;
     const int32_t m = (int32_t)m64;
-    float dv = 1.0f;
+    float rd = 1.0f;
     if constexpr (FINAL) {
-        dv = den[m];
-        if (!(dv > 0.0f)) return;  // no input in the window: the neuron keeps its weights
+        rd = rden[m];
+        if (!(rd > 0.0f)) return;  // no input in the window: the neuron keeps its weights
     }
     const int32_t y = m / cols, x = m - y * cols;
     const int32_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void k_som_pass_blk(const float *__restri
     float *o = out + (int64_t)blk * D64 + lane + (int64_t)kbase * 64;
 #pragma unroll
     for (int i = 0; i < kKV; ++i)
-        if (i < nk) o[i * 64] = FINAL ? acc[i] / dv : acc[i];
+        if (i < nk) o[i * 64] = FINAL ? acc[i] * rd : acc[i];
 }
 
 // Both passes in one sweep (blocked layout, window radius R <= 8 known at
@@ -230,16 +232,19 @@ struct Unroll<E, E> {
     __device__ __forceinline__ static void run(F &) {}
 };
 
-template <int R>
+template <int R, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     const float *__restrict__ S, float *__restrict__ C, int32_t d, int32_t rows, int32_t cols,
-    int32_t ntx, int64_t n_items, const float *__restrict__ g, const float *__restrict__ den) {
+    int32_t ntx, int64_t n_items, const float *__restrict__ g, const float *__restrict__ rden) {
     constexpr int P = 2 * R + 1;
     constexpr int W = 64 + 2 * R;
     __shared__ float buf[kThreads / 64][W];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + wave;
     if (item >= n_items) return;
+    // strips fastest: the waves of a workgroup sweep neighbouring strips of
+    // one feature together, so each one's halo columns are lines another has
+    // just fetched (ordering features fastest instead measured 23 % slower)
     const int32_t k = (int32_t)(item / ntx);
     const int32_t x0 = (int32_t)(item - (int64_t)k * ntx) * 64;
     const int64_t D64 = 64 * (int64_t)d;
@@ -257,9 +262,16 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     // clamped (always in-bounds) columns, so every load is unconditional
     const int32_t xcl = c_ok ? xc : cols - 1;
     const int32_t xhl = h_ok ? xh : (xh < 0 ? 0 : cols - 1);
+    // ALIGNED (cols % 64 == 0): a map row is cols / 64 whole blocks, so row y
+    // of a column sits y * (cols / 64) * 64 d floats after row 0
+    const int64_t rs = (int64_t)(cols >> 6) * D64;
     auto at_rc = [&](int32_t y, int32_t x) -> int64_t {
-        const int32_t n = y * cols + x;
-        return (int64_t)(n >> 6) * D64 + (n & 63);
+        if constexpr (ALIGNED) {
+            return (int64_t)y * rs + ((int64_t)(x >> 6) * D64 + (x & 63));
+        } else {
+            const int32_t n = y * cols + x;
+            return (int64_t)(n >> 6) * D64 + (n & 63);
+        }
     };
 
     float gw[R + 1];
@@ -270,9 +282,9 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     for (int i = 0; i < P; ++i) acc[i] = 0.0f;
 
     float vc = Sk[at_rc(0, xcl)], vh = Sk[at_rc(0, xhl)];
-    // denominator of the output row finished after the current input row
+    // 1 / denominator of the output row finished after the current input row
     // (row yy - R; none for yy < R)
-    float dnext = 0.0f;
+    float rnext = 0.0f;
     int32_t base = 0;
     // one input row; u = yy mod P is a compile-time constant
     auto step = [&](auto U) {
@@ -281,14 +293,14 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
         if (yy < rows) {
             const float cc = c_ok ? vc : 0.0f;
             const float hh = h_ok ? vh : 0.0f;
-            const float dv = dnext;
+            const float rd = rnext;
             {
                 const int32_t yn = yy + 1 < rows ? yy + 1 : rows - 1;
                 vc = Sk[at_rc(yn, xcl)];
                 vh = Sk[at_rc(yn, xhl)];
                 int32_t yd1 = yy + 1 - R;
                 yd1 = yd1 < 0 ? 0 : (yd1 >= rows ? rows - 1 : yd1);
-                dnext = den[(int64_t)yd1 * cols + xcl];
+                rnext = rden[(int64_t)yd1 * cols + xcl];
             }
             asm volatile("" ::: "memory");
             row[R + lane] = cc;
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
             }
             constexpr int qd = (u - R + 2 * P) % P;
             const int32_t yd = yy - R;
-            if (yd >= 0 && c_ok && dv > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] / dv;
+            if (yd >= 0 && c_ok && rd > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] * rd;
             acc[qd] = 0.0f;
         }
     };
@@ -319,12 +331,13 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
         float v = 0.0f;
 #pragma unroll
         for (int qq = 0; qq < P; ++qq) v = qq == q ? acc[qq] : v;
-        const float dv = den[(int64_t)y * cols + xc];
-        if (dv > 0.0f) Ck[at_rc(y, xc)] = v / dv;
+        const float rd = rden[(int64_t)y * cols + xc];
+        if (rd > 0.0f) Ck[at_rc(y, xc)] = v * rd;
     }
 }
 
-// The same two passes over the counts (one "feature", int32 input first).
+// The same two passes over the counts (one "feature", int32 input first);
+// the second writes 1 / den (0 where den = 0).
 template <bool ALONG_X, typename TIn>
 __global__ __launch_bounds__(kThreads) void k_som_den_pass(const TIn *__restrict__ in,
                                                            float *__restrict__ out, int64_t nc,
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_som_den_pass(const TIn *__restrict
         float acc = 0.0f;
         for (int t = lo; t <= hi; ++t)
             acc = __builtin_fmaf(g[t < 0 ? -t : t], (float)in[m + t * step], acc);
-        out[m] = acc;
+        out[m] = ALONG_X ? acc : (acc > 0.0f ? 1.0f / acc : 0.0f);
     }
 }
 
@@ -399,7 +412,7 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
     const dim3 gd(grid_for(nc, n_cu));
     hipLaunchKernelGGL((k_som_den_pass<true, int32_t>), gd, dim3(kThreads), 0, st, a.cnt, a.den_t,
                        nc, a.rows, a.cols, R, a.g);
-    hipLaunchKernelGGL((k_som_den_pass<false, float>), gd, dim3(kThreads), 0, st, a.den_t, a.den,
+    hipLaunchKernelGGL((k_som_den_pass<false, float>), gd, dim3(kThreads), 0, st, a.den_t, a.rden,
                        nc, a.rows, a.cols, R, a.g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const dim3 ge(grid_for(elems, n_cu));
@@ -409,8 +422,12 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
         const dim3 gw((unsigned)((items + 3) / 4));
 #define VS_SMOOTH(RR)                                                                          \
     case RR:                                                                                   \
-        hipLaunchKernelGGL((k_som_smooth_blk<RR>), gw, dim3(kThreads), 0, st, a.S, a.C, a.d,    \
-                           a.rows, a.cols, ntx, items, a.g, a.den);                            \
+        if (a.cols % 64 == 0)                                                                  \
+            hipLaunchKernelGGL((k_som_smooth_blk<RR, true>), gw, dim3(kThreads), 0, st, a.S,    \
+                               a.C, a.d, a.rows, a.cols, ntx, items, a.g, a.rden);              \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_som_smooth_blk<RR, false>), gw, dim3(kThreads), 0, st, a.S,   \
+                               a.C, a.d, a.rows, a.cols, ntx, items, a.g, a.rden);              \
         break;
         switch (R) {
             VS_SMOOTH(1) VS_SMOOTH(2) VS_SMOOTH(3) VS_SMOOTH(4)
@@ -425,12 +442,12 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
         hipLaunchKernelGGL((k_som_pass_blk<true, false>), gb, dim3(kThreads), 0, st, a.S, a.T,
                            (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, nullptr);
         hipLaunchKernelGGL((k_som_pass_blk<false, true>), gb, dim3(kThreads), 0, st, a.T, a.C,
-                           (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, a.den);
+                           (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, a.rden);
     } else {
         hipLaunchKernelGGL((k_som_pass<false, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
                            nc, a.d, a.rows, a.cols, R, a.g, nullptr);
         hipLaunchKernelGGL((k_som_pass<false, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
-                           nc, a.d, a.rows, a.cols, R, a.g, a.den);
+                           nc, a.d, a.rows, a.cols, R, a.g, a.rden);
     }
     return hipGetLastError();
 }

@@ -192,7 +192,7 @@ struct SomArgs {
     float *C;                             // codebook, updated in place
     int32_t rows, cols, R;                // map and window radius (R < max(rows, cols))
     double sigma;
-    float *S, *T, *den_t, *den, *g;       // workspace
+    float *S, *T, *den_t, *rden, *g;      // workspace (rden: 1 / denominator, 0 where none)
     int32_t *cnt;
 };
 hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu);

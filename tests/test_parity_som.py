@@ -8,7 +8,8 @@ window (the oracle's reading).
 Bar, derived from the arithmetic: the GPU sums each neuron's inputs with fp32
 atomics (at most c terms, c = the largest number of inputs sharing a BMU), then
 runs two window passes of at most 2R+1 fp32 fused multiply-adds each over the
-same magnitudes, the same for the denominator, and divides.  Every step adds at
+same magnitudes, the same for the denominator, and multiplies by the
+denominator's fp32 reciprocal (two roundings).  Every step adds at
 most a unit roundoff u = 2^-24 per term on sum_i h |x_i| / den (the oracle's
 ``mass``), so |w_gpu - w| <= 2 (c + 8R + 12) u mass (factor 2 for second-order
 terms).  Neurons with a zero denominator must keep their weights bit for bit.
