@@ -604,8 +604,9 @@ def main():
         record_traffic(a)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(queries split across GPUs with no exchange would be the way). Use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import farthest_vector_search_amd as vs
