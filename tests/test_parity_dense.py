@@ -82,6 +82,17 @@ def test_feature_dims(d, metric, kernel):
     assert_parity(Q, C, metric)
 
 
+@pytest.mark.parametrize("d", [1536, 4097, 16384])
+@pytest.mark.parametrize("metric", [0, 3])
+def test_wide_rows(d, metric):
+    """Rows far wider than the register-resident kernels take (d > 768): the
+    LDS-tiled kernel's slab loop over many slabs, a ragged last slab, and the
+    sparse workload's vocabulary width."""
+    dist = "unit" if metric == 3 else "normal"
+    Q, C = synth.dense_case(70, 260, d, dist, key=d + metric)
+    assert_parity(Q, C, metric)
+
+
 SHAPES = [(1, 1), (1, 2), (2, 13), (63, 127), (65, 128), (129, 129), (200, 1000), (1, 5000)]
 
 

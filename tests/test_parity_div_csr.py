@@ -322,6 +322,19 @@ def test_csr_shapes(metric, nc, chunk):
     csr_parity(indptr, indices, values, CT, metric)
 
 
+@pytest.mark.parametrize("metric", [0, 2])
+def test_csr_wide_vocabulary(metric):
+    """A 65,536-feature vocabulary (four times the sparse workload's): the
+    codebook slices hold 64 neurons x 65,536 features, and the blocked copy
+    agrees with the plain layout bit for bit."""
+    indptr, indices, values, CT = csr_case(60, 65536, 300, 0.002, key=640 + metric)
+    csr_parity(indptr, indices, values, CT, metric)
+    a = run_csr(indptr, indices, values, CT, metric)
+    b = run_csr_blocked(indptr, indices, values, CT, metric)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("pad", [1, 64])
 def test_csr_row_stride(pad, chunk):
     """A padded codebook row stride (ldct > nc) gives bit-identical results."""

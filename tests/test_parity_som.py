@@ -334,6 +334,25 @@ def test_workload_2_som_epoch():
 
 
 @pytest.mark.slow
+def test_workload_5_som_update_sampled():
+    """The largest map, 512 x 512 (262,144 neurons, d = 256), updated from the
+    65,536 inputs of the large dense workload with a seeded BMU assignment;
+    256 seeded neurons checked against the oracle."""
+    w = synth.workload(5)
+    rows = cols = 512
+    bmu = synth.random_indices(w["nq"], w["nc"], key=5)
+    Cg = T(w["C"])
+    vs.vs_som_update(T(w["Q"]), T(bmu), Cg, (rows, cols), SOM_SIGMA, SOM_R)
+    sel = synth.sample_queries(w["nc"], 256, key=51)
+    w_gpu = Cg.cpu().numpy()[sel]
+    ip, ix, vv = oracle.dense_as_csr(w["Q"])
+    w_o, mass, den = oracle.som_update(ip, ix, vv, w["d"], bmu, w["C"], rows, cols, SOM_SIGMA,
+                                       SOM_R, neurons=sel.astype(np.int32), threads=16)
+    bad = check_update(w_gpu, w["C"][sel], w_o, mass, den, bmu, rows, cols, SOM_R)
+    assert not bad, bad
+
+
+@pytest.mark.slow
 def test_workload_4_som_update_sampled():
     """The 256 x 256 map of the sparse workload (32,768 CSR rows, d = 16,384)
     at full size over the blocked codebook; a seeded BMU assignment; 48
