@@ -45,20 +45,6 @@ __device__ __forceinline__ int64_t at(int64_t m, int64_t k, int32_t d) {
     else return m * d + k;
 }
 
-// element e of the buffer (in storage order) -> (neuron, feature)
-template <bool BLOCKED>
-__device__ __forceinline__ void coords(int64_t e, int32_t d, int64_t &m, int64_t &k) {
-    if constexpr (BLOCKED) {
-        const int64_t blk = e / (64 * (int64_t)d);
-        const int64_t r = e - blk * 64 * (int64_t)d;
-        k = r >> 6;
-        m = blk * 64 + (r & 63);
-    } else {
-        m = e / d;
-        k = e - m * d;
-    }
-}
-
 __global__ __launch_bounds__(kThreads) void k_som_zero(float *p, int64_t n4, int32_t *cnt,
                                                        int64_t nc) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -115,34 +101,85 @@ __global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
     }
 }
 
-// One separable pass over (neuron, feature) elements.  ALONG_X: offsets
-// m + t on the same map row; else m + t cols on the same map column.  FINAL:
-// out(m, k) = acc * rden[m] written to the codebook where rden[m] > 0.
-template <bool BLOCKED, bool ALONG_X, bool FINAL>
-__global__ __launch_bounds__(kThreads) void k_som_pass(const float *__restrict__ in,
-                                                       float *__restrict__ out, int64_t nc,
-                                                       int32_t d, int32_t rows, int32_t cols,
-                                                       int32_t R, const float *__restrict__ g,
-                                                       const float *__restrict__ rden) {
-    const int64_t total = BLOCKED ? ((nc + 63) >> 6) * 64 * (int64_t)d : nc * (int64_t)d;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
-        int64_t m, k;
-        coords<BLOCKED>(e, d, m, k);
-        if (m >= nc) continue;
-        const int64_t y = m / cols, x = m - y * cols;
-        const int64_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
-        const int64_t step = ALONG_X ? 1 : cols;
-        const int lo = (int)(pos < R ? -pos : -R);
-        const int hi = (int)(ext - 1 - pos < R ? ext - 1 - pos : R);
-        float acc = 0.0f;
-        for (int t = lo; t <= hi; ++t) acc = __builtin_fmaf(g[t < 0 ? -t : t],
-                                                           in[at<BLOCKED>(m + t * step, k, d)], acc);
-        if constexpr (FINAL) {
-            const float rd = rden[m];
-            if (rd > 0.0f) out[e] = acc * rd;
+// The neuron-major layout's passes (dense rows).  Threads of a workgroup are
+// split into groups of sg = min(256, d rounded up to a power of two) lanes;
+// each group takes one neuron and runs along its features, so every tap is a
+// coalesced row segment and the neuron's grid position and window are worked
+// out once per neuron.  XCD x (workgroups blockIdx % 8 == x) owns map rows
+// [x * rpx, (x + 1) * rpx) and its workgroups sweep them in an order that
+// keeps the window's taps in that XCD's L2: row by row for the pass along
+// map rows (taps m + t), in strips of kStrip columns, row by row within a
+// strip, for the pass along map columns (taps m + t cols).  ALONG_X selects
+// the pass; FINAL: out(m, k) = acc * rden[m] written where rden[m] > 0.
+constexpr int kStrip = 32;
+
+template <bool ALONG_X, bool FINAL>
+__global__ __launch_bounds__(kThreads) void k_som_pass_nm(const float *__restrict__ in,
+                                                          float *__restrict__ out, int32_t d,
+                                                          int32_t sg, int32_t rows, int32_t cols,
+                                                          int32_t rpx, int32_t R,
+                                                          const float *__restrict__ g,
+                                                          const float *__restrict__ rden) {
+    const int per = kThreads / sg;  // neurons per workgroup step
+    const int sub = (int)threadIdx.x / sg, kk = (int)threadIdx.x - sub * sg;
+    const int xcd = (int)(blockIdx.x & 7);
+    const int64_t wg = blockIdx.x >> 3, n_wg = gridDim.x >> 3;
+    const int32_t y0 = xcd * rpx;
+    const int32_t nstrip = (cols + kStrip - 1) / kStrip;
+    // positions of this XCD's sweep (with holes past the map's edges)
+    const int64_t npos = ALONG_X ? (int64_t)rpx * cols : (int64_t)nstrip * rpx * kStrip;
+    for (int64_t p0 = wg * per; p0 < npos; p0 += n_wg * per) {
+        const int64_t pos_i = p0 + sub;
+        if (pos_i >= npos) continue;
+        int32_t y, x;
+        if constexpr (ALONG_X) {
+            y = y0 + (int32_t)(pos_i / cols);
+            x = (int32_t)(pos_i % cols);
         } else {
-            out[e] = acc;
+            const int64_t strip = pos_i / ((int64_t)rpx * kStrip);
+            const int64_t rem = pos_i - strip * rpx * kStrip;
+            y = y0 + (int32_t)(rem / kStrip);
+            x = (int32_t)(strip * kStrip + rem % kStrip);
+        }
+        if (y >= rows || x >= cols) continue;
+        const int64_t m = (int64_t)y * cols + x;
+        float rd = 1.0f;
+        if constexpr (FINAL) {
+            rd = rden[m];
+            if (!(rd > 0.0f)) continue;  // no input in the window: the neuron keeps its weights
+        }
+        const int32_t pos = ALONG_X ? x : y, ext = ALONG_X ? cols : rows;
+        const int64_t step = ALONG_X ? 1 : cols;
+        const int lo = pos < R ? -pos : -R;
+        const int hi = ext - 1 - pos < R ? ext - 1 - pos : R;
+        const float *src = in + m * d;
+        const int64_t sd = step * d;  // floats between successive taps
+        for (int k = kk; k < d; k += sg) {
+            // taps kTB at a time, loads first: the window's loads are in
+            // flight together instead of one round trip per tap
+            constexpr int kTB = 8;
+            float acc = 0.0f;
+            int t = lo;
+            // A batch's taps past the window read tap hi again with weight 0:
+            // for finite data that adds exactly 0, and a non-finite tap hi is
+            // summed with its own weight anyway.  (Guarding the add with a
+            // branch or a select measured 30-50 % slower: the compiler then
+            // waits for each load before the next.)
+            for (; t <= hi; t += kTB) {
+                float v[kTB];
+#pragma unroll
+                for (int i = 0; i < kTB; ++i) {
+                    const int ti = t + i <= hi ? t + i : hi;
+                    v[i] = src[(int64_t)ti * sd + k];
+                }
+#pragma unroll
+                for (int i = 0; i < kTB; ++i) {
+                    const int ti = t + i;
+                    const float w = ti <= hi ? g[ti < 0 ? -ti : ti] : 0.0f;
+                    acc = __builtin_fmaf(w, v[i], acc);
+                }
+            }
+            out[m * d + k] = FINAL ? acc * rd : acc;
         }
     }
 }
@@ -415,7 +452,6 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
     hipLaunchKernelGGL((k_som_den_pass<false, float>), gd, dim3(kThreads), 0, st, a.den_t, a.rden,
                        nc, a.rows, a.cols, R, a.g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const dim3 ge(grid_for(elems, n_cu));
     if (blocked && R >= 1 && R <= 8) {
         const int32_t ntx = (a.cols + 63) / 64;
         const int64_t items = (int64_t)a.d * ntx;
@@ -444,10 +480,19 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
         hipLaunchKernelGGL((k_som_pass_blk<false, true>), gb, dim3(kThreads), 0, st, a.T, a.C,
                            (int32_t)nc, a.d, a.rows, a.cols, R, per, a.g, a.rden);
     } else {
-        hipLaunchKernelGGL((k_som_pass<false, true, false>), ge, dim3(kThreads), 0, st, a.S, a.T,
-                           nc, a.d, a.rows, a.cols, R, a.g, nullptr);
-        hipLaunchKernelGGL((k_som_pass<false, false, true>), ge, dim3(kThreads), 0, st, a.T, a.C,
-                           nc, a.d, a.rows, a.cols, R, a.g, a.rden);
+        int32_t sg = 1;
+        while (sg < a.d && sg < kThreads) sg <<= 1;
+        const int64_t per = kThreads / sg;
+        const int32_t rpx = (a.rows + 7) / 8;
+        const int64_t npos = (int64_t)rpx * ((a.cols + kStrip - 1) / kStrip) * kStrip;
+        int64_t wpx = (npos + per - 1) / per;  // workgroups per XCD
+        const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256) * 4;
+        wpx = wpx < 1 ? 1 : (wpx > cap ? cap : wpx);
+        const dim3 gn((unsigned)(8 * wpx));
+        hipLaunchKernelGGL((k_som_pass_nm<true, false>), gn, dim3(kThreads), 0, st, a.S, a.T,
+                           a.d, sg, a.rows, a.cols, rpx, R, a.g, nullptr);
+        hipLaunchKernelGGL((k_som_pass_nm<false, true>), gn, dim3(kThreads), 0, st, a.T, a.C,
+                           a.d, sg, a.rows, a.cols, rpx, R, a.g, a.rden);
     }
     return hipGetLastError();
 }
