@@ -221,6 +221,31 @@ def test_diversity_validation(L):
     assert call(ws_bytes=8) == 4
 
 
+def test_diversity_reference_validation(L):
+    def step(C=FAKE, n=100, d=8, Q=FAKE, mask=FAKE, nseq=5, idx=FAKE, score=FAKE, ws=FAKE,
+             ws_bytes=1 << 20):
+        return L.vs_diversity_step_ref(_P(C), n, d, _P(Q), _P(mask), nseq, _P(idx), _P(score),
+                                       _P(ws), ws_bytes, None)
+    assert step(n=0) == 2
+    assert step(d=0) == 2
+    assert step(nseq=-1) == 2
+    assert step(nseq=0, Q=0) == 0
+    assert step(Q=0) == 1
+    assert step(mask=0) == 1
+    assert step(Q=FAKE + 2) == 5
+    assert step(ws=FAKE + 8) == 5
+    assert step(ws_bytes=8) == 4
+
+    def acc(C=FAKE, n=100, d=8, pick=FAKE, Q=FAKE, nseq=5):
+        return L.vs_diversity_accumulate(_P(C), n, d, _P(pick), _P(Q), nseq, None)
+    assert acc(n=0) == 2
+    assert acc(d=0) == 2
+    assert acc(nseq=0, C=0) == 0
+    assert acc(pick=0) == 1
+    assert acc(Q=0) == 1
+    assert acc(pick=FAKE + 1) == 5
+
+
 def test_som_validation(L):
     F = ctypes.c_float
     assert L.vs_som_update_workspace(0, 4, 8) == 0
