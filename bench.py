@@ -165,8 +165,6 @@ def setup(k, torch, vs, a):
         n, d, nseq, steps = w["n"], w["d"], w["nseq"], w["steps"]
         if a.div_steps is not None:
             steps = n - 1 if a.div_steps == "full" else int(a.div_steps)
-        if a.div_ref == "centroid" and a.div_mode != "step":
-            raise SystemExit("--div-ref centroid runs the per-step scan (--div-mode step)")
         C = torch.from_numpy(w["C"]).to(dev)
         seeds = torch.from_numpy(w["seeds"]).to(dev)
         W = (n + 31) // 32
@@ -183,20 +181,35 @@ def setup(k, torch, vs, a):
             # one Gram row per sequence
             ldg = (n + 63) // 64 * 64
             Gbuf = torch.empty((n, ldg), dtype=torch.float32, device=dev)
-
-            def step():
-                mask.copy_(mask0)
-                G = vs.vs_diversity_gram(C, out=Gbuf)
-                last = seeds
-                for t in range(steps):
-                    vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t],
-                                              want_score=False)
-                    last = picks[t]
             # algorithmic bytes of one scan, averaged over the run: the live
             # (unmasked) entries of one Gram row per sequence -- n - 1 - t at
-            # step t -- its mask row read and written, the pick read and written
+            # step t -- (with the centroid reference also the running sums
+            # read and written), its mask row read and written, the pick read
+            # and written
             live = sum(max(n - 1 - t, 0) for t in range(steps)) / steps
-            w["scan_bytes"] = nseq * (4 * live + 8 * W + 8)
+            if a.div_ref == "centroid":
+                Rbuf = torch.empty((nseq, ldg), dtype=torch.float32, device=dev)
+
+                def step():
+                    mask.copy_(mask0)
+                    G = vs.vs_diversity_gram(C, out=Gbuf)
+                    R = vs.vs_diversity_gram_sums(G, nseq, out=Rbuf)
+                    last = seeds
+                    for t in range(steps):
+                        vs.vs_diversity_step_gram_sum(G, last, R, mask, idx_out=picks[t],
+                                                      want_score=False)
+                        last = picks[t]
+                w["scan_bytes"] = nseq * (12 * live + 8 * W + 8)
+            else:
+                def step():
+                    mask.copy_(mask0)
+                    G = vs.vs_diversity_gram(C, out=Gbuf)
+                    last = seeds
+                    for t in range(steps):
+                        vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t],
+                                                  want_score=False)
+                        last = picks[t]
+                w["scan_bytes"] = nseq * (4 * live + 8 * W + 8)
         elif a.div_ref == "centroid":
             # the reference of each sequence is the running sum of its rows
             # (the centroid times a positive count): start at the seed's row

@@ -42,7 +42,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
            "vs_diversity_step_ref", "vs_diversity_accumulate",
-           "vs_diversity_gram", "vs_diversity_step_gram",
+           "vs_diversity_gram", "vs_diversity_step_gram", "vs_diversity_step_gram_sum",
            "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
            "vs_som_epoch_workspace", "vs_som_epoch", "vs_som_epoch_csr_workspace",
            "vs_som_epoch_csr",
@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_accumulate.argtypes = [P, I64, I32, P, P, I64, P]
     L.vs_diversity_gram.argtypes = [P, I64, I32, P, I64, P]
     L.vs_diversity_step_gram.argtypes = [P, I64, I64, P, P, I64, P, P, P]
+    L.vs_diversity_step_gram_sum.argtypes = [P, I64, I64, P, P, I64, P, I64, P, P, P]
     F = ctypes.c_float
     L.vs_som_update_workspace.argtypes = [I32, I32, I32]
     L.vs_som_update_workspace.restype = SZ
@@ -122,6 +123,7 @@ def lib() -> ctypes.CDLL:
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
                  "vs_diversity_step_gram", "vs_diversity_step_ref", "vs_diversity_accumulate",
+                 "vs_diversity_step_gram_sum",
                  "vs_som_update", "vs_som_update_csr", "vs_som_qe",
                  "vs_som_epoch", "vs_som_epoch_csr",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
@@ -516,6 +518,52 @@ def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None
         rc = L.vs_diversity_step_gram(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(mask_bits),
                                       nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
     _check(rc, "vs_diversity_step_gram")
+    return idx_out, score_out
+
+
+def vs_diversity_gram_sums(G, nseq: int, out=None):
+    """Zeroed running-sum rows R for vs_diversity_step_gram_sum: an
+    (nseq, n) view of an (nseq, ldr) float32 buffer, ldr = n rounded up to 64."""
+    torch = _torch()
+    n = G.shape[0]
+    ldr = (n + 63) // 64 * 64
+    if out is None:
+        out = torch.empty((nseq, ldr), dtype=torch.float32, device=G.device)
+    out.zero_()
+    return out[:, :n]
+
+
+def vs_diversity_step_gram_sum(G, last_pick, R, mask_bits, idx_out=None, score_out=None,
+                               want_score: bool = True):
+    """One centroid-reference step from the Gram matrix: R[s] += G[last_pick[s]],
+    then the masked arg-min of R[s] (R from vs_diversity_gram_sums, updated
+    in place, as is mask_bits)."""
+    torch = _torch()
+    L = lib()
+    for name, t in (("G", G), ("R", R)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
+                or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride")
+    _dev(last_pick, "last_pick", torch.int32, 1)
+    n = G.shape[0]
+    nseq = last_pick.numel()
+    if G.shape[1] != n or tuple(R.shape) != (nseq, n):
+        raise ValueError("G must be n x n and R nseq x n")
+    if mask_bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask_bits must be int32 or uint32 words")
+    _dev(mask_bits, "mask_bits", mask_bits.dtype, 2)
+    if tuple(mask_bits.shape) != (nseq, (n + 31) // 32):
+        raise ValueError("mask_bits disagree with G and last_pick")
+    dev = G.device
+    if idx_out is None:
+        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
+    if score_out is None and want_score:
+        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_step_gram_sum(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(R),
+                                          R.stride(0), _ptr(mask_bits), nseq, _ptr(idx_out),
+                                          _ptr(score_out), _stream(dev))
+    _check(rc, "vs_diversity_step_gram_sum")
     return idx_out, score_out
 
 

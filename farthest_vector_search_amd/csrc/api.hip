@@ -549,6 +549,25 @@ VS_API int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg,
     return VS_OK;
 }
 
+VS_API int vs_diversity_step_gram_sum(const float *G, int64_t n, int64_t ldg,
+                                      const int32_t *last_pick, float *R, int64_t ldr,
+                                      uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
+                                      float *score_out, void *stream) {
+    if (n < 1 || n > kMaxIndex || ldg < n || ldg % 4 != 0 || ldr < n || ldr % 4 != 0 ||
+        nseq < 0 || nseq > kMaxIndex)
+        return VS_ERR_SHAPE;
+    if (nseq == 0) return VS_OK;
+    if (!G || !last_pick || !R || !mask_bits || !idx_out) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(G) & 15) != 0 || (reinterpret_cast<uintptr_t>(R) & 15) != 0 ||
+        !al4(last_pick) || !al4(mask_bits) || !al4(idx_out) || !al4(score_out))
+        return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_div_gram_step(G, n, ldg, last_pick, mask_bits, nseq, idx_out, score_out,
+                                        reinterpret_cast<hipStream_t>(stream), R, ldr));
+    return VS_OK;
+}
+
 // ---- norms, tile rule, status ---------------------------------------------
 
 VS_API int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t feature_major,

@@ -30,15 +30,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // hide the row loads' latency), then the waves' (value, index) pairs are
 // merged through LDS; the order of a lexicographic minimum is immaterial, so
 // the pick equals the one-wave scan's.
+//
+// SUM: the centroid reading.  C's rows are unit-norm, so the cosine to a
+// sequence's centroid ranks candidates as C[j] . sum_p C[p] = sum_p G[p][j]
+// does (p over the sequence's rows so far); R[s] keeps that running sum of
+// Gram rows.  A step first adds the reference's row, R[s] += G[pick[s]],
+// then takes the masked arg-min of R[s]; masked columns are neither read nor
+// updated (they are never candidates again).
 constexpr int kWPS = 4;
 
+template <bool SUM>
 __global__ __launch_bounds__(64 * kWPS) void k_div_gram_step(const float *__restrict__ G,
                                                             int64_t n, int64_t ldg,
                                                             const int32_t *__restrict__ pick,
                                                             uint32_t *__restrict__ mask,
                                                             int64_t nseq,
                                                             int32_t *__restrict__ idx_out,
-                                                            float *__restrict__ score_out) {
+                                                            float *__restrict__ score_out,
+                                                            float *__restrict__ R, int64_t ldr) {
     __shared__ float s_best[kWPS];
     __shared__ int64_t s_idx[kWPS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -76,7 +85,13 @@ __global__ __launch_bounds__(64 * kWPS) void k_div_gram_step(const float *__rest
             if (live4 == 0) continue;
             // ld % 4 == 0 and G 16-byte aligned: columns j0 .. j0 + 3 are in the
             // row's padded storage even past n
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
+            f32x4 v = *reinterpret_cast<const f32x4 *>(row + j0);
+        if constexpr (SUM) {
+            // ldr % 4 == 0 and R 16-byte aligned, as for G
+            f32x4 *rp = reinterpret_cast<f32x4 *>(R + s * ldr + j0);
+            v += *rp;
+            *rp = v;
+        }
     #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float x = v[e];
@@ -124,12 +139,18 @@ __global__ __launch_bounds__(64 * kWPS) void k_div_gram_step(const float *__rest
 
 hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
                                 uint32_t *mask, int64_t nseq, int32_t *idx_out,
-                                float *score_out, hipStream_t st) {
+                                float *score_out, hipStream_t st, float *R, int64_t ldr) {
     if (nseq <= 0) return hipSuccess;
-    timing_before(st, "k_div_gram_step");
     const unsigned grid = (unsigned)(nseq < (1 << 20) ? nseq : (1 << 20));
-    hipLaunchKernelGGL(k_div_gram_step, dim3(grid), dim3(64 * kWPS), 0, st, G, n, ldg, pick, mask,
-                       nseq, idx_out, score_out);
+    if (R) {
+        timing_before(st, "k_div_gram_step<sum>");
+        hipLaunchKernelGGL(k_div_gram_step<true>, dim3(grid), dim3(64 * kWPS), 0, st, G, n, ldg,
+                           pick, mask, nseq, idx_out, score_out, R, ldr);
+    } else {
+        timing_before(st, "k_div_gram_step");
+        hipLaunchKernelGGL(k_div_gram_step<false>, dim3(grid), dim3(64 * kWPS), 0, st, G, n, ldg,
+                           pick, mask, nseq, idx_out, score_out, R, ldr);
+    }
     const hipError_t err = hipGetLastError();
     timing_after(st);
     return err;

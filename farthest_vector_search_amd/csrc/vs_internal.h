@@ -162,10 +162,13 @@ hipError_t launch_row_argbest(const float *S, int64_t nq, int64_t nc, int64_t ld
 // Q[s] += C[pick[s]] for every sequence whose pick is in [0, n)
 hipError_t launch_div_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick,
                                  float *Q, int64_t nseq, hipStream_t st);
-// one diversity step from a cached score block G (G[r * ldg + j] = C[r] . C[j])
+// one diversity step from a cached score block G (G[r * ldg + j] = C[r] . C[j]);
+// with R (nseq x ldr running sums of Gram rows) the centroid reading:
+// R[s] += G[pick[s]], then the masked arg-min of R[s]
 hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const int32_t *pick,
                                 uint32_t *mask, int64_t nseq, int32_t *idx_out,
-                                float *score_out, hipStream_t st);
+                                float *score_out, hipStream_t st, float *R = nullptr,
+                                int64_t ldr = 0);
 // CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
 int32_t csr_groups(int64_t nc);
 hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);

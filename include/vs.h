@@ -249,6 +249,26 @@ int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const int32_t 
  */
 int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ldg,
                       void *stream);
+/*
+ *   vs_diversity_step_gram_sum  the centroid reading from G [DIV, "FP16
+ *                           storage (compounding optimization)": the
+ *                           reference is the sequence's centroid].  C's rows
+ *                           unit-norm: C[j] . sum_p C[p] = sum_p G[p][j], so
+ *                           a run keeps R (nseq x ldr float32, ldr >= n,
+ *                           ldr % 4 == 0, 16-byte aligned, all zero before
+ *                           its first step) and each call first adds the
+ *                           reference's row, R[s] += G[last_pick[s]] (for
+ *                           the first step last_pick is the seed), then picks
+ *                           the unmasked j with the smallest R[s][j] (lowest
+ *                           index on ties), sets its bit, and reports
+ *                           score_out = R[s][pick].  Columns already masked
+ *                           are neither read nor updated.  last_pick outside
+ *                           [0, n): -1, mask and R[s] unchanged.  No
+ *                           workspace.
+ */
+int vs_diversity_step_gram_sum(const float *G, int64_t n, int64_t ldg, const int32_t *last_pick,
+                               float *R, int64_t ldr, uint32_t *mask_bits, int64_t nseq,
+                               int32_t *idx_out, float *score_out, void *stream);
 int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg, const int32_t *last_pick,
                            uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
                            float *score_out, void *stream);

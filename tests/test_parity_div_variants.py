@@ -160,6 +160,100 @@ def test_workload_3_centroid():
     assert (picks >= 0).all()
 
 
+# ------------------------------------------- centroid from the Gram matrix --
+
+def gpu_chain_gram_centroid(C, seeds, steps):
+    """Centroid-reference run from the cached Gram matrix: R[s] += G[last],
+    masked arg-min of R[s].  Returns picks, cosines (score over the norm of
+    the sum of the sequence's rows so far, taken on the host in fp64), masks."""
+    Cd = T(C)
+    nseq = len(seeds)
+    mask = T(seed_masks(C.shape[0], seeds).view(np.int32))
+    last = T(np.asarray(seeds, np.int32))
+    picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    scores = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    G = vs.vs_diversity_gram(Cd)
+    R = vs.vs_diversity_gram_sums(G, nseq)
+    for t in range(steps):
+        vs.vs_diversity_step_gram_sum(G, last, R, mask, idx_out=picks[t], score_out=scores[t])
+        last = picks[t]
+    torch.cuda.synchronize()
+    picks = picks.cpu().numpy().T.copy()
+    scores = scores.cpu().numpy().T.astype(np.float64)
+    C64 = C.astype(np.float64)
+    ref = C64[np.asarray(seeds)].copy()
+    cos = np.full(picks.shape, np.nan)
+    for t in range(steps):
+        live = picks[:, t] >= 0
+        cos[live, t] = scores[live, t] / np.linalg.norm(ref[live], axis=1)
+        ref[live] += C64[picks[live, t]]
+    return picks, cos, mask.cpu().numpy().view(np.uint32)
+
+
+def test_gram_centroid_walk():
+    """The hand-worked plane walk, the vectors padded with zeros to d = 4
+    (cosines unchanged)."""
+    w = diversity_centroid()
+    C = np.zeros((w["C"].shape[0], 4), np.float32)
+    C[:, :2] = w["C"]
+    picks, cos, _ = gpu_chain_gram_centroid(C, np.array([w["seed"]], np.int32), len(w["picks"]))
+    assert list(picks[0]) == w["picks"]
+    for v, e in zip(cos[0], w["values"]):
+        assert (np.isnan(v) and np.isnan(e)) or abs(v - e) <= 1e-6
+
+
+@pytest.mark.parametrize("n,d,nseq,steps", [(40, 4, 5, 41), (300, 64, 129, 20),
+                                            (129, 768, 70, 6), (700, 500, 520, 5)])
+def test_gram_centroid_chain(n, d, nseq, steps):
+    C = synth.dense_case(1, n, d, "unit", key=n + d + 1)[1]
+    (r,) = synth.rng_children(1900 + n, 1)
+    seeds = r.choice(n, nseq, replace=nseq > n).astype(np.int32)
+    picks, cos, masks = gpu_chain_gram_centroid(C, seeds, steps)
+    fails, _ = validate_centroid(C, seeds, picks, cos, masks)
+    assert not fails, fails
+
+
+def test_gram_centroid_full_length():
+    n, d, nseq = 160, 48, 24
+    C = synth.dense_case(1, n, d, "unit", key=888)[1]
+    (r,) = synth.rng_children(2888, 1)
+    seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+    picks, cos, masks = gpu_chain_gram_centroid(C, seeds, n + 1)
+    fails, _ = validate_centroid(C, seeds, picks, cos, masks)
+    assert not fails, fails
+    assert (picks[:, :n - 1] >= 0).all() and (picks[:, n - 1:] == -1).all()
+
+
+def test_gram_centroid_invalid_reference():
+    """A reference outside [0, n) gives -1 and leaves the mask and R alone."""
+    C = synth.dense_case(1, 100, 8, "unit", key=3)[1]
+    Cd = T(C)
+    G = vs.vs_diversity_gram(Cd)
+    R = vs.vs_diversity_gram_sums(G, 3)
+    last = T(np.array([5, -1, 100], np.int32))
+    mask = T(seed_masks(100, [5, 0, 0]).view(np.int32))
+    before = mask.cpu().numpy().copy()
+    idx, _ = vs.vs_diversity_step_gram_sum(G, last, R, mask)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    assert idx[0] >= 0 and idx[1] == -1 and idx[2] == -1
+    assert np.array_equal(mask.cpu().numpy()[1:], before[1:])
+    assert not R[1:].any()
+
+
+@pytest.mark.slow
+def test_workload_3_gram_centroid():
+    """8,359 x 768 table, 3,584 sequences, 64 centroid-reference steps from the
+    Gram matrix; 96 seeded sequences replayed by the oracle."""
+    w = synth.workload(3)
+    picks, cos, masks = gpu_chain_gram_centroid(w["C"], w["seeds"], w["steps"])
+    sel = synth.sample_queries(len(w["seeds"]), 96, key=33)
+    fails, stats = validate_centroid(w["C"], w["seeds"][sel], picks[sel], cos[sel], masks[sel],
+                                     threads=16)
+    assert not fails, fails
+    assert (picks >= 0).all()
+
+
 # --------------------------------------------------------- full length --
 
 @pytest.mark.parametrize("n,d,nseq", [(300, 64, 40), (97, 8, 33)])
