@@ -193,22 +193,15 @@ def setup(k, torch, vs, a):
                 def step():
                     mask.copy_(mask0)
                     G = vs.vs_diversity_gram(C, out=Gbuf)
-                    R = vs.vs_diversity_gram_sums(G, nseq, out=Rbuf)
-                    last = seeds
-                    for t in range(steps):
-                        vs.vs_diversity_step_gram_sum(G, last, R, mask, idx_out=picks[t],
-                                                      want_score=False)
-                        last = picks[t]
+                    vs.vs_diversity_run_gram(G, seeds, mask, steps, R=Rbuf[:, :n],
+                                             picks_out=picks, want_scores=False)
                 w["scan_bytes"] = nseq * (12 * live + 8 * W + 8)
             else:
                 def step():
                     mask.copy_(mask0)
                     G = vs.vs_diversity_gram(C, out=Gbuf)
-                    last = seeds
-                    for t in range(steps):
-                        vs.vs_diversity_step_gram(G, last, mask, idx_out=picks[t],
-                                                  want_score=False)
-                        last = picks[t]
+                    vs.vs_diversity_run_gram(G, seeds, mask, steps, picks_out=picks,
+                                             want_scores=False)
                 w["scan_bytes"] = nseq * (4 * live + 8 * W + 8)
         elif a.div_ref == "centroid":
             # the reference of each sequence is the running sum of its rows
@@ -226,11 +219,8 @@ def setup(k, torch, vs, a):
         else:
             def step():
                 mask.copy_(mask0)
-                last = seeds
-                for t in range(steps):
-                    vs.vs_diversity_step(C, last, mask, idx_out=picks[t], workspace=ws,
-                                         want_score=False)
-                    last = picks[t]
+                vs.vs_diversity_run(C, seeds, mask, steps, picks_out=picks, workspace=ws,
+                                    want_scores=False)
         pairs = nseq * n * steps
         flops = 2.0 * d * pairs
         cfg = dict(workload=w["name"], n=n, d=d, nseq=nseq, steps_per_run=steps,

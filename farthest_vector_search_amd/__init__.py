@@ -41,6 +41,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
+           "vs_diversity_run", "vs_diversity_run_gram",
            "vs_diversity_step_ref", "vs_diversity_accumulate",
            "vs_diversity_gram", "vs_diversity_step_gram", "vs_diversity_step_gram_sum",
            "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_gram.argtypes = [P, I64, I32, P, I64, P]
     L.vs_diversity_step_gram.argtypes = [P, I64, I64, P, P, I64, P, P, P]
     L.vs_diversity_step_gram_sum.argtypes = [P, I64, I64, P, P, I64, P, I64, P, P, P]
+    L.vs_diversity_run.argtypes = [P, I64, I32, P, P, I64, I32, P, P, P, SZ, P]
+    L.vs_diversity_run_gram.argtypes = [P, I64, I64, P, P, I64, P, I64, I32, P, P, P]
     F = ctypes.c_float
     L.vs_som_update_workspace.argtypes = [I32, I32, I32]
     L.vs_som_update_workspace.restype = SZ
@@ -123,7 +126,7 @@ def lib() -> ctypes.CDLL:
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
                  "vs_diversity_step_gram", "vs_diversity_step_ref", "vs_diversity_accumulate",
-                 "vs_diversity_step_gram_sum",
+                 "vs_diversity_step_gram_sum", "vs_diversity_run", "vs_diversity_run_gram",
                  "vs_som_update", "vs_som_update_csr", "vs_som_qe",
                  "vs_som_epoch", "vs_som_epoch_csr",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
@@ -519,6 +522,71 @@ def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None
                                       nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
     _check(rc, "vs_diversity_step_gram")
     return idx_out, score_out
+
+
+def _mask_arg(mask_bits, nseq, n):
+    torch = _torch()
+    if mask_bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask_bits must be int32 or uint32 words")
+    _dev(mask_bits, "mask_bits", mask_bits.dtype, 2)
+    if tuple(mask_bits.shape) != (nseq, (n + 31) // 32):
+        raise ValueError(f"mask_bits must be [{nseq}, {(n + 31) // 32}]")
+
+
+def vs_diversity_run(C, seeds, mask_bits, steps: int, picks_out=None, scores_out=None,
+                     workspace=None, want_scores: bool = True):
+    """`steps` diversity steps from the seeds; returns picks [steps, nseq] and
+    scores [steps, nseq] (or None).  mask_bits (seed bits set) is updated."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    _dev(seeds, "seeds", torch.int32, 1)
+    n, d = C.shape
+    nseq = seeds.numel()
+    _mask_arg(mask_bits, nseq, n)
+    dev = C.device
+    if picks_out is None:
+        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+    if scores_out is None and want_scores:
+        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_run(_ptr(C), n, d, _ptr(seeds), _ptr(mask_bits), nseq, int(steps),
+                                _ptr(picks_out), _ptr(scores_out), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_diversity_run")
+    return picks_out, scores_out
+
+
+def vs_diversity_run_gram(G, seeds, mask_bits, steps: int, R=None, picks_out=None,
+                          scores_out=None, want_scores: bool = True):
+    """A whole run from the Gram matrix G: the last-pick reading, or with R
+    (rows from vs_diversity_gram_sums; cleared by the call) the centroid one."""
+    torch = _torch()
+    L = lib()
+    for name, t in (("G", G), ("R", R)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
+                or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride")
+    _dev(seeds, "seeds", torch.int32, 1)
+    n = G.shape[0]
+    nseq = seeds.numel()
+    if G.shape[1] != n or (R is not None and tuple(R.shape) != (nseq, n)):
+        raise ValueError("G must be n x n and R nseq x n")
+    _mask_arg(mask_bits, nseq, n)
+    dev = G.device
+    if picks_out is None:
+        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+    if scores_out is None and want_scores:
+        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_run_gram(_ptr(G), n, G.stride(0), _ptr(seeds), _ptr(R),
+                                     0 if R is None else R.stride(0), _ptr(mask_bits), nseq,
+                                     int(steps), _ptr(picks_out), _ptr(scores_out), _stream(dev))
+    _check(rc, "vs_diversity_run_gram")
+    return picks_out, scores_out
 
 
 def vs_diversity_gram_sums(G, nseq: int, out=None):

@@ -461,6 +461,28 @@ VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t
     return VS_OK;
 }
 
+// A whole run: `steps` steps chained on the stream, step t's references being
+// step t-1's picks (the seeds for t = 0).
+VS_API int vs_diversity_run(const float *C, int64_t n, int32_t d, const int32_t *seeds,
+                            uint32_t *mask_bits, int64_t nseq, int32_t steps,
+                            int32_t *picks_out, float *scores_out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || d > kMaxDim || nseq < 0 || nseq > kMaxIndex ||
+        steps < 0)
+        return VS_ERR_SHAPE;
+    if (nseq == 0 || steps == 0) return VS_OK;
+    if (!seeds || !picks_out) return VS_ERR_NULL;
+    for (int32_t t = 0; t < steps; ++t) {
+        const int32_t *last = t == 0 ? seeds : picks_out + (int64_t)(t - 1) * nseq;
+        float *sc = scores_out ? scores_out + (int64_t)t * nseq : nullptr;
+        if (const int s = vs_diversity_step(C, n, d, last, mask_bits, nseq,
+                                            picks_out + (int64_t)t * nseq, sc, workspace,
+                                            workspace_bytes, stream))
+            return s;
+    }
+    return VS_OK;
+}
+
 // ---- diversity from a cached Gram matrix -------------------------------------
 
 VS_API int vs_diversity_step_ref(const float *C, int64_t n, int32_t d, const float *Q,
@@ -565,6 +587,34 @@ VS_API int vs_diversity_step_gram_sum(const float *G, int64_t n, int64_t ldg,
     if (const int s = device_ready(&n_cu)) return s;
     VS_TRY_HIP(vs::launch_div_gram_step(G, n, ldg, last_pick, mask_bits, nseq, idx_out, score_out,
                                         reinterpret_cast<hipStream_t>(stream), R, ldr));
+    return VS_OK;
+}
+
+VS_API int vs_diversity_run_gram(const float *G, int64_t n, int64_t ldg, const int32_t *seeds,
+                                 float *R, int64_t ldr, uint32_t *mask_bits, int64_t nseq,
+                                 int32_t steps, int32_t *picks_out, float *scores_out,
+                                 void *stream) {
+    if (n < 1 || n > kMaxIndex || ldg < n || nseq < 0 || nseq > kMaxIndex || steps < 0 ||
+        (R && (ldr < n || ldr % 4 != 0)))
+        return VS_ERR_SHAPE;
+    if (nseq == 0 || steps == 0) return VS_OK;
+    if (!seeds || !picks_out) return VS_ERR_NULL;
+    if (R) {
+        if ((reinterpret_cast<uintptr_t>(R) & 15) != 0) return VS_ERR_ALIGN;
+        int n_cu = 0;
+        if (const int s = device_ready(&n_cu)) return s;
+        VS_TRY_HIP(vs::launch_zero_rows(R, nseq, ldr, n, reinterpret_cast<hipStream_t>(stream)));
+    }
+    for (int32_t t = 0; t < steps; ++t) {
+        const int32_t *last = t == 0 ? seeds : picks_out + (int64_t)(t - 1) * nseq;
+        int32_t *idx = picks_out + (int64_t)t * nseq;
+        float *sc = scores_out ? scores_out + (int64_t)t * nseq : nullptr;
+        const int s = R ? vs_diversity_step_gram_sum(G, n, ldg, last, R, ldr, mask_bits, nseq,
+                                                     idx, sc, stream)
+                        : vs_diversity_step_gram(G, n, ldg, last, mask_bits, nseq, idx, sc,
+                                                 stream);
+        if (s) return s;
+    }
     return VS_OK;
 }
 

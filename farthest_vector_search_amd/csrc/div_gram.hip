@@ -156,4 +156,21 @@ hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const in
     return err;
 }
 
+__global__ __launch_bounds__(256) void k_zero_rows(float *__restrict__ p, int64_t rows,
+                                                  int64_t ld, int64_t n) {
+    const int64_t total = rows * ld;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride)
+        if (i % ld < n) p[i] = 0.0f;
+}
+
+hipError_t launch_zero_rows(float *p, int64_t rows, int64_t ld, int64_t n, hipStream_t st) {
+    const int64_t total = rows * ld;
+    if (total <= 0) return hipSuccess;
+    const int64_t want = (total + 255) / 256;
+    const unsigned grid = (unsigned)(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(k_zero_rows, dim3(grid), dim3(256), 0, st, p, rows, ld, n);
+    return hipGetLastError();
+}
+
 }  // namespace vs

@@ -205,6 +205,20 @@ int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * A whole diversity run [DIV "Current Behavior": the driver repeats the
+ * step, each iteration's picks becoming the next one's references]: `steps`
+ * calls of vs_diversity_step chained on the stream, step t's last_pick
+ * being step t-1's picks (seeds for t = 0).  mask_bits as for the step (the
+ * seeds' bits set by the caller), updated in place; picks_out int32[steps x
+ * nseq] (row t = step t), scores_out float32[steps x nseq] or NULL.  Same
+ * workspace as vs_diversity_step.  Results equal those of the steps called
+ * one by one, bit for bit.
+ */
+int vs_diversity_run(const float *C, int64_t n, int32_t d, const int32_t *seeds,
+                     uint32_t *mask_bits, int64_t nseq, int32_t steps, int32_t *picks_out,
+                     float *scores_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The diversity step against explicit reference rows [DIV "Current
  * Behavior"; "FP16 storage (compounding optimization)" ranks candidates
  * against the sequence's centroid].
@@ -269,6 +283,16 @@ int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ld
 int vs_diversity_step_gram_sum(const float *G, int64_t n, int64_t ldg, const int32_t *last_pick,
                                float *R, int64_t ldr, uint32_t *mask_bits, int64_t nseq,
                                int32_t *idx_out, float *score_out, void *stream);
+/*
+ *   vs_diversity_run_gram   a whole run from G, as vs_diversity_run: with R
+ *                           NULL the last-pick reading (vs_diversity_step_gram
+ *                           per step), else the centroid reading
+ *                           (vs_diversity_step_gram_sum per step; R as there,
+ *                           cleared by this call before the first step).
+ */
+int vs_diversity_run_gram(const float *G, int64_t n, int64_t ldg, const int32_t *seeds,
+                          float *R, int64_t ldr, uint32_t *mask_bits, int64_t nseq,
+                          int32_t steps, int32_t *picks_out, float *scores_out, void *stream);
 int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg, const int32_t *last_pick,
                            uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
                            float *score_out, void *stream);

@@ -246,6 +246,31 @@ def test_diversity_reference_validation(L):
     assert acc(pick=FAKE + 1) == 5
 
 
+def test_diversity_run_validation(L):
+    def run(C=FAKE, n=100, d=8, seeds=FAKE, mask=FAKE, nseq=5, steps=3, picks=FAKE, scores=FAKE,
+            ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_diversity_run(_P(C), n, d, _P(seeds), _P(mask), nseq, steps, _P(picks),
+                                  _P(scores), _P(ws), ws_bytes, None)
+    assert run(steps=-1) == 2
+    assert run(n=0) == 2
+    assert run(steps=0, seeds=0) == 0
+    assert run(seeds=0) == 1
+    assert run(picks=0) == 1
+    assert run(ws_bytes=8) == 4
+
+    def run_gram(G=FAKE, n=100, ldg=128, seeds=FAKE, R=0, ldr=0, mask=FAKE, nseq=5, steps=3,
+                 picks=FAKE, scores=FAKE):
+        return L.vs_diversity_run_gram(_P(G), n, ldg, _P(seeds), _P(R), ldr, _P(mask), nseq,
+                                       steps, _P(picks), _P(scores), None)
+    assert run_gram(steps=-2) == 2
+    assert run_gram(ldg=99) == 2
+    assert run_gram(R=FAKE, ldr=98) == 2
+    assert run_gram(R=FAKE, ldr=102) == 2
+    assert run_gram(nseq=0, seeds=0) == 0
+    assert run_gram(picks=0) == 1
+    assert run_gram(R=FAKE + 4, ldr=128) == 5
+
+
 def test_som_validation(L):
     F = ctypes.c_float
     assert L.vs_som_update_workspace(0, 4, 8) == 0

@@ -306,3 +306,56 @@ def test_workload_3_full_length_gram():
                                   threads=16)
     assert not fails, fails
     assert stats["rows"] == 16 * (n - 1)
+
+
+# ------------------------------------------------------------ whole runs --
+
+@pytest.mark.parametrize("n,d,nseq,steps", [(300, 64, 129, 20), (1000, 65, 70, 9)])
+def test_run_matches_steps(n, d, nseq, steps, div_kernel):
+    """vs_diversity_run chains the steps on the stream: the same picks,
+    scores and masks, bit for bit, as calling the step one by one."""
+    C = synth.dense_case(1, n, d, "unit", key=n + 5 * d)[1]
+    (r,) = synth.rng_children(2950 + n, 1)
+    seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+    p1, s1, m1 = gpu_chain(C, seeds, steps)
+    mask = T(seed_masks(n, seeds).view(np.int32))
+    p2, s2 = vs.vs_diversity_run(T(C), T(seeds), mask, steps)
+    torch.cuda.synchronize()
+    assert np.array_equal(p2.cpu().numpy().T, p1)
+    assert np.array_equal(s2.cpu().numpy().T.view(np.uint32), s1.view(np.uint32))
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), m1)
+
+
+@pytest.mark.parametrize("centroid", [False, True])
+def test_run_gram_matches_steps(centroid):
+    n, d, nseq, steps = 400, 96, 90, 30
+    C = synth.dense_case(1, n, d, "unit", key=4000 + centroid)[1]
+    (r,) = synth.rng_children(4100, 1)
+    seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+    Cd = T(C)
+    G = vs.vs_diversity_gram(Cd)
+    # step by step
+    m1 = T(seed_masks(n, seeds).view(np.int32))
+    R1 = vs.vs_diversity_gram_sums(G, nseq) if centroid else None
+    p1 = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    s1 = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    last = T(seeds)
+    for t in range(steps):
+        if centroid:
+            vs.vs_diversity_step_gram_sum(G, last, R1, m1, idx_out=p1[t], score_out=s1[t])
+        else:
+            vs.vs_diversity_step_gram(G, last, m1, idx_out=p1[t], score_out=s1[t])
+        last = p1[t]
+    # one call (R deliberately left dirty: the call clears it)
+    m2 = T(seed_masks(n, seeds).view(np.int32))
+    R2 = None
+    if centroid:
+        R2 = vs.vs_diversity_gram_sums(G, nseq)
+        R2.fill_(7.0)
+    p2, s2 = vs.vs_diversity_run_gram(G, T(seeds), m2, steps, R=R2)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(m1, m2)
+    if centroid:
+        assert torch.equal(R1, R2)
