@@ -210,12 +210,8 @@ def setup(k, torch, vs, a):
 
             def step():
                 mask.copy_(mask0)
-                Q.zero_()
-                vs.vs_diversity_accumulate(C, seeds, Q)
-                for t in range(steps):
-                    vs.vs_diversity_step_ref(C, Q, mask, idx_out=picks[t], workspace=ws,
-                                             want_score=False)
-                    vs.vs_diversity_accumulate(C, picks[t], Q)
+                vs.vs_diversity_run_ref(C, seeds, mask, steps, Q=Q, picks_out=picks,
+                                        workspace=ws, want_scores=False)
         else:
             def step():
                 mask.copy_(mask0)

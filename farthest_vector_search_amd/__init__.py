@@ -41,7 +41,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
            "vs_bmu_search_csr_blocked_f16", "vs_diversity_step_workspace", "vs_diversity_step",
-           "vs_diversity_run", "vs_diversity_run_gram",
+           "vs_diversity_run", "vs_diversity_run_gram", "vs_diversity_run_ref",
            "vs_diversity_step_ref", "vs_diversity_accumulate",
            "vs_diversity_gram", "vs_diversity_step_gram", "vs_diversity_step_gram_sum",
            "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
     L.vs_diversity_step_gram_sum.argtypes = [P, I64, I64, P, P, I64, P, I64, P, P, P]
     L.vs_diversity_run.argtypes = [P, I64, I32, P, P, I64, I32, P, P, P, SZ, P]
     L.vs_diversity_run_gram.argtypes = [P, I64, I64, P, P, I64, P, I64, I32, P, P, P]
+    L.vs_diversity_run_ref.argtypes = [P, I64, I32, P, P, P, I64, I32, P, P, P, SZ, P]
     F = ctypes.c_float
     L.vs_som_update_workspace.argtypes = [I32, I32, I32]
     L.vs_som_update_workspace.restype = SZ
@@ -127,6 +128,7 @@ def lib() -> ctypes.CDLL:
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
                  "vs_diversity_step_gram", "vs_diversity_step_ref", "vs_diversity_accumulate",
                  "vs_diversity_step_gram_sum", "vs_diversity_run", "vs_diversity_run_gram",
+                 "vs_diversity_run_ref",
                  "vs_som_update", "vs_som_update_csr", "vs_som_qe",
                  "vs_som_epoch", "vs_som_epoch_csr",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
@@ -556,6 +558,36 @@ def vs_diversity_run(C, seeds, mask_bits, steps: int, picks_out=None, scores_out
                                 ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_diversity_run")
     return picks_out, scores_out
+
+
+def vs_diversity_run_ref(C, seeds, mask_bits, steps: int, Q=None, picks_out=None,
+                         scores_out=None, workspace=None, want_scores: bool = True):
+    """A whole centroid-reading run with explicit references; returns (picks,
+    scores, Q) with Q the final per-sequence sums of rows."""
+    torch = _torch()
+    L = lib()
+    _dev(C, "C", torch.float32, 2)
+    _dev(seeds, "seeds", torch.int32, 1)
+    n, d = C.shape
+    nseq = seeds.numel()
+    _mask_arg(mask_bits, nseq, n)
+    dev = C.device
+    if Q is None:
+        Q = torch.empty((nseq, d), dtype=torch.float32, device=dev)
+    _dev(Q, "Q", torch.float32, 2)
+    if tuple(Q.shape) != (nseq, d):
+        raise ValueError("Q must be (nseq, d)")
+    if picks_out is None:
+        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+    if scores_out is None and want_scores:
+        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_diversity_run_ref(_ptr(C), n, d, _ptr(seeds), _ptr(Q), _ptr(mask_bits), nseq,
+                                    int(steps), _ptr(picks_out), _ptr(scores_out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_diversity_run_ref")
+    return picks_out, scores_out, Q
 
 
 def vs_diversity_run_gram(G, seeds, mask_bits, steps: int, R=None, picks_out=None,

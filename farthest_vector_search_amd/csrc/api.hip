@@ -534,6 +534,33 @@ VS_API int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const i
     return VS_OK;
 }
 
+VS_API int vs_diversity_run_ref(const float *C, int64_t n, int32_t d, const int32_t *seeds,
+                                float *Q, uint32_t *mask_bits, int64_t nseq, int32_t steps,
+                                int32_t *picks_out, float *scores_out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (n < 1 || n > kMaxIndex || d < 1 || d > kMaxDim || nseq < 0 || nseq > kMaxIndex ||
+        steps < 0)
+        return VS_ERR_SHAPE;
+    if (nseq == 0 || steps == 0) return VS_OK;
+    if (!C || !seeds || !Q || !picks_out) return VS_ERR_NULL;
+    if (!al4(C) || !al4(seeds) || !al4(Q)) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // Q[s] = the seed's row: cleared, then the seed added (0 + x is exact)
+    VS_TRY_HIP(vs::launch_zero_rows(Q, nseq, d, d, st));
+    VS_TRY_HIP(vs::launch_div_accumulate(C, n, d, seeds, Q, nseq, st));
+    for (int32_t t = 0; t < steps; ++t) {
+        int32_t *idx = picks_out + (int64_t)t * nseq;
+        float *sc = scores_out ? scores_out + (int64_t)t * nseq : nullptr;
+        if (const int s = vs_diversity_step_ref(C, n, d, Q, mask_bits, nseq, idx, sc, workspace,
+                                                workspace_bytes, stream))
+            return s;
+        VS_TRY_HIP(vs::launch_div_accumulate(C, n, d, idx, Q, nseq, st));
+    }
+    return VS_OK;
+}
+
 VS_API int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ldg,
                              void *stream) {
     if (n < 1 || n > kMaxIndex || d < 1 || ldg < n || ldg % 4 != 0) return VS_ERR_SHAPE;

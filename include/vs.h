@@ -242,6 +242,19 @@ int vs_diversity_step_ref(const float *C, int64_t n, int32_t d, const float *Q,
                           void *workspace, size_t workspace_bytes, void *stream);
 int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick, float *Q,
                             int64_t nseq, void *stream);
+/*
+ *   vs_diversity_run_ref     a whole centroid-reading run with explicit
+ *                            references, as vs_diversity_run: Q (nseq x d
+ *                            float32, caller-owned) is set to the seeds' rows,
+ *                            then each step is vs_diversity_step_ref followed
+ *                            by vs_diversity_accumulate of its picks; on
+ *                            return Q holds each sequence's sum of rows.
+ *                            Workspace as vs_diversity_step.
+ */
+int vs_diversity_run_ref(const float *C, int64_t n, int32_t d, const int32_t *seeds, float *Q,
+                         uint32_t *mask_bits, int64_t nseq, int32_t steps, int32_t *picks_out,
+                         float *scores_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * The diversity step from a cached Gram matrix [DIV "Current Behavior"; the

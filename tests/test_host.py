@@ -271,6 +271,19 @@ def test_diversity_run_validation(L):
     assert run_gram(R=FAKE + 4, ldr=128) == 5
 
 
+def test_diversity_run_ref_validation(L):
+    def run(C=FAKE, n=100, d=8, seeds=FAKE, Q=FAKE, mask=FAKE, nseq=5, steps=3, picks=FAKE,
+            scores=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_diversity_run_ref(_P(C), n, d, _P(seeds), _P(Q), _P(mask), nseq, steps,
+                                      _P(picks), _P(scores), _P(ws), ws_bytes, None)
+    assert run(steps=-1) == 2
+    assert run(d=0) == 2
+    assert run(steps=0, Q=0) == 0
+    assert run(Q=0) == 1
+    assert run(seeds=0) == 1
+    assert run(Q=FAKE + 2) == 5
+
+
 def test_som_validation(L):
     F = ctypes.c_float
     assert L.vs_som_update_workspace(0, 4, 8) == 0

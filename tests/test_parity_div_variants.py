@@ -359,3 +359,27 @@ def test_run_gram_matches_steps(centroid):
     assert torch.equal(m1, m2)
     if centroid:
         assert torch.equal(R1, R2)
+
+
+def test_run_ref_matches_steps(div_kernel):
+    """vs_diversity_run_ref equals the step_ref / accumulate chain bit for bit."""
+    n, d, nseq, steps = 500, 64, 100, 15
+    C = synth.dense_case(1, n, d, "unit", key=4200)[1]
+    (r,) = synth.rng_children(4201, 1)
+    seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+    Cd = T(C)
+    Q1 = Cd[T(seeds).long()].contiguous()
+    m1 = T(seed_masks(n, seeds).view(np.int32))
+    p1 = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    s1 = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    for t in range(steps):
+        vs.vs_diversity_step_ref(Cd, Q1, m1, idx_out=p1[t], score_out=s1[t])
+        vs.vs_diversity_accumulate(Cd, p1[t], Q1)
+    m2 = T(seed_masks(n, seeds).view(np.int32))
+    Q2 = torch.full((nseq, d), 3.0, dtype=torch.float32, device=dev())  # overwritten by the call
+    p2, s2, Q2 = vs.vs_diversity_run_ref(Cd, T(seeds), m2, steps, Q=Q2)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(m1, m2)
+    assert torch.equal(Q1.view(torch.int32), Q2.view(torch.int32))
