@@ -325,19 +325,37 @@ def setup_som(k, torch, vs, a):
         ws_u = torch.empty(L.vs_som_update_workspace(rows, cols, d), dtype=torch.uint8,
                            device=dev)
 
-        def step():
-            vs.vs_som_epoch_csr(indptr, indices, values, CB, (rows, cols), d, sig, R,
-                                bmu_out=bmu, score_out=score, qe_out=qe, workspace=ws)
-        phases["search"] = lambda: vs.vs_bmu_search_csr_blocked(
-            indptr, indices, values, CB, nc, 0, d=d, idx_out=bmu, score_out=score,
-            workspace=ws_s)
+        if a.csr_storage == "f16":
+            # the search runs over an fp16 copy remade from the fp32 codebook
+            # each epoch; the update keeps the fp32 weights
+            CB16 = torch.empty(L.vs_csr_blocked_f16_bytes(nc, d) // 2, dtype=torch.float16,
+                               device=dev)
+
+            def step():
+                vs.vs_som_epoch_csr_f16(indptr, indices, values, CB, (rows, cols), d, sig, R,
+                                        CB16=CB16, bmu_out=bmu, score_out=score, qe_out=qe,
+                                        workspace=ws)
+
+            def search_phase():
+                vs.vs_csr_blocked_to_f16(CB, nc, d, out=CB16)
+                vs.vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, 0, d=d,
+                                                 idx_out=bmu, score_out=score, workspace=ws_s)
+            phases["search"] = search_phase
+        else:
+            def step():
+                vs.vs_som_epoch_csr(indptr, indices, values, CB, (rows, cols), d, sig, R,
+                                    bmu_out=bmu, score_out=score, qe_out=qe, workspace=ws)
+            phases["search"] = lambda: vs.vs_bmu_search_csr_blocked(
+                indptr, indices, values, CB, nc, 0, d=d, idx_out=bmu, score_out=score,
+                workspace=ws_s)
         phases["update"] = lambda: vs.vs_som_update_csr(indptr, indices, values, bmu, CB,
                                                         (rows, cols), d, sig, R, workspace=ws_u)
         w["nnz"] = int(w["indices"].shape[0])
-        w["value_bytes"] = 4
+        f16 = a.csr_storage == "f16"
+        w["value_bytes"] = 2 if f16 else 4
         in_bytes = w["nnz"] * 8 + (nq + 1) * 4
         flops = 2.0 * w["nnz"] * nc
-        chunks = (nc + 63) // 64
+        chunks = (nc + (127 if f16 else 63)) // (128 if f16 else 64)
         launches = (chunks + min(8, chunks) - 1) // min(8, chunks)
     phases["qe"] = lambda: vs.vs_som_qe(score, qe_out=qe)
     # the update's algorithmic HBM bytes: read the inputs and their BMUs once,
@@ -349,7 +367,7 @@ def setup_som(k, torch, vs, a):
                sigma=sig, radius=R, metric="l2sq_min",
                update="batch map, Gaussian in a square window, separable passes")
     if w["kind"] == "csr":
-        cfg.update(nnz=w["nnz"], codebook_layout="blocked")
+        cfg.update(nnz=w["nnz"], codebook_layout="blocked", codebook_storage=a.csr_storage)
     return w, step, nq * nc, flops, launches, cfg
 
 

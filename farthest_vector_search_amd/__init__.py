@@ -46,7 +46,7 @@ EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
            "vs_diversity_gram", "vs_diversity_step_gram", "vs_diversity_step_gram_sum",
            "vs_som_update_workspace", "vs_som_update", "vs_som_update_csr", "vs_som_qe",
            "vs_som_epoch_workspace", "vs_som_epoch", "vs_som_epoch_csr_workspace",
-           "vs_som_epoch_csr",
+           "vs_som_epoch_csr", "vs_som_epoch_csr_f16", "vs_csr_blocked_to_f16",
            "vs_candidate_norms", "vs_tile_rows", "vs_timing_enable", "vs_timing_read",
            "vs_timing_kernel_name", "vs_status_str", "vs_last_hip_error", "vs_version"]
 
@@ -113,6 +113,9 @@ def lib() -> ctypes.CDLL:
     L.vs_som_epoch_csr_workspace.restype = SZ
     L.vs_som_epoch_csr.argtypes = [P, P, P, I64, I64, P, I32, I32, I32, F, I32, P, P, P, P, SZ,
                                    P]
+    L.vs_csr_blocked_to_f16.argtypes = [P, I64, I32, P, P]
+    L.vs_som_epoch_csr_f16.argtypes = [P, P, P, I64, I64, P, P, I32, I32, I32, F, I32, P, P, P,
+                                       P, SZ, P]
     L.vs_candidate_norms.argtypes = [P, I64, I32, I32, P, P]
     L.vs_tile_rows.argtypes = [I64, I32, I32]
     L.vs_tile_rows.restype = I64
@@ -130,7 +133,8 @@ def lib() -> ctypes.CDLL:
                  "vs_diversity_step_gram_sum", "vs_diversity_run", "vs_diversity_run_gram",
                  "vs_diversity_run_ref",
                  "vs_som_update", "vs_som_update_csr", "vs_som_qe",
-                 "vs_som_epoch", "vs_som_epoch_csr",
+                 "vs_som_epoch", "vs_som_epoch_csr", "vs_som_epoch_csr_f16",
+                 "vs_csr_blocked_to_f16",
                  "vs_candidate_norms", "vs_timing_enable", "vs_timing_read",
                  "vs_last_hip_error"):
         getattr(L, name).restype = ctypes.c_int
@@ -799,6 +803,54 @@ def vs_som_epoch_csr(indptr, indices, values, CB, map_shape, d: int, sigma: floa
                                 _ptr(qe_out), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(dev))
     _check(rc, "vs_som_epoch_csr")
+    return bmu_out, score_out, qe_out
+
+
+def vs_csr_blocked_to_f16(CB, nc: int, d: int, out=None):
+    """The fp16 128-neuron blocked copy of a 64-neuron blocked fp32 codebook."""
+    torch = _torch()
+    L = lib()
+    _dev(CB, "CB", torch.float32, 1)
+    if CB.numel() < ((nc + 63) // 64) * 64 * d:
+        raise ValueError("CB is smaller than the blocked layout of nc x d")
+    if out is None:
+        out = torch.empty(L.vs_csr_blocked_f16_bytes(nc, d) // 2, dtype=torch.float16,
+                          device=CB.device)
+    with torch.cuda.device(CB.device):
+        rc = L.vs_csr_blocked_to_f16(_ptr(CB), nc, d, _ptr(out), _stream(CB.device))
+    _check(rc, "vs_csr_blocked_to_f16")
+    return out
+
+
+def vs_som_epoch_csr_f16(indptr, indices, values, CB, map_shape, d: int, sigma: float,
+                         radius: int, CB16=None, bmu_out=None, score_out=None, qe_out=None,
+                         workspace=None):
+    """One SOM epoch on CSR rows searching an fp16 copy (CB16) of the fp32
+    blocked codebook CB, updating CB in place.  Returns (bmu, score, qe)."""
+    torch = _torch()
+    L = lib()
+    n, nnz = _csr_args(indptr, indices, values)
+    _dev(CB, "CB", torch.float32, 1)
+    rows, cols = (int(v) for v in map_shape)
+    nc = rows * cols
+    if CB.numel() < ((nc + 63) // 64) * 64 * d:
+        raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
+    dev = CB.device
+    if CB16 is None:
+        CB16 = torch.empty(L.vs_csr_blocked_f16_bytes(nc, d) // 2, dtype=torch.float16,
+                           device=dev)
+    bmu_out = torch.empty(max(n, 0), dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
+    score_out = (torch.empty(max(n, 0), dtype=torch.float32, device=dev) if score_out is None
+                 else score_out)
+    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
+    with torch.cuda.device(dev):
+        rc = L.vs_som_epoch_csr_f16(_ptr(indptr), _ptr(indices) if nnz else None,
+                                    _ptr(values) if nnz else None, n, nnz, _ptr(CB), _ptr(CB16),
+                                    rows, cols, d, float(sigma), int(radius), _ptr(bmu_out),
+                                    _ptr(score_out), _ptr(qe_out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "vs_som_epoch_csr_f16")
     return bmu_out, score_out, qe_out
 
 

@@ -393,6 +393,18 @@ VS_API int vs_csr_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, 
     return VS_OK;
 }
 
+VS_API int vs_csr_blocked_to_f16(const float *CB, int64_t nc, int32_t d, uint16_t *CB16,
+                                 void *stream) {
+    if (nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxIndex) return VS_ERR_SHAPE;
+    if (!CB || !CB16) return VS_ERR_NULL;
+    if (!al4(CB) || (reinterpret_cast<uintptr_t>(CB16) & 15) != 0) return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    VS_TRY_HIP(vs::launch_block_codebook_f16(CB, nc, 64, d, CB16,
+                                             reinterpret_cast<hipStream_t>(stream), true));
+    return VS_OK;
+}
+
 VS_API int vs_bmu_search_csr_blocked_f16(const int32_t *indptr, const int32_t *indices,
                                          const float *values, int64_t nq, int64_t nnz,
                                          const uint16_t *CB16, int64_t nc, int32_t d,
@@ -836,6 +848,33 @@ VS_API int vs_som_epoch_csr(const int32_t *indptr, const int32_t *indices, const
     if (const int s = vs_bmu_search_csr_blocked(indptr, indices, values, n, nnz, CB, nc, d,
                                                 vs::L2SQ_MIN, bmu_out, score_out, ws, ws1,
                                                 stream))
+        return s;
+    if (qe_out)
+        if (const int s = vs_som_qe(score_out, n, qe_out, stream)) return s;
+    return vs_som_update_csr(indptr, indices, values, n, nnz, bmu_out, CB, map_rows, map_cols, d,
+                             sigma, radius, ws + ws1, workspace_bytes - ws1, stream);
+}
+
+VS_API int vs_som_epoch_csr_f16(const int32_t *indptr, const int32_t *indices,
+                                const float *values, int64_t n, int64_t nnz, float *CB,
+                                uint16_t *CB16, int32_t map_rows, int32_t map_cols, int32_t d,
+                                float sigma, int32_t radius, int32_t *bmu_out, float *score_out,
+                                double *qe_out, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    int32_t R = 0;
+    if (const int s = som_params(map_rows, map_cols, d, sigma, radius, &R)) return s;
+    if (n < 0 || n > kMaxIndex || nnz < 0 || nnz > kMaxIndex) return VS_ERR_SHAPE;
+    if (!CB || !CB16 || !workspace || (n > 0 && (!bmu_out || !score_out))) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(qe_out) & 7) != 0) return VS_ERR_ALIGN;
+    const size_t need = vs_som_epoch_csr_workspace(n, map_rows, map_cols, d);
+    if (workspace_bytes < need) return VS_ERR_WORKSPACE;
+    const int64_t nc = (int64_t)map_rows * map_cols;
+    const size_t ws1 = up256(csr_layout(n, nc).total);
+    char *ws = static_cast<char *>(workspace);
+    if (const int s = vs_csr_blocked_to_f16(CB, nc, d, CB16, stream)) return s;
+    if (const int s = vs_bmu_search_csr_blocked_f16(indptr, indices, values, n, nnz, CB16, nc, d,
+                                                    vs::L2SQ_MIN, bmu_out, score_out, ws, ws1,
+                                                    stream))
         return s;
     if (qe_out)
         if (const int s = vs_som_qe(score_out, n, qe_out, stream)) return s;

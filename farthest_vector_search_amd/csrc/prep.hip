@@ -215,6 +215,10 @@ hipError_t launch_col_sqnorms_f16(const uint16_t *X, int64_t cols, int32_t d, fl
 // 128-column blocked fp16 copy of a feature-major fp32 codebook: CB[b][k][j]
 // = fp16(CT[k * ldct + 128 b + j]) (round to nearest even) for 128 b + j < nc,
 // 0 past nc.  One thread per value.
+// SRC64: the source is the 64-neuron blocked fp32 layout (feature k of
+// neuron n at CT[(n / 64) * 64 d + k * 64 + n % 64]) instead of the plain
+// feature-major one; the fp16 values are the same roundings either way.
+template <bool SRC64>
 __global__ __launch_bounds__(256) void k_block_codebook_f16(const float *__restrict__ CT, int64_t nc,
                                                            int64_t ldct, int32_t d, int64_t total,
                                                            _Float16 *__restrict__ CB) {
@@ -222,17 +226,22 @@ __global__ __launch_bounds__(256) void k_block_codebook_f16(const float *__restr
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const int64_t j = e & 127, k = (e >> 7) % d, b = (e >> 7) / d;
         const int64_t n = b * 128 + j;
-        CB[e] = n < nc ? (_Float16)CT[k * ldct + n] : (_Float16)0.0f;
+        const int64_t src = SRC64 ? (n >> 6) * 64 * (int64_t)d + k * 64 + (n & 63) : k * ldct + n;
+        CB[e] = n < nc ? (_Float16)CT[src] : (_Float16)0.0f;
     }
 }
 
 hipError_t launch_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
-                                     uint16_t *CB, hipStream_t st) {
+                                     uint16_t *CB, hipStream_t st, bool src_blocked64) {
     const int64_t total = (nc + 127) / 128 * 128 * (int64_t)d;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_block_codebook_f16, dim3((unsigned)blocks), dim3(256), 0, st, CT, nc,
-                       ldct, d, total, reinterpret_cast<_Float16 *>(CB));
+    if (src_blocked64)
+        hipLaunchKernelGGL(k_block_codebook_f16<true>, dim3((unsigned)blocks), dim3(256), 0, st, CT,
+                           nc, ldct, d, total, reinterpret_cast<_Float16 *>(CB));
+    else
+        hipLaunchKernelGGL(k_block_codebook_f16<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           CT, nc, ldct, d, total, reinterpret_cast<_Float16 *>(CB));
     return hipGetLastError();
 }
 

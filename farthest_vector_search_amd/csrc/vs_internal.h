@@ -131,9 +131,10 @@ hipError_t launch_col_sqnorms(const float *X, int64_t cols, int64_t ld, int64_t 
 hipError_t launch_block_codebook(const float *CT, int64_t nc, int64_t ldct, int32_t d, float *CB,
                                  hipStream_t st);
 // fp16 codebook, 128-neuron blocks: feature k of neuron 128 b + j at
-// CB[(b * d + k) * 128 + j]
+// CB[(b * d + k) * 128 + j]; from the plain feature-major CT, or (when
+// src_blocked64) from the 64-neuron blocked fp32 layout
 hipError_t launch_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
-                                     uint16_t *CB, hipStream_t st);
+                                     uint16_t *CB, hipStream_t st, bool src_blocked64 = false);
 hipError_t launch_col_sqnorms_f16(const uint16_t *X, int64_t cols, int32_t d, float *out,
                                   hipStream_t st);
 hipError_t launch_csr_row_sqnorms(const int32_t *indptr, const float *values, int64_t nq,

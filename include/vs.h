@@ -179,6 +179,14 @@ int vs_bmu_search_csr_blocked(const int32_t *indptr, const int32_t *indices,
 size_t vs_csr_blocked_f16_bytes(int64_t nc, int32_t d);
 int vs_csr_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
                               uint16_t *CB16, void *stream);
+/*
+ * The same fp16 128-neuron blocked copy, made from the 64-neuron blocked fp32
+ * codebook CB (the layout vs_csr_block_codebook writes and the SOM update
+ * keeps) instead of the plain feature-major one: bit-identical to
+ * vs_csr_block_codebook_f16 of the same values.  CB16 16-byte aligned,
+ * vs_csr_blocked_f16_bytes(nc, d) bytes.
+ */
+int vs_csr_blocked_to_f16(const float *CB, int64_t nc, int32_t d, uint16_t *CB16, void *stream);
 int vs_bmu_search_csr_blocked_f16(const int32_t *indptr, const int32_t *indices,
                                   const float *values, int64_t nq, int64_t nnz,
                                   const uint16_t *CB16, int64_t nc, int32_t d, int32_t metric,
@@ -367,6 +375,22 @@ int vs_som_epoch_csr(const int32_t *indptr, const int32_t *indices, const float 
                      int64_t n, int64_t nnz, float *CB, int32_t map_rows, int32_t map_cols,
                      int32_t d, float sigma, int32_t radius, int32_t *bmu_out, float *score_out,
                      double *qe_out, void *workspace, size_t workspace_bytes, void *stream);
+/*
+ *   vs_som_epoch_csr_f16  the CSR epoch with the search over an fp16 copy of
+ *                      the codebook [Issue "FP16 storage (compounding
+ *                      optimization)": load half, compute fp32]:
+ *                      vs_csr_blocked_to_f16 of CB into CB16 (caller-owned,
+ *                      vs_csr_blocked_f16_bytes), vs_bmu_search_csr_blocked_f16,
+ *                      vs_som_qe, then vs_som_update_csr of the fp32 CB.  BMUs
+ *                      and the error are those of the fp16-rounded codebook;
+ *                      the update keeps full fp32 weights.  Workspace as
+ *                      vs_som_epoch_csr.
+ */
+int vs_som_epoch_csr_f16(const int32_t *indptr, const int32_t *indices, const float *values,
+                         int64_t n, int64_t nnz, float *CB, uint16_t *CB16, int32_t map_rows,
+                         int32_t map_cols, int32_t d, float sigma, int32_t radius,
+                         int32_t *bmu_out, float *score_out, double *qe_out, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * Squared L2 norms of candidates, float32, fixed summation order (the same

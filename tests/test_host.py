@@ -284,6 +284,25 @@ def test_diversity_run_ref_validation(L):
     assert run(Q=FAKE + 2) == 5
 
 
+def test_fp16_epoch_validation(L):
+    F = ctypes.c_float
+    assert L.vs_csr_blocked_to_f16(_P(FAKE), 0, 8, _P(FAKE), None) == 2
+    assert L.vs_csr_blocked_to_f16(_P(FAKE), 10, 0, _P(FAKE), None) == 2
+    assert L.vs_csr_blocked_to_f16(None, 10, 8, _P(FAKE), None) == 1
+    assert L.vs_csr_blocked_to_f16(_P(FAKE), 10, 8, _P(FAKE + 8), None) == 5
+
+    def ep(indptr=FAKE, indices=FAKE, values=FAKE, n=10, nnz=30, CB=FAKE, CB16=FAKE, rows=4,
+           cols=4, d=8, sigma=1.0, R=2, bmu=FAKE, score=FAKE, qe=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return L.vs_som_epoch_csr_f16(_P(indptr), _P(indices), _P(values), n, nnz, _P(CB),
+                                      _P(CB16), rows, cols, d, F(sigma), R, _P(bmu), _P(score),
+                                      _P(qe), _P(ws), ws_bytes, None)
+    assert ep(R=-1) == 2
+    assert ep(CB16=0) == 1
+    assert ep(CB=0) == 1
+    assert ep(qe=FAKE + 4) == 5
+    assert ep(ws_bytes=10) == 4
+
+
 def test_som_validation(L):
     F = ctypes.c_float
     assert L.vs_som_update_workspace(0, 4, 8) == 0

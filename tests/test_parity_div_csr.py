@@ -420,6 +420,20 @@ def f16_rounded(CT):
     return CT.astype(np.float16).astype(np.float32)
 
 
+@pytest.mark.parametrize("nc", [1, 63, 100, 128, 300, 1030])
+def test_csr_blocked_to_f16_equals_plain(nc):
+    """The fp16 copy made from the 64-neuron blocked fp32 codebook equals,
+    bit for bit, the one made from the plain feature-major codebook."""
+    d = 41
+    (r,) = synth.rng_children(4300 + nc, 1)
+    CT = synth.uniform01(r, (d, nc))
+    a = vs.vs_csr_block_codebook_f16(T(CT))
+    b = vs.vs_csr_blocked_to_f16(vs.vs_csr_block_codebook(T(CT)), nc, d)
+    torch.cuda.synchronize()
+    assert a.numel() == b.numel()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 @pytest.mark.parametrize("nc,pad", [(1, 0), (100, 0), (128, 0), (300, 5), (1030, 0)])
 def test_csr_block_codebook_f16_layout(nc, pad):
     """The fp16 blocked copy holds fp16(feature k of neuron 128 b + j) at

@@ -270,6 +270,47 @@ def test_som_epoch_csr(rows, cols, d, n, sigma, R, density):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("rows,cols,d,n,sigma,R,density", [
+    (8, 16, 200, 300, 1.5, 4, 0.05),
+    (5, 27, 77, 150, 1.0, 2, 0.25),
+])
+def test_som_epoch_csr_f16(rows, cols, d, n, sigma, R, density):
+    """The epoch searching an fp16 copy: BMUs and the error are those of the
+    fp16-rounded codebook (checked against the oracle on the rounded
+    codebook); the update applies to the fp32 weights (checked against the
+    oracle's update of the fp32 codebook with the oracle's BMUs)."""
+    nc = rows * cols
+    (r,) = synth.rng_children(1300 + nc, 1)
+    indptr, indices, values = synth.sparse_rows(r, n, d, density)
+    assert (np.diff(indptr) > 0).all()
+    CT = synth.uniform01(r, (d, nc))
+    synth.normalize_columns(CT)
+    CB = vs.vs_csr_block_codebook(T(CT))
+    bmu, score, qe = vs.vs_som_epoch_csr_f16(T(indptr), T(indices), T(values), CB, (rows, cols),
+                                             d, sigma, R)
+    torch.cuda.synchronize()
+    g_bmu, g_score, g_qe = bmu.cpu().numpy(), score.cpu().numpy(), qe.cpu().numpy()[0]
+    w_gpu = unblock(CB.cpu().numpy(), nc, d)
+    C_old = np.ascontiguousarray(CT.T)
+    CT16 = CT.astype(np.float16).astype(np.float32)  # the rounded codebook, exact in fp32
+    C16 = np.ascontiguousarray(CT16.T)
+    o_idx, o_val, o_gap = oracle.csr(indptr, indices, values, CT16, 0, threads=8)
+    Xd = np.zeros((n, d), np.float32)
+    for i in range(n):
+        Xd[i, indices[indptr[i]:indptr[i + 1]]] = values[indptr[i]:indptr[i + 1]]
+    floor = l2_floor(Xd, C16, o_idx)
+    fails, _ = check(g_bmu, g_score, o_idx, o_val, o_gap, 0, floor,
+                     lambda r_, c: oracle.pair_values(Xd, C16, 0, r_, c))
+    assert not fails, fails
+    assert abs(g_qe - oracle.mean_sqrt(o_val)) <= qe_bound(o_val, floor) + 1e-12
+    sel = clean_neurons(g_bmu, o_idx, rows, cols, R)
+    assert sel.size >= nc // 2
+    w_o, mass, den = oracle.som_update(indptr, indices, values, d, o_idx, C_old, rows, cols,
+                                       float(np.float32(sigma)), R, neurons=sel, threads=8)
+    bad = check_update(w_gpu[sel], C_old[sel], w_o, mass, den, o_idx, rows, cols, R)
+    assert not bad, bad
+
+
 def test_som_epoch_no_inputs():
     rows, cols, d = 4, 4, 8
     _, C = dense_inputs(1, rows, cols, d, key=1300)
