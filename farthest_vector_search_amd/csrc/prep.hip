@@ -231,9 +231,49 @@ __global__ __launch_bounds__(256) void k_block_codebook_f16(const float *__restr
     }
 }
 
+// Four neurons per thread: one 16-byte load of four consecutive neurons'
+// values (they are contiguous in both source layouts, which the launcher
+// checks for the plain one) and one 8-byte store of their halves.
+template <bool SRC64>
+__global__ __launch_bounds__(256) void k_block_codebook_f16_x4(const float *__restrict__ CT,
+                                                              int64_t nc, int64_t ldct, int32_t d,
+                                                              int64_t total4,
+                                                              _Float16 *__restrict__ CB) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e4 < total4; e4 += stride) {
+        const int64_t j = (e4 & 31) * 4, bk = e4 >> 5;
+        const int64_t k = bk % d, b = bk / d;
+        const int64_t n = b * 128 + j;
+        f16x4 h = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+        if (n < nc) {  // nc % 4 == 0: all four neurons exist
+            const int64_t src =
+                SRC64 ? (n >> 6) * 64 * (int64_t)d + k * 64 + (n & 63) : k * ldct + n;
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(CT + src);
+            h = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        }
+        *reinterpret_cast<f16x4 *>(CB + e4 * 4) = h;
+    }
+}
+
 hipError_t launch_block_codebook_f16(const float *CT, int64_t nc, int64_t ldct, int32_t d,
                                      uint16_t *CB, hipStream_t st, bool src_blocked64) {
     const int64_t total = (nc + 127) / 128 * 128 * (int64_t)d;
+    const bool vec = nc % 4 == 0 && (src_blocked64 || ldct % 4 == 0) &&
+                     ((reinterpret_cast<uintptr_t>(CT) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(CB) & 7) == 0);
+    if (vec) {
+        int64_t blocks = (total / 4 + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        if (src_blocked64)
+            hipLaunchKernelGGL(k_block_codebook_f16_x4<true>, dim3((unsigned)blocks), dim3(256), 0,
+                               st, CT, nc, ldct, d, total / 4, reinterpret_cast<_Float16 *>(CB));
+        else
+            hipLaunchKernelGGL(k_block_codebook_f16_x4<false>, dim3((unsigned)blocks), dim3(256), 0,
+                               st, CT, nc, ldct, d, total / 4, reinterpret_cast<_Float16 *>(CB));
+        return hipGetLastError();
+    }
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (src_blocked64)
