@@ -26,6 +26,8 @@
 // dot product therefore runs over one fixed feature order.
 #include "vs_internal.h"
 
+#include <type_traits>
+
 namespace vs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -100,7 +102,8 @@ void k_bmu_qreg(const DenseArgs a) {
     if (it0 >= it1) return;
 
     const int32_t d = a.d;
-    const int64_t nq = a.nq, nc = a.nc, nct = a.n_ctiles;
+    const int64_t nq = a.nq, nc = a.nc;
+    const int32_t nct = (int32_t)a.n_ctiles;  // nc < 2^31 rows
 
     f32x4 qreg[NCH];
     auto load_queries = [&](int64_t qt) {
@@ -113,35 +116,51 @@ void k_bmu_qreg(const DenseArgs a) {
     // ---- candidate slab loader ----------------------------------------
     // VEC: direct-to-LDS.  Wave w fills rows [RPW w, RPW w + RPW); one
     // instruction covers RPI rows x kPieces slots, lane l -> row +l/kPieces,
-    // slot l%kPieces, which holds piece slot ^ (row % 16) of that row.  Elements outside the
-    // table (rows >= nc, features >= d) are written as zeros with ds_write.
+    // slot l%kPieces, which holds piece slot ^ (row % 16) of that row.  The
+    // source of each lane is fixed per candidate tile (a 32-bit element
+    // offset from the tile's first row, kept in voff); a slab only moves the
+    // tile's base.  Rows past nc re-read row nc - 1 (their results are
+    // discarded); features >= d are written as zeros with ds_write.
     // Scalar path: through registers, as in the tiled kernel.
     const int lrow = tid / kPieces, lpiece = tid % kPieces;
     const float *aptr[AP];
     f32x4 ra[AP];
-    int64_t row_base = 0;  // first candidate of the item being loaded
-    auto set_rows = [&](int64_t item) {
-        row_base = (item % nct) * kBC;
-        if constexpr (!VEC) {
+    uint32_t voff[RPW / RPI];
+    int32_t dpiece[RPW / RPI];  // 4 x the piece this lane loads
+    int32_t row_base = 0;       // first candidate of the tile being loaded
+    auto set_rows = [&](int32_t ctile) {
+        row_base = ctile * kBC;
+        if constexpr (VEC) {
+            const int32_t last = (int32_t)(nc - row_base) - 1;  // last row of the tile inside C
+#pragma unroll
+            for (int i = 0; i < RPW / RPI; ++i) {
+                const int row = wave * RPW + RPI * i + lane / kPieces;
+                const int piece = (lane % kPieces) ^ (row & 15);
+                dpiece[i] = 4 * piece;
+                voff[i] = (uint32_t)((row < last ? row : last) * d + 4 * piece);
+            }
+        } else {
 #pragma unroll
             for (int i = 0; i < AP; ++i) {
-                const int64_t c = row_base + lrow + i * RPP;
+                const int64_t c = (int64_t)row_base + lrow + i * RPP;
                 aptr[i] = c < nc ? a.C + c * d : nullptr;
             }
         }
     };
     auto load_slab = [&](int slab, int buf) {
         if constexpr (VEC) {
+            const float *tile = a.C + (int64_t)row_base * d + slab * kBK;
+            if ((slab + 1) * kBK <= d) {  // uniform: no feature past d
 #pragma unroll
-            for (int i = 0; i < RPW / RPI; ++i) {
-                const int row = wave * RPW + RPI * i + lane / kPieces;
-                const int slot = lane % kPieces;
-                const int piece = slot ^ (row & 15);
-                const int64_t c = row_base + row;
-                const int32_t k = slab * kBK + 4 * piece;
-                float *dst = &sA[buf][(wave * RPW + RPI * i) * kBK];
-                if (c < nc && k < d) dma16(a.C + c * d + k, dst);
-                else *reinterpret_cast<f32x4 *>(dst + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int i = 0; i < RPW / RPI; ++i)
+                    dma16(tile + voff[i], &sA[buf][(wave * RPW + RPI * i) * kBK]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < RPW / RPI; ++i) {
+                    float *dst = &sA[buf][(wave * RPW + RPI * i) * kBK];
+                    if (dpiece[i] < d - slab * kBK) dma16(tile + voff[i], dst);
+                    else *reinterpret_cast<f32x4 *>(dst + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
             }
         } else {
             const int32_t k = slab * kBK + 4 * lpiece;
@@ -156,10 +175,10 @@ void k_bmu_qreg(const DenseArgs a) {
                 *reinterpret_cast<f32x4 *>(&sA[buf][slab_at(lrow + i * RPP, lpiece)]) = ra[i];
         }
     };
-    auto load_norms = [&](int par) {  // wave 0: the item's 64 candidate norms
+    auto load_norms = [&](int par) {  // wave 0: the tile's 64 candidate norms
         if constexpr (metric_is_l2(M)) {
             if (wave == 0) {
-                const int64_t c = row_base + lane;
+                const int64_t c = (int64_t)row_base + lane;
                 if constexpr (VEC) {
                     if (c < nc) dma4(a.cn + c, &sN[par][0]);
                     else sN[par][lane] = 0.0f;
@@ -179,18 +198,31 @@ void k_bmu_qreg(const DenseArgs a) {
 
     // Accumulator register r of a lane = candidate row 8*(r/4)+4h+(r%4) of
     // its 32-row block, query column l32; rows rise with r and tiles are
-    // visited in ascending order, so strict "<" keeps the lowest index.
-    auto epilogue = [&](int64_t item, int par) {
-        const int64_t base = (item % nct) * kBC;
+    // visited in ascending order.  A tile first reduces to its own best
+    // (strict "<" over rising rows keeps the lowest row among equal values),
+    // which replaces the running best only when strictly lower, so the
+    // lowest index wins ties across tiles too.
+    // The norms of this lane's 32 rows of the tile (L2 metrics), read from
+    // LDS ahead of the epilogue so that their latency is hidden.
+    f32x4 cnr[8];
+    auto read_norms = [&](int par) {
+        if constexpr (metric_is_l2(M)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                cnr[j] = *reinterpret_cast<const f32x4 *>(&sN[par][(j >> 2) * 32 + 8 * (j & 3) + 4 * h]);
+        }
+    };
+    auto epilogue = [&](int64_t qtile, int32_t ctile) {
+        const int32_t base = ctile * kBC;  // < nc < 2^31
         if constexpr (M == kStoreDots) {
             // S[q][c] for this lane's query column; register quad r4 holds
             // rows 8 r4 + 4h .. + 3 of each 32-row block
-            const int64_t q = (item / nct) * kBQ + wave * 32 + l32;
+            const int64_t q = qtile * kBQ + wave * 32 + l32;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int64_t c = base + cb * 32 + 8 * r4 + 4 * h;
+                    const int64_t c = (int64_t)base + cb * 32 + 8 * r4 + 4 * h;
                     if (q < nq && c < nc) {
                         float *dst = a.S + q * a.ld_s + c;
                         const f32x4 v = {acc[cb][4 * r4], acc[cb][4 * r4 + 1],
@@ -206,28 +238,38 @@ void k_bmu_qreg(const DenseArgs a) {
             }
             return;
         }
+        // rows r + 4h < live exist (all of them unless this is C's last tile)
+        const int32_t live = (int32_t)(nc - base < kBC ? nc - base : kBC) - 4 * h;
+        float tb = __builtin_inff();
+        int32_t tr = 0;
+        auto scan = [&](auto check_rows) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int row0 = cb * 32 + 8 * r4 + 4 * h;
-                f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (metric_is_l2(M))
-                    cn4 = *reinterpret_cast<const f32x4 *>(&sN[par][row0]);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (metric_is_l2(M)) cn4 = cnr[4 * cb + r4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t c = base + row0 + e;
-                    const float v = rank_value<M>(acc[cb][4 * r4 + e], cn4[e]);
-                    if (c < nc && v < best) {
-                        best = v;
-                        bidx = (int32_t)c;
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = cb * 32 + 8 * r4 + e;  // row in the tile, less 4h
+                        const float v = rank_value<M>(acc[cb][4 * r4 + e], cn4[e]);
+                        bool lt = v < tb;
+                        if constexpr (decltype(check_rows)::value) lt = lt && r < live;
+                        tb = lt ? v : tb;
+                        tr = lt ? r : tr;
                     }
                 }
+                acc[cb] = f32x16{};
             }
-            acc[cb] = f32x16{};
+        };
+        if ((int64_t)base + kBC <= nc) scan(std::false_type{});  // uniform
+        else scan(std::true_type{});
+        if (tb < best) {
+            best = tb;
+            bidx = base + 4 * h + tr;
         }
     };
-    auto flush = [&](int64_t qt) {
+    auto flush = [&](int64_t qtile) {
         if constexpr (M == kStoreDots) return;
         const float oe = __shfl_xor(best, 32);
         const int32_t oi = __shfl_xor(bidx, 32);
@@ -235,7 +277,7 @@ void k_bmu_qreg(const DenseArgs a) {
             best = oe;
             bidx = oi;
         }
-        const int64_t q = qt * kBQ + wave * 32 + l32;
+        const int64_t q = qtile * kBQ + wave * 32 + l32;
         if (h == 0 && bidx >= 0 && q < nq)
             atomicMin(reinterpret_cast<unsigned long long *>(a.keys + q),
                       (unsigned long long)pack_key(best, (uint32_t)bidx));
@@ -243,16 +285,42 @@ void k_bmu_qreg(const DenseArgs a) {
         bidx = -1;
     };
 
+    // (query tile, candidate tile) of the item being computed; items are
+    // visited candidate-tile major inside a query tile
     int64_t qt = it0 / nct;
+    int32_t ct = (int32_t)(it0 - qt * nct);
     load_queries(qt);
-    set_rows(it0);
+    set_rows(ct);
     load_slab(0, 0);
     load_norms(0);
     finish_slab(0);
     wait_loads();
     __syncthreads();
     int buf = 0, par = 0;
+    // With two or more slabs per item, the last chunk of each slab is held
+    // in registers across the slab's barrier: after the barrier a wave first
+    // reads the next slab's first operands, then issues the held MFMAs (and
+    // at an item's end its epilogue), so the pipe has work while the barrier
+    // resolves and the reads land.  The held epilogue reads norms slot par
+    // after the barrier; that slot is reloaded two items later, behind at
+    // least one more barrier when NSLAB >= 2.
+    constexpr bool HOLD = NSLAB >= 2;
+    auto mfma_chunk = [&](const f32x4 &x0, const f32x4 &x1, const f32x4 &qv) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0[e], qv[e], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1[e], qv[e], acc[1], 0, 0, 0);
+        }
+    };
+    f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sA[0][slab_at(l32, h)]);
+    f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sA[0][slab_at(32 + l32, h)]);
     for (int64_t item = it0; item < it1; ++item) {
+        int64_t nqt = qt;
+        int32_t nctile = ct + 1;
+        if (nctile == nct) {
+            nctile = 0;
+            ++nqt;
+        }
 #pragma unroll
         for (int s = 0; s < NSLAB; ++s) {
             bool has_next = true;
@@ -261,49 +329,67 @@ void k_bmu_qreg(const DenseArgs a) {
             } else {
                 has_next = item + 1 < it1;
                 if (has_next) {
-                    set_rows(item + 1);
+                    set_rows(nctile);
                     load_slab(0, buf ^ 1);
                     load_norms(par ^ 1);
                 }
             }
             // 8 chunks of 8 features; the operands of chunk cc+1 are read
-            // from LDS while the MFMAs of chunk cc run
+            // from LDS before the MFMAs of chunk cc are issued (the
+            // scheduling barriers keep the compiler from sinking the reads
+            // behind the MFMAs, where their latency would be exposed)
             if constexpr (VS_QREG_PRIO) __builtin_amdgcn_s_setprio(1);
             const float *A = sA[buf];
-            f32x4 f0[2], f1[2];
-            f0[0] = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, h)]);
-            f1[0] = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, h)]);
+            if constexpr (!HOLD) {
+                a0 = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, h)]);
+                a1 = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, h)]);
+            }
 #pragma unroll
             for (int cc = 0; cc < kCPS; ++cc) {
+                // this chunk's operands have landed (LDS reads complete in order)
+                asm volatile("" ::"v"(a0), "v"(a1));
+                if (HOLD && cc == kCPS - 1) continue;  // held: issued after the barrier
+                f32x4 n0 = a0, n1 = a1;
                 if (cc + 1 < kCPS) {
                     const int piece = 2 * (cc + 1) + h;
-                    f0[(cc + 1) & 1] = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, piece)]);
-                    f1[(cc + 1) & 1] = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, piece)]);
+                    n0 = *reinterpret_cast<const f32x4 *>(&A[slab_at(l32, piece)]);
+                    n1 = *reinterpret_cast<const f32x4 *>(&A[slab_at(32 + l32, piece)]);
                 }
-                const f32x4 a0 = f0[cc & 1], a1 = f1[cc & 1];
-                const f32x4 qv = qreg[s * kCPS + cc];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[e], qv[e], acc[0], 0, 0, 0);
-                    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], qv[e], acc[1], 0, 0, 0);
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_chunk(a0, a1, qreg[s * kCPS + cc]);
+                __builtin_amdgcn_sched_barrier(0);
+                a0 = n0;
+                a1 = n1;
             }
             if constexpr (VS_QREG_PRIO) __builtin_amdgcn_s_setprio(0);
-            if (s == NSLAB - 1) epilogue(item, par);
+            if (!HOLD && s == NSLAB - 1) {
+                read_norms(par);
+                epilogue(qt, ct);
+            }
             if (has_next) finish_slab(buf ^ 1);
             wait_loads();
             __syncthreads();
             buf ^= 1;
-        }
-        par ^= 1;
-        const int64_t next_qt = (item + 1) / nct;
-        if (item + 1 == it1 || next_qt != qt) {
-            flush(qt);
-            if (item + 1 < it1) {
-                qt = next_qt;
-                load_queries(qt);
+            if constexpr (HOLD) {
+                const f32x4 h0 = a0, h1 = a1;
+                if (s + 1 < NSLAB || has_next) {
+                    a0 = *reinterpret_cast<const f32x4 *>(&sA[buf][slab_at(l32, h)]);
+                    a1 = *reinterpret_cast<const f32x4 *>(&sA[buf][slab_at(32 + l32, h)]);
+                }
+                if (s == NSLAB - 1) read_norms(par);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_chunk(h0, h1, qreg[s * kCPS + kCPS - 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s == NSLAB - 1) epilogue(qt, ct);
             }
         }
+        par ^= 1;
+        if (item + 1 == it1 || nqt != qt) {
+            flush(qt);
+            if (item + 1 < it1) load_queries(nqt);
+        }
+        qt = nqt;
+        ct = nctile;
     }
 }
 
