@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes "
                          "(the reference kernel for scaling HBM byte counters)")
-    ap.add_argument("--roof", choices=["l2"], default=None,
+    ap.add_argument("--roof", choices=["l2", "mfma"], default=None,
                     help="measure the on-chip roof of the sparse scan's access pattern "
                          "(256-byte dword row loads from an L2-resident region per XCD)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
@@ -595,6 +595,45 @@ def measure_l2_roof(a, torch):
     print(json.dumps({"l2_roof": res}), flush=True)
 
 
+def measure_mfma_roof(a, torch):
+    """The fp32 MFMA rate this part sustains with no memory traffic: every
+    wave issues MFMAs over two independent accumulator chains (the
+    dependence pattern of the dense scans), one workgroup per CU, for 1, 2
+    and 4 waves per SIMD; 32x32x2 and 16x16x4 shapes.  Against the
+    published 157.3 TFLOP/s this is the highest fraction a dense scan can
+    reach here."""
+    import ctypes
+    from farthest_vector_search_amd.build import ROOF_LIB
+    L = ctypes.CDLL(ROOF_LIB)
+    L.vs_roof_mfma.restype = ctypes.c_int64
+    L.vs_roof_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(n_cu * 256 * 4, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for shape in (32, 16):
+        for wps in (1, 2, 4):
+            iters = 4000 if shape == 32 else 8000
+            args = (shape, wps, iters, n_cu, ctypes.c_void_p(out.data_ptr()), stream)
+            if L.vs_roof_mfma(*args) < 0:
+                raise RuntimeError("vs_roof_mfma rejected its arguments")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            flop = 0
+            for _ in range(a.steps):
+                flop += L.vs_roof_mfma(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            tf = flop / ms / 1e9
+            res[f"{shape}x{shape}_waves_per_simd_{wps}"] = dict(
+                TFLOPs=round(tf, 2), frac_of_published=round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                ms_per_launch=round(ms / a.steps, 4), flop_per_launch=flop // a.steps)
+    print(json.dumps({"mfma_roof": res}), flush=True)
+
+
 def copy_calibration(a, torch):
     """A plain copy of known size (read n bytes, write n bytes) per launch."""
     n = a.copy_bytes // 4
@@ -635,6 +674,9 @@ def main():
         return
     if a.roof == "l2":
         measure_l2_roof(a, torch)
+        return
+    if a.roof == "mfma":
+        measure_mfma_roof(a, torch)
         return
     log(f"workload {a.workload}: generating inputs")
     if a.som:

@@ -1,4 +1,5 @@
-// roofs.hip -- measurement kernels for the on-chip roof of the sparse scan.
+// roofs.hip -- measurement kernels: the on-chip roof of the sparse scan, and
+// the fp32 MFMA issue rate the dense scans are measured against.
 //
 // Not part of the search ABI (built into libvs_roofs.so, used by bench.py's
 // --roof mode).  The sparse scan reads codebook rows as 256-byte segments,
@@ -19,6 +20,7 @@
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int VW, int RPI>  // floats per lane per load; rows per load instruction
 __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, int64_t rows,
@@ -56,6 +58,41 @@ __global__ __launch_bounds__(256) void k_l2_roof(const float *__restrict__ buf, 
     if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
 }
 
+
+// fp32 MFMA issue rate: every wave runs `iters` x 8 MFMAs over two
+// independent accumulator chains with operands in registers (no memory in the
+// loop), the dependence pattern of the dense scans.  SHAPE 32: 32x32x2
+// (4,096 FLOP each), SHAPE 16: 16x16x4 (2,048 FLOP each).  One float per
+// thread is written so the chains are not dead.
+template <int SHAPE>
+__global__ __launch_bounds__(1024) void k_mfma_roof(int32_t iters, float a, float b,
+                                                    float *__restrict__ out) {
+    const float x = a + (float)threadIdx.x * 1e-7f, y = b;
+    float s = 0.0f;
+    if constexpr (SHAPE == 32) {
+        f32x16 c0 = {}, c1 = {};
+        for (int32_t i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, c1, 0, 0, 0);
+            }
+        }
+        s = c0[0] + c1[15];
+    } else {
+        f32x4 c0 = {}, c1 = {};
+        for (int32_t i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c1, 0, 0, 0);
+            }
+        }
+        s = c0[0] + c1[3];
+    }
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 // Reads, per XCD region (8 regions, rows a power of two, row stride ld),
@@ -84,4 +121,23 @@ VS_API int64_t vs_roof_l2_read(const float *buf, int64_t rows, int64_t ld, int32
     const int64_t steps = (int64_t)passes * rows / (waves / 8);
     const int64_t loads_per_wave = (steps + 15) / 16 * 16;
     return waves * loads_per_wave * 64 * 4 * vw;
+}
+
+// Launches k_mfma_roof with `cus` workgroups of 4 x waves_per_simd waves
+// (one workgroup per CU) and returns its FLOPs; the caller times the launch
+// on `stream`.  out needs cus * 256 * waves_per_simd floats.
+VS_API int64_t vs_roof_mfma(int32_t shape, int32_t waves_per_simd, int32_t iters, int32_t cus,
+                            float *out, void *stream) {
+    if (!out || (shape != 16 && shape != 32) || waves_per_simd < 1 || waves_per_simd > 4 ||
+        iters < 1 || cus < 1)
+        return -1;
+    const dim3 grid((unsigned)cus), block((unsigned)(256 * waves_per_simd));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (shape == 32)
+        hipLaunchKernelGGL((k_mfma_roof<32>), grid, block, 0, st, iters, 1.0f, 1.0f, out);
+    else
+        hipLaunchKernelGGL((k_mfma_roof<16>), grid, block, 0, st, iters, 1.0f, 1.0f, out);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const int64_t waves = (int64_t)cus * 4 * waves_per_simd;
+    return waves * (int64_t)iters * 8 * (shape == 32 ? 4096 : 2048);
 }
