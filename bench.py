@@ -181,11 +181,11 @@ def setup(k, torch, vs, a):
             # one Gram row per sequence
             ldg = (n + 63) // 64 * 64
             Gbuf = torch.empty((n, ldg), dtype=torch.float32, device=dev)
-            # algorithmic bytes of one scan, averaged over the run: the live
-            # (unmasked) entries of one Gram row per sequence -- n - 1 - t at
-            # step t -- (with the centroid reference also the running sums
-            # read and written), its mask row read and written, the pick read
-            # and written
+            # algorithmic bytes of one run: the live (unmasked) entries of one
+            # Gram row per sequence and step -- n - 1 - t at step t -- (with
+            # the centroid reference also the running sums read and written),
+            # the mask row read and written once, the seed read and one pick
+            # written per step
             live = sum(max(n - 1 - t, 0) for t in range(steps)) / steps
             if a.div_ref == "centroid":
                 Rbuf = torch.empty((nseq, ldg), dtype=torch.float32, device=dev)
@@ -195,14 +195,15 @@ def setup(k, torch, vs, a):
                     G = vs.vs_diversity_gram(C, out=Gbuf)
                     vs.vs_diversity_run_gram(G, seeds, mask, steps, R=Rbuf[:, :n],
                                              picks_out=picks, want_scores=False)
-                w["scan_bytes"] = nseq * (12 * live + 8 * W + 8)
+                per_col = 12
             else:
                 def step():
                     mask.copy_(mask0)
                     G = vs.vs_diversity_gram(C, out=Gbuf)
                     vs.vs_diversity_run_gram(G, seeds, mask, steps, picks_out=picks,
                                              want_scores=False)
-                w["scan_bytes"] = nseq * (4 * live + 8 * W + 8)
+                per_col = 4
+            w["run_bytes"] = nseq * (steps * (per_col * live + 4) + 8 * W + 4)
         elif a.div_ref == "centroid":
             # the reference of each sequence is the running sum of its rows
             # (the centroid times a positive count): start at the seed's row
@@ -704,8 +705,11 @@ def main():
     kernel_ms = kt.ms / launches
     kernel_s_total = kt.ms * 1e-3
     if w["kind"] == "diversity" and a.div_mode == "gram":
-        # the Gram scans are HBM-bound reads of one table row per sequence
-        achieved = w["scan_bytes"] * launches / kernel_s_total / 1e9
+        # the Gram scans are HBM-bound reads of one table row per sequence and
+        # step (a run is one launch, or one per step for masks wider than the
+        # whole-run kernel keeps): algorithmic bytes of the timed runs over
+        # the dominant kernel's summed time
+        achieved = w["run_bytes"] * a.steps / kernel_s_total / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     elif w["kind"] in ("dense", "diversity"):

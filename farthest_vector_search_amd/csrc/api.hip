@@ -644,6 +644,21 @@ VS_API int vs_diversity_run_gram(const float *G, int64_t n, int64_t ldg, const i
         if (const int s = device_ready(&n_cu)) return s;
         VS_TRY_HIP(vs::launch_zero_rows(R, nseq, ldr, n, reinterpret_cast<hipStream_t>(stream)));
     }
+    if (vs::div_gram_run_supports(n)) {
+        // the whole run in one launch (same picks, scores, masks and R as the
+        // per-step calls below, which serve wider masks)
+        if (ldg % 4 != 0) return VS_ERR_SHAPE;
+        if (!G || !mask_bits) return VS_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(G) & 15) != 0 || !al4(seeds) || !al4(mask_bits) ||
+            !al4(picks_out) || !al4(scores_out))
+            return VS_ERR_ALIGN;
+        int n_cu = 0;
+        if (const int s = device_ready(&n_cu)) return s;
+        VS_TRY_HIP(vs::launch_div_gram_run(G, n, ldg, seeds, mask_bits, nseq, steps, picks_out,
+                                           scores_out, reinterpret_cast<hipStream_t>(stream), R,
+                                           ldr));
+        return VS_OK;
+    }
     for (int32_t t = 0; t < steps; ++t) {
         const int32_t *last = t == 0 ? seeds : picks_out + (int64_t)(t - 1) * nseq;
         int32_t *idx = picks_out + (int64_t)t * nseq;

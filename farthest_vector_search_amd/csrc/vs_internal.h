@@ -173,6 +173,13 @@ hipError_t launch_div_gram_step(const float *G, int64_t n, int64_t ldg, const in
 // columns 0 .. n-1 of `rows` rows of stride ld set to 0 (a fill kernel, so a
 // caller may capture it in a graph)
 hipError_t launch_zero_rows(float *p, int64_t rows, int64_t ld, int64_t n, hipStream_t st);
+// A whole run from G in one launch (masks of up to 32,768 columns): picks
+// [steps x nseq] (and scores, optional) of the per-step kernel, bit for bit.
+bool div_gram_run_supports(int64_t n);
+hipError_t launch_div_gram_run(const float *G, int64_t n, int64_t ldg, const int32_t *seeds,
+                               uint32_t *mask, int64_t nseq, int32_t steps, int32_t *picks,
+                               float *scores, hipStream_t st, float *R = nullptr,
+                               int64_t ldr = 0);
 // CSR scan; `part` holds csr_groups(nc) x nq packed keys of scratch.
 int32_t csr_groups(int64_t nc);
 hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);

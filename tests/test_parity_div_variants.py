@@ -326,16 +326,48 @@ def test_run_matches_steps(n, d, nseq, steps, div_kernel):
     assert np.array_equal(mask.cpu().numpy().view(np.uint32), m1)
 
 
+def masks_for(n, seeds):
+    """Seed masks; a seed outside [0, n) sets no bit."""
+    W = (n + 31) // 32
+    m = np.zeros((len(seeds), W), np.uint32)
+    for s, j in enumerate(seeds):
+        if 0 <= j < n:
+            m[s, j // 32] |= np.uint32(1 << (j % 32))
+    return m
+
+
+# the whole-run kernel keeps a sequence's mask row in LDS up to 32,768 columns
+# and falls back to per-step launches above; (n, d, nseq, steps, seeds)
+RUN_GRAM_CASES = [
+    (400, 96, 90, 30, "distinct"),
+    (37, 8, 20, 40, "distinct"),       # exhausts every candidate, then -1
+    (1, 4, 3, 3, "repeat"),            # nothing but the seed: -1 from the first step
+    (2049, 16, 300, 12, "repeat"),     # sequences sharing a seed
+    (777, 32, 40, 9, "invalid"),       # seeds -1 and n mixed in
+    (32768, 4, 8, 3, "distinct"),      # widest mask row kept in LDS
+    (32769, 4, 8, 3, "distinct"),      # one column more: per-step launches
+]
+
+
 @pytest.mark.parametrize("centroid", [False, True])
-def test_run_gram_matches_steps(centroid):
-    n, d, nseq, steps = 400, 96, 90, 30
-    C = synth.dense_case(1, n, d, "unit", key=4000 + centroid)[1]
-    (r,) = synth.rng_children(4100, 1)
-    seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+@pytest.mark.parametrize("n,d,nseq,steps,kind", RUN_GRAM_CASES)
+def test_run_gram_matches_steps(centroid, n, d, nseq, steps, kind):
+    """vs_diversity_run_gram (one launch per run where the mask row fits in
+    LDS) equals the step-by-step calls bit for bit: picks, scores, masks and,
+    for the centroid reading, the running sums."""
+    C = synth.dense_case(1, n, d, "unit", key=4000 + n + centroid)[1]
+    (r,) = synth.rng_children(4100 + n, 1)
+    if kind == "distinct":
+        seeds = r.choice(n, nseq, replace=False).astype(np.int32)
+    else:
+        seeds = r.choice(n, nseq, replace=True).astype(np.int32)
+    if kind == "invalid":
+        seeds[::7] = -1
+        seeds[3::7] = n
     Cd = T(C)
     G = vs.vs_diversity_gram(Cd)
     # step by step
-    m1 = T(seed_masks(n, seeds).view(np.int32))
+    m1 = T(masks_for(n, seeds).view(np.int32))
     R1 = vs.vs_diversity_gram_sums(G, nseq) if centroid else None
     p1 = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
     s1 = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
@@ -347,7 +379,7 @@ def test_run_gram_matches_steps(centroid):
             vs.vs_diversity_step_gram(G, last, m1, idx_out=p1[t], score_out=s1[t])
         last = p1[t]
     # one call (R deliberately left dirty: the call clears it)
-    m2 = T(seed_masks(n, seeds).view(np.int32))
+    m2 = T(masks_for(n, seeds).view(np.int32))
     R2 = None
     if centroid:
         R2 = vs.vs_diversity_gram_sums(G, nseq)
@@ -359,6 +391,13 @@ def test_run_gram_matches_steps(centroid):
     assert torch.equal(m1, m2)
     if centroid:
         assert torch.equal(R1, R2)
+    p = p2.cpu().numpy()
+    assert ((p >= 0) | (p == -1)).all()
+    if kind == "invalid":
+        bad = (seeds < 0) | (seeds >= n)
+        assert (p[:, bad] == -1).all() and (p[:, ~bad][0] >= 0).all()
+    if steps >= n:  # exhausted: n - 1 picks (a distinct seed each), then -1
+        assert (p[n - 1:] == -1).all()
 
 
 def test_run_ref_matches_steps(div_kernel):
