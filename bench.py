@@ -42,6 +42,12 @@ PEAK_HBM_GBS = 8000.0
 # per XCD), measured with `bench.py --roof l2` (kernel in csrc/roofs.hip);
 # the sparse scan is served from L2, so this is its roof
 PEAK_L2_WIDE_GBS = 28795.7  # the higher of two boxes' runs (28,072 and 28,795.7)
+# Row-gather rate of the diversity run from the Gram matrix: the run's own
+# reference rows read whole, in the run's order, with nothing else in the
+# loop (`bench.py --roof gather`, kernel in csrc/roofs.hip).  The 280 MB Gram
+# matrix is served partly by the 256 MB last-level cache, so this exceeds
+# the 8 TB/s HBM peak; it is the roof of the last-pick Gram run.
+PEAK_GRAM_GATHER_GBS = 8429.8  # the higher of two boxes' runs (8,402.7 and 8,429.8)
 
 
 def parse():
@@ -82,9 +88,12 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes "
                          "(the reference kernel for scaling HBM byte counters)")
-    ap.add_argument("--roof", choices=["l2", "mfma"], default=None,
-                    help="measure the on-chip roof of the sparse scan's access pattern "
-                         "(256-byte dword row loads from an L2-resident region per XCD)")
+    ap.add_argument("--roof", choices=["l2", "mfma", "gather"], default=None,
+                    help="measure a roof and exit: l2 = the on-chip read rate of the sparse "
+                         "scan's access pattern (256-byte row loads from an L2-resident region "
+                         "per XCD); mfma = the fp32 MFMA rate of a loop with no memory "
+                         "traffic; gather = the rate of reading the diversity run's Gram rows "
+                         "whole, in the run's order")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
                                                           "COPY_WRITE_DB"),
                     help="record HBM traffic per launch of the workload's dominant kernel from "
@@ -635,6 +644,64 @@ def measure_mfma_roof(a, torch):
     print(json.dumps({"mfma_roof": res}), flush=True)
 
 
+def measure_gather_roof(a, torch):
+    """Row-gather rate of the diversity run from the Gram matrix.  The 8,359
+    x 768 table's Gram matrix (8,359 x 8,384 fp32, 280 MB: more than the
+    256 MB last-level cache) is built, one 64-step run of the 3,584
+    sequences gives the run's own reference rows (the seed, then the picks of
+    steps 0 .. 62), and k_gather_roof reads those rows whole, in the run's
+    order, with nothing else in the loop; for comparison the same number of
+    uniformly random rows."""
+    import ctypes
+    import numpy as np
+    import synth
+    import farthest_vector_search_amd as vs
+    from farthest_vector_search_amd.build import ROOF_LIB
+    L = ctypes.CDLL(ROOF_LIB)
+    L.vs_roof_gather.restype = ctypes.c_int32
+    L.vs_roof_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    w = synth.workload(3)
+    n, nseq, steps = w["n"], w["nseq"], w["steps"]
+    C = torch.from_numpy(w["C"]).to(dev)
+    seeds = torch.from_numpy(w["seeds"]).to(dev)
+    W = (n + 31) // 32
+    m0 = np.zeros((nseq, W), np.uint32)
+    m0[np.arange(nseq), w["seeds"] // 32] |= (np.uint32(1) << (w["seeds"] % 32).astype(np.uint32))
+    mask = torch.from_numpy(m0.view(np.int32)).to(dev)
+    ldg = (n + 63) // 64 * 64
+    G = vs.vs_diversity_gram(C, out=torch.empty((n, ldg), dtype=torch.float32, device=dev))
+    picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+    vs.vs_diversity_run_gram(G, seeds, mask, steps, picks_out=picks, want_scores=False)
+    run_rows = torch.cat([seeds[None], picks[:-1]]).contiguous()
+    (r,) = synth.rng_children(77, 1)
+    rand_rows = torch.from_numpy(r.integers(0, n, (steps, nseq), dtype=np.int32)).to(dev)
+    grid = nseq
+    out = torch.empty(grid * 256, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, rows in (("run_rows", run_rows), ("random_rows", rand_rows)):
+        valid = int(((rows >= 0) & (rows < n)).sum())
+        args = (ctypes.c_void_p(G.data_ptr()), n, n, ldg, ctypes.c_void_p(rows.data_ptr()), nseq,
+                steps, grid, ctypes.c_void_p(out.data_ptr()), stream)
+        if L.vs_roof_gather(*args) != 0:
+            raise RuntimeError("vs_roof_gather rejected its arguments")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            L.vs_roof_gather(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        nbytes = valid * n * 4
+        res[name] = dict(GBps=round(nbytes / ms / 1e6, 1), bytes_per_launch=nbytes,
+                         ms_per_launch=round(ms, 4), table_bytes=n * ldg * 4)
+    print(json.dumps({"gather_roof": res}), flush=True)
+
+
 def copy_calibration(a, torch):
     """A plain copy of known size (read n bytes, write n bytes) per launch."""
     n = a.copy_bytes // 4
@@ -679,6 +746,9 @@ def main():
     if a.roof == "mfma":
         measure_mfma_roof(a, torch)
         return
+    if a.roof == "gather":
+        measure_gather_roof(a, torch)
+        return
     log(f"workload {a.workload}: generating inputs")
     if a.som:
         w, step, pairs, flops, launches_per_step, cfg = setup_som(a.workload, torch, vs, a)
@@ -710,8 +780,15 @@ def main():
         # whole-run kernel keeps): algorithmic bytes of the timed runs over
         # the dominant kernel's summed time
         achieved = w["run_bytes"] * a.steps / kernel_s_total / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4))
+        if a.div_ref == "centroid":
+            # the running sums (120 MB) stream through HBM beside the Gram rows
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(achieved / PEAK_HBM_GBS, 4))
+        else:
+            roof = dict(bound="gather", achieved=round(achieved, 1), peak=PEAK_GRAM_GATHER_GBS,
+                        unit="GB/s", frac=round(achieved / PEAK_GRAM_GATHER_GBS, 4),
+                        frac_of_hbm_peak=round(achieved / PEAK_HBM_GBS, 4),
+                        peak_source="measured: bench.py --roof gather (the run's own rows)")
     elif w["kind"] in ("dense", "diversity"):
         achieved = flops * a.steps / kernel_s_total / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,

@@ -1,5 +1,6 @@
-// roofs.hip -- measurement kernels: the on-chip roof of the sparse scan, and
-// the fp32 MFMA issue rate the dense scans are measured against.
+// roofs.hip -- measurement kernels: the on-chip roof of the sparse scan, the
+// fp32 MFMA issue rate the dense scans are measured against, and the
+// row-gather rate of the diversity runs from the Gram matrix.
 //
 // Not part of the search ABI (built into libvs_roofs.so, used by bench.py's
 // --roof mode).  The sparse scan reads codebook rows as 256-byte segments,
@@ -93,6 +94,38 @@ __global__ __launch_bounds__(1024) void k_mfma_roof(int32_t iters, float a, floa
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Row gather: one workgroup of 4 waves per sequence (grid-stride over
+// sequences) reads, for each step t, the whole row rows[t * nseq + s] of a
+// table (n floats, row stride ld with ld % 4 == 0), 16 bytes per lane and two
+// loads in flight, the way the whole-run Gram kernel reads its reference
+// rows, with nothing else in the loop.  Row indices outside [0, nrows) are
+// skipped.  Every thread writes one float so the loads are not dead.
+__global__ __launch_bounds__(256) void k_gather_roof(const float *__restrict__ G, int64_t nrows,
+                                                     int64_t n, int64_t ld,
+                                                     const int32_t *__restrict__ rows,
+                                                     int64_t nseq, int32_t steps,
+                                                     float *__restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t nn = (int32_t)n;
+    float acc = 0.0f;
+    for (int64_t s = blockIdx.x; s < nseq; s += gridDim.x) {
+        for (int32_t t = 0; t < steps; ++t) {
+            const int32_t r = rows[(int64_t)t * nseq + s];
+            if (r < 0 || r >= nrows) continue;
+            const float *row = G + (int64_t)r * ld;
+            for (int32_t j0 = 256 * wave + 4 * lane; j0 < nn; j0 += 2048) {
+                const int32_t j1 = j0 + 1024;
+                // j < n <= ld, j % 4 == 0 and ld % 4 == 0: j + 3 < ld
+                const f32x4 va = *reinterpret_cast<const f32x4 *>(row + j0);
+                f32x4 vb = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (j1 < nn) vb = *reinterpret_cast<const f32x4 *>(row + j1);
+                acc += (va.x + va.y) + (va.z + va.w) + (vb.x + vb.y) + (vb.z + vb.w);
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 // Reads, per XCD region (8 regions, rows a power of two, row stride ld),
@@ -140,4 +173,19 @@ VS_API int64_t vs_roof_mfma(int32_t shape, int32_t waves_per_simd, int32_t iters
     if (hipGetLastError() != hipSuccess) return -1;
     const int64_t waves = (int64_t)cus * 4 * waves_per_simd;
     return waves * (int64_t)iters * 8 * (shape == 32 ? 4096 : 2048);
+}
+
+// Launches k_gather_roof over `grid` workgroups (out needs grid * 256
+// floats); the caller times the launch on `stream` and counts the bytes
+// (n * 4 per row index in [0, nrows)).  Returns 0, or -1 on bad arguments.
+VS_API int32_t vs_roof_gather(const float *G, int64_t nrows, int64_t n, int64_t ld,
+                              const int32_t *rows, int64_t nseq, int32_t steps, int32_t grid,
+                              float *out, void *stream) {
+    if (!G || !rows || !out || nrows < 1 || n < 1 || n > 2147483647 || ld < n || ld % 4 != 0 ||
+        (reinterpret_cast<uintptr_t>(G) & 15) != 0 || nseq < 1 || steps < 1 || grid < 1)
+        return -1;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(k_gather_roof, dim3((unsigned)grid), dim3(256), 0, st, G, nrows, n, ld,
+                       rows, nseq, steps, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
