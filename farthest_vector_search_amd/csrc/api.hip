@@ -589,7 +589,8 @@ VS_API int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int
     a.d = d;
     a.S = G;
     a.ld_s = ldg;
-    VS_TRY_HIP(vs::launch_dense_q16_store(a, reinterpret_cast<hipStream_t>(stream), n_cu));
+    VS_TRY_HIP(vs::launch_dense_q16_store(a, reinterpret_cast<hipStream_t>(stream), n_cu,
+                                          true));
     return VS_OK;
 }
 

@@ -60,6 +60,8 @@ constexpr int kPPR = kBK / 4;     // 16-byte pieces per slab row
 constexpr int kRPI = 64 / kPPR;   // slab rows per DMA instruction (1 KiB)
 constexpr int kDPW = kBC / kRPI / kW;  // DMA instructions per wave per slab
 constexpr int kMaxD = 768;
+constexpr int kTPQ = kBQ / kBC;   // candidate tiles per query tile's rows
+constexpr int32_t kSplitTriangle = 2;  // DenseArgs.split: the symmetric Gram walk
 constexpr int kMaxSlabs = kMaxD / kBK;
 static_assert(kBK == 64 || kBK == 128, "slab width");
 static_assert(kW == 4 || kW == 8, "waves per workgroup");
@@ -97,8 +99,14 @@ void k_bmu_q16(const DenseArgs a) {
 
     // ---- this workgroup's items: a run of n_my items over a range of nctx
     // candidate tiles starting at ct_lo, visited query-tile major: item
-    // (qt, ct) is followed by (qt, ct + 1), or (qt + 1, ct_lo) at the range end
+    // (qt, ct) is followed by (qt, ct + 1), or (qt + 1, ct_lo) at the range end.
+    // Triangle walk (a.split == kSplitTriangle, the symmetric Gram build):
+    // query tile q covers the candidate tiles from kTPQ q on, the first kTPQ
+    // of them holding the tile's own rows.
+    const bool tri = STORE && a.split == kSplitTriangle;
     int32_t ct_lo = 0, nctx = (int32_t)nct, qt, ctl, n_my;
+    auto row_lo = [&](int32_t q) { return tri ? kTPQ * q : ct_lo; };
+    auto row_n = [&](int32_t q) { return tri ? (int32_t)nct - kTPQ * q : nctx; };
     {
         const int G = a.grid;
         int64_t it0, it1;
@@ -116,8 +124,15 @@ void k_bmu_q16(const DenseArgs a) {
             it1 = (int64_t)(gg + 1) * a.n_items / G;
         }
         if (it0 >= it1) return;  // whole workgroup: no barrier is skipped by part of it
-        qt = (int32_t)(it0 / nctx);
-        ctl = (int32_t)(it0 - (int64_t)qt * nctx);
+        if (tri) {
+            int64_t left = it0;
+            qt = 0;
+            while (left >= row_n(qt)) left -= row_n(qt++);
+            ctl = (int32_t)left;
+        } else {
+            qt = (int32_t)(it0 / nctx);
+            ctl = (int32_t)(it0 - (int64_t)qt * nctx);
+        }
         n_my = (int32_t)(it1 - it0);
     }
 
@@ -233,6 +248,16 @@ void k_bmu_q16(const DenseArgs a) {
                     } else {
                         for (int r = 0; r < 4 && c + r < nc; ++r) dst[r] = acc[b][r];
                     }
+                    // triangle walk: a tile right of the query tile's own rows
+                    // also writes its transpose, S[c][q] (the pairs below the
+                    // diagonal blocks are computed nowhere else); S[c][q] is
+                    // the same MFMA dot product with the operands' roles
+                    // exchanged, and the products and their order over the
+                    // features are the same, so it is bit-identical
+                    if (tri && ct >= kTPQ * (qt + 1)) {
+                        for (int r = 0; r < 4 && c + r < nc; ++r)
+                            a.S[(c + r) * a.ld_s + q] = acc[b][r];
+                    }
                 }
                 acc[b] = f32x4{};
             }
@@ -294,17 +319,17 @@ void k_bmu_q16(const DenseArgs a) {
         int ops = kDPW;
         if (ts == 0) {
             int32_t c = ctl + io, q = qt;
-            while (c >= nctx) {
-                c -= nctx;
+            while (c >= row_n(q)) {
+                c -= row_n(q);
                 ++q;
             }
-            set_rows(ct_lo + c);
+            set_rows(row_lo(q) + c);
             if constexpr (metric_is_l2(M)) {
                 load_norms((n + io) % 3);
                 if (wave == 0) ++ops;
             }
             if constexpr (MASKED) {
-                load_mask(q, ct_lo + c, (n + io) % 3);
+                load_mask(q, row_lo(q) + c, (n + io) % 3);
                 if (wave < kBQ / 64) ++ops;
             }
         }
@@ -318,10 +343,10 @@ void k_bmu_q16(const DenseArgs a) {
     lds_barrier();
     int buf = 0;
     for (int32_t n = 0; n < n_my; ++n) {
-        const int32_t ct = ct_lo + ctl;
+        const int32_t ct = row_lo(qt) + ctl;
         // the item that follows this one
         int32_t nqt = qt, nctl = ctl + 1;
-        if (nctl == nctx) {
+        if (nctl == row_n(qt)) {
             nctl = 0;
             ++nqt;
         }
@@ -450,14 +475,21 @@ hipError_t launch_dense_q16(const DenseArgs &a0, int metric, int qmode, hipStrea
 // ld_s % 4 == 0, S 16-byte aligned) by the same MFMA arithmetic, in the
 // same per-pair order, as the scans above: each stored value equals,
 // bit for bit, the dot product those scans rank.
-hipError_t launch_dense_q16_store(const DenseArgs &a0, hipStream_t st, int n_cu) {
+hipError_t launch_dense_q16_store(const DenseArgs &a0, hipStream_t st, int n_cu,
+                                  bool symmetric) {
     DenseArgs a = a0;
     const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
     a.n_ctiles = (a.nc + kBC - 1) / kBC;
     a.n_items = nqt * a.n_ctiles;
+    if (symmetric) {
+        // query tile q takes candidate tiles kTPQ q .. n_ctiles - 1 (at least
+        // one: 128 (nqt - 1) < n, so kTPQ (nqt - 1) < n_ctiles)
+        a.n_items -= (int64_t)kTPQ * nqt * (nqt - 1) / 2;
+    }
     const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256) * (8 / kW);
     a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
     a.split = (a.grid % 8 == 0 && a.n_ctiles >= 8 && a.nq < a.nc) ? 8 : 1;
+    if (symmetric) a.split = kSplitTriangle;
     const dim3 grid((unsigned)a.grid);
     dispatch_slabs<COS_MIN, kStore>(a, grid, st);  // not a dominant kernel: no timing events
     return hipGetLastError();

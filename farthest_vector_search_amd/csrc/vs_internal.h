@@ -102,7 +102,8 @@ struct DenseArgs {
     int64_t n_items;        // query tiles x candidate tiles
     int64_t n_ctiles;
     int32_t grid;           // launched workgroups (for the item split)
-    int32_t split;          // 1, or 8: candidate tiles split into one range per XCD
+    int32_t split;          // 1; 8: candidate tiles split into one range per XCD;
+                            // 2: the triangle walk of the symmetric store mode
     float *S;               // score block (store mode): S[q * ld_s + c]
     int64_t ld_s;
 };

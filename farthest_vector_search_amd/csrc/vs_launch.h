@@ -39,7 +39,11 @@ bool q16_supports(int32_t d, const float *C, const float *Q);
 hipError_t launch_dense_q16(const DenseArgs &a, int metric, int qmode, hipStream_t st,
                             int n_cu);
 // every dot product Q[q] . C[c] into a.S (same arithmetic as the scans)
-hipError_t launch_dense_q16_store(const DenseArgs &a, hipStream_t st, int n_cu);
+// symmetric (Q == C, nq == nc): only the tiles at or right of each query
+// tile's own rows are computed; those right of them also write their
+// transpose, so every entry is written once
+hipError_t launch_dense_q16_store(const DenseArgs &a, hipStream_t st, int n_cu,
+                                  bool symmetric = false);
 hipError_t launch_dense_qreg_store(const DenseArgs &a, hipStream_t st, int n_cu);
 // per-row best of a score block into packed keys (the unfused comparator)
 hipError_t launch_row_argbest(const float *S, int64_t nq, int64_t nc, int64_t ld_s,

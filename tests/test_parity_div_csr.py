@@ -146,6 +146,26 @@ def test_diversity_gram_entries():
     assert np.abs(G.astype(np.float64) - ref).max() <= 2e-6
 
 
+@pytest.mark.parametrize("n,d", [(40, 4), (129, 300), (700, 768), (1000, 260), (2049, 16)])
+def test_diversity_gram_symmetric_build(n, d):
+    """The Gram build computes the tiles at or right of each 128-row block's
+    own rows and writes the rest as their transpose: G equals its transpose
+    bit for bit, every entry of a bound check against the oracle, and for
+    256 < d <= 768 it equals, bit for bit, the full product written by the
+    same 16-query kernel in the unfused comparator (no symmetry used)."""
+    C = synth.dense_case(1, n, d, "unit", key=31 * n + d)[1]
+    Cd = T(C)
+    G = vs.vs_diversity_gram(Cd)[:, :n]
+    assert torch.equal(G, G.t())
+    Gh = G.cpu().numpy()
+    ref = oracle.gram_cos(C, threads=8)
+    assert np.abs(Gh.astype(np.float64) - ref).max() <= 2e-6
+    if 256 < d:
+        S = torch.empty((n, (n + 63) // 64 * 64), dtype=torch.float32, device=dev())
+        vs.vs_bmu_search_unfused(Cd, Cd, vs.VS_COS_MAX, S=S)
+        assert torch.equal(G, S[:, :n])
+
+
 def test_diversity_gram_invalid_reference():
     """A reference outside [0, n) yields -1, NaN and leaves the mask alone;
     a sequence with every row masked yields -1 and NaN."""
