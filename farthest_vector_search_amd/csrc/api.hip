@@ -19,7 +19,7 @@
 
 namespace {
 
-int g_last_hip = 0;
+thread_local int g_last_hip = 0;  // the HIP error of this thread's last failed call
 
 struct DevInfo {
     bool probed = false, ok = false;

@@ -39,11 +39,14 @@
  *  - Return value: a vs_status.  The library never aborts, prints or throws.
  *    Arguments are checked before anything is enqueued; a failed check
  *    enqueues nothing.  A HIP launch failure returns VS_ERR_HIP and the HIP
- *    error code is kept for vs_last_hip_error().
+ *    error code is kept, per calling thread, for vs_last_hip_error().
  *  - A query whose every candidate is masked gets index -1 and score NaN;
  *    this is not an error.
  *  - Results are deterministic: the same inputs give bit-identical outputs
  *    on every call, independent of how the work is split across the GPU.
+ *    The one exception is the SOM batch update (vs_som_update*, and the
+ *    epochs that run it), whose per-neuron sums use float atomics: their
+ *    last bits may differ from run to run (see there).
  */
 #ifndef VS_H
 #define VS_H
