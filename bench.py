@@ -47,7 +47,7 @@ PEAK_L2_WIDE_GBS = 28795.7  # the higher of two boxes' runs (28,072 and 28,795.7
 # loop (`bench.py --roof gather`, kernel in csrc/roofs.hip).  The 280 MB Gram
 # matrix is served partly by the 256 MB last-level cache, so this exceeds
 # the 8 TB/s HBM peak; it is the roof of the last-pick Gram run.
-PEAK_GRAM_GATHER_GBS = 8429.8  # the higher of two boxes' runs (8,402.7 and 8,429.8)
+PEAK_GRAM_GATHER_GBS = 8694.5  # the highest of three boxes' runs (8,402.7, 8,429.8, 8,694.5)
 
 
 def parse():
