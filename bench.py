@@ -41,13 +41,13 @@ PEAK_HBM_GBS = 8000.0
 # shape (four 256-byte row segments per 16-byte-per-lane load, a 4 MiB slice
 # per XCD), measured with `bench.py --roof l2` (kernel in csrc/roofs.hip);
 # the sparse scan is served from L2, so this is its roof
-PEAK_L2_WIDE_GBS = 28795.7  # the higher of two boxes' runs (28,072 and 28,795.7)
+PEAK_L2_WIDE_GBS = 28795.7  # the highest of the runs on four machines (28,072 to 28,795.7)
 # Row-gather rate of the diversity run from the Gram matrix: the run's own
 # reference rows read whole, in the run's order, with nothing else in the
 # loop (`bench.py --roof gather`, kernel in csrc/roofs.hip).  The 280 MB Gram
 # matrix is served partly by the 256 MB last-level cache, so this exceeds
 # the 8 TB/s HBM peak; it is the roof of the last-pick Gram run.
-PEAK_GRAM_GATHER_GBS = 8694.5  # the highest of three boxes' runs (8,402.7, 8,429.8, 8,694.5)
+PEAK_GRAM_GATHER_GBS = 8694.5  # the highest of the runs on three machines (8,402.7 to 8,694.5)
 
 
 def parse():
