@@ -554,8 +554,12 @@ VS_API int vs_diversity_run_ref(const float *C, int64_t n, int32_t d, const int3
         steps < 0)
         return VS_ERR_SHAPE;
     if (nseq == 0 || steps == 0) return VS_OK;
-    if (!C || !seeds || !Q || !picks_out) return VS_ERR_NULL;
-    if (!al4(C) || !al4(seeds) || !al4(Q)) return VS_ERR_ALIGN;
+    // every check of the steps below, before anything is enqueued
+    if (!C || !seeds || !Q || !picks_out || !mask_bits || !workspace) return VS_ERR_NULL;
+    if (!al4(C) || !al4(seeds) || !al4(Q) || !al4(mask_bits) || !al4(picks_out) ||
+        !al4(scores_out) || !al256(workspace))
+        return VS_ERR_ALIGN;
+    if (workspace_bytes < vs_diversity_step_workspace(n, d, nseq)) return VS_ERR_WORKSPACE;
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -638,23 +642,18 @@ VS_API int vs_diversity_run_gram(const float *G, int64_t n, int64_t ldg, const i
         (R && (ldr < n || ldr % 4 != 0)))
         return VS_ERR_SHAPE;
     if (nseq == 0 || steps == 0) return VS_OK;
-    if (!seeds || !picks_out) return VS_ERR_NULL;
-    if (R) {
-        if ((reinterpret_cast<uintptr_t>(R) & 15) != 0) return VS_ERR_ALIGN;
-        int n_cu = 0;
-        if (const int s = device_ready(&n_cu)) return s;
-        VS_TRY_HIP(vs::launch_zero_rows(R, nseq, ldr, n, reinterpret_cast<hipStream_t>(stream)));
-    }
+    // every check of the steps below, before anything is enqueued
+    if (ldg % 4 != 0) return VS_ERR_SHAPE;
+    if (!G || !seeds || !picks_out || !mask_bits) return VS_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(G) & 15) != 0 || (reinterpret_cast<uintptr_t>(R) & 15) != 0 ||
+        !al4(seeds) || !al4(mask_bits) || !al4(picks_out) || !al4(scores_out))
+        return VS_ERR_ALIGN;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    if (R) VS_TRY_HIP(vs::launch_zero_rows(R, nseq, ldr, n, reinterpret_cast<hipStream_t>(stream)));
     if (vs::div_gram_run_supports(n)) {
         // the whole run in one launch (same picks, scores, masks and R as the
         // per-step calls below, which serve wider masks)
-        if (ldg % 4 != 0) return VS_ERR_SHAPE;
-        if (!G || !mask_bits) return VS_ERR_NULL;
-        if ((reinterpret_cast<uintptr_t>(G) & 15) != 0 || !al4(seeds) || !al4(mask_bits) ||
-            !al4(picks_out) || !al4(scores_out))
-            return VS_ERR_ALIGN;
-        int n_cu = 0;
-        if (const int s = device_ready(&n_cu)) return s;
         VS_TRY_HIP(vs::launch_div_gram_run(G, n, ldg, seeds, mask_bits, nseq, steps, picks_out,
                                            scores_out, reinterpret_cast<hipStream_t>(stream), R,
                                            ldr));

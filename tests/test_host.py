@@ -269,6 +269,12 @@ def test_diversity_run_validation(L):
     assert run_gram(nseq=0, seeds=0) == 0
     assert run_gram(picks=0) == 1
     assert run_gram(R=FAKE + 4, ldr=128) == 5
+    # every check of the steps is made before anything (clearing R) is enqueued
+    assert run_gram(ldg=130) == 2
+    assert run_gram(G=0, R=FAKE, ldr=128) == 1
+    assert run_gram(mask=0, R=FAKE, ldr=128) == 1
+    assert run_gram(G=FAKE + 4, R=FAKE, ldr=128) == 5
+    assert run_gram(mask=FAKE + 2, R=FAKE, ldr=128) == 5
 
 
 def test_diversity_run_ref_validation(L):
@@ -282,6 +288,12 @@ def test_diversity_run_ref_validation(L):
     assert run(Q=0) == 1
     assert run(seeds=0) == 1
     assert run(Q=FAKE + 2) == 5
+    # every check of the steps is made before Q is cleared and seeded
+    assert run(mask=0) == 1
+    assert run(ws=0) == 1
+    assert run(ws=FAKE + 16) == 5
+    assert run(picks=FAKE + 2) == 5
+    assert run(ws_bytes=8) == 4
 
 
 def test_fp16_epoch_validation(L):
