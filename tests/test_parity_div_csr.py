@@ -243,6 +243,53 @@ def test_workload_3_gram_chain():
     assert np.array_equal(a[2], b[2])
 
 
+def test_workload_3_gram_run():
+    """The full diversity workload as bench.py times it from the Gram matrix:
+    one vs_diversity_run_gram launch for all 64 steps of 3,584 sequences
+    (and the triangle Gram build) equals the per-step MFMA scan bit for bit:
+    picks, scores and final masks."""
+    w = synth.workload(3)
+    a = gpu_chain(w["C"], w["seeds"], w["steps"])
+    Cd = T(w["C"])
+    n = w["C"].shape[0]
+    G = vs.vs_diversity_gram(Cd)
+    mask = T(seed_masks(n, w["seeds"]).view(np.int32))
+    picks, scores = vs.vs_diversity_run_gram(G, T(np.asarray(w["seeds"], np.int32)), mask,
+                                             w["steps"])
+    torch.cuda.synchronize()
+    assert np.array_equal(picks.cpu().numpy().T, a[0])
+    assert np.array_equal(scores.cpu().numpy().T.view(np.uint32), a[1].view(np.uint32))
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), a[2])
+
+
+def test_workload_3_gram_centroid_run():
+    """The centroid reading at full size, as bench.py times it: one
+    vs_diversity_run_gram launch with running sums equals the chained
+    vs_diversity_step_gram_sum calls bit for bit (picks, scores, masks and
+    the final running sums)."""
+    w = synth.workload(3)
+    Cd = T(w["C"])
+    n, nseq, steps = w["C"].shape[0], len(w["seeds"]), w["steps"]
+    seeds = T(np.asarray(w["seeds"], np.int32))
+    G = vs.vs_diversity_gram(Cd)
+    m1 = T(seed_masks(n, w["seeds"]).view(np.int32))
+    R1 = vs.vs_diversity_gram_sums(G, nseq)
+    p1 = torch.empty((steps, nseq), dtype=torch.int32, device=dev())
+    s1 = torch.empty((steps, nseq), dtype=torch.float32, device=dev())
+    last = seeds
+    for t in range(steps):
+        vs.vs_diversity_step_gram_sum(G, last, R1, m1, idx_out=p1[t], score_out=s1[t])
+        last = p1[t]
+    m2 = T(seed_masks(n, w["seeds"]).view(np.int32))
+    R2 = vs.vs_diversity_gram_sums(G, nseq)
+    p2, s2 = vs.vs_diversity_run_gram(G, seeds, m2, steps, R=R2)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(m1, m2)
+    assert torch.equal(R1, R2)
+
+
 @pytest.mark.slow
 def test_workload_3_full_chain():
     """8,359 x 768 table, 3,584 sequences, 64 steps, every pick replayed."""
