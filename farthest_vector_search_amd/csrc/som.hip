@@ -21,6 +21,9 @@
 //      reciprocal taken once per neuron by the denominator's second pass
 //      (0 where den = 0: those neurons keep their weights).
 // Both passes only sum over offsets that stay on the map (the planar edge).
+// For window radii 1 .. 8 both passes run as one sweep over the map
+// (k_som_smooth_blk, k_som_smooth_nm) that holds the pending outputs in a
+// ring of registers; the two-pass kernels take R = 0 and R > 8.
 //
 // Element (neuron m, feature k) of the codebook and of the S / T buffers:
 //   neuron-major (dense rows):  m * d + k
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
     }
 }
 
-// The neuron-major layout's passes (dense rows).  Threads of a workgroup are
+// The neuron-major layout's two passes (dense rows).  Threads of a workgroup are
 // split into groups of sg = min(256, d rounded up to a power of two) lanes;
 // each group takes one neuron and runs along its features, so every tap is a
 // coalesced row segment and the neuron's grid position and window are worked
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_som_pass_nm(const float *__restric
     }
 }
 
-// The blocked layout's passes.  A workgroup owns one 64-neuron block (lane =
+// The blocked layout's two passes.  A workgroup owns one 64-neuron block (lane =
 // neuron) and 4 x kKV features (kKV per wave); each thread works out its
 // neuron's grid position and window once, then for every tap reads kKV
 // features of the tap neuron -- kKV loads, each a coalesced 256-byte row of a
@@ -373,6 +376,156 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     }
 }
 
+// Both passes in one sweep for the neuron-major layout (dense rows, window
+// radius R <= 8 known at compile time).  A wave owns 64 consecutive features
+// (one per lane, so a neuron's segment is one 256-byte load), a strip of kSW
+// map columns x0 .. x0+kSW-1 and a band of output rows [ya, yb), and walks
+// the input rows ya-R .. yb+R-1 that lie on the map:
+//   - the row's kSW + 2R neurons (0 off the map) are loaded into registers,
+//     where every column's window along the row is summed:
+//     X(y', x) = sum_t g(t) S(y', x + t);
+//   - X(y', x) is added, weighted g(s), to the pending outputs of rows
+//     y' - s in a ring of 2R+1 registers per column (the row loop is unrolled
+//     by 2R+1, so every ring slot is a fixed register);
+//   - once row y' is in, output row y' - R has all its terms; inside the band
+//     it is multiplied by its reciprocal denominator and stored (or left
+//     alone where the denominator is 0).
+// The four waves of a workgroup take four adjacent strips, so most halo
+// columns are lines a neighbouring wave has just fetched; the bands' halo
+// rows are read twice.  No intermediate buffer: S is read about once and the
+// codebook written once.
+constexpr int kSW = 8;  // map columns per wave
+#ifndef VS_SOM_SMOOTH_WAVES
+#define VS_SOM_SMOOTH_WAVES 2048
+#endif
+constexpr int64_t kSmoothWaves = VS_SOM_SMOOTH_WAVES;  // target wave count of a launch
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_som_smooth_nm(
+    const float *__restrict__ S, float *__restrict__ C, int32_t d, int32_t rows, int32_t cols,
+    int32_t nkc, int32_t nsg, int32_t band, int64_t n_items, const float *__restrict__ g,
+    const float *__restrict__ rden) {
+    constexpr int P = 2 * R + 1;
+    constexpr int NH = kSW + 2 * R;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // the grid is a multiple of 8: XCD x (blockIdx % 8) takes a contiguous
+    // run of items, so the strips of neighbouring workgroups share an L2
+    const int64_t G8 = gridDim.x >> 3;
+    const int64_t item = (int64_t)(blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
+    if (item >= n_items) return;
+    // item = (band, feature chunk, group of 4 strips), strips fastest
+    const int32_t sg = (int32_t)(item % nsg);
+    const int64_t rest = item / nsg;
+    const int32_t kc = (int32_t)(rest % nkc);
+    const int32_t bnd = (int32_t)(rest / nkc);
+    const int32_t x0 = (sg * 4 + wave) * kSW;
+    if (x0 >= cols) return;  // whole wave (no barriers in this kernel)
+    const int32_t ya = bnd * band;
+    const int32_t yb = ya + band < rows ? ya + band : rows;
+    const int32_t ys = ya - R > 0 ? ya - R : 0;       // first input row
+    const int32_t ye = yb + R < rows ? yb + R : rows;  // input rows end
+
+    const int32_t k = kc * 64 + lane;
+    const bool k_ok = k < d;
+    const int32_t kl = k_ok ? k : d - 1;  // loads stay inside the row
+    float gw[R + 1];
+#pragma unroll
+    for (int i = 0; i <= R; ++i) gw[i] = g[i];
+
+    // raw loads of input row y (columns clamped onto the map; the columns
+    // off the map are zeroed where the values are used)
+    auto load_row = [&](int32_t y, float(&h)[NH]) {
+        const float *row = S + (int64_t)y * cols * d + kl;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int32_t x = x0 - R + i;
+            const int32_t xc = x < 0 ? 0 : (x >= cols ? cols - 1 : x);
+            h[i] = row[(int64_t)xc * d];
+        }
+    };
+    float hn[NH];
+    load_row(ys, hn);
+    float acc[kSW][P];
+#pragma unroll
+    for (int j = 0; j < kSW; ++j)
+#pragma unroll
+        for (int q = 0; q < P; ++q) acc[j][q] = 0.0f;
+
+    int32_t base = ys;
+    // one input row yy; its ring position u = (yy - ys) mod P is a
+    // compile-time constant (output row y sits in slot (y - ys) mod P)
+    auto step = [&](auto U) {
+        constexpr int u = decltype(U)::value;
+        const int32_t yy = base + u;
+        if (yy < ye) {
+            float h[NH];
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+                const int32_t x = x0 - R + i;
+                h[i] = (x >= 0 && x < cols) ? hn[i] : 0.0f;
+            }
+            // output row of this step: its reciprocal denominators, then
+            // the next input row's loads, all issued before the sums
+            const int32_t yo = yy - R;
+            float rq[kSW];
+            {
+                const int64_t ro = (int64_t)(yo > 0 ? yo : 0) * cols;
+#pragma unroll
+                for (int j = 0; j < kSW; ++j) {
+                    const int32_t xo = x0 + j < cols ? x0 + j : cols - 1;
+                    rq[j] = rden[ro + xo];
+                }
+            }
+            load_row(yy + 1 < ye ? yy + 1 : yy, hn);
+            asm volatile("" ::: "memory");
+            float X[kSW];
+#pragma unroll
+            for (int j = 0; j < kSW; ++j) {
+                float x = gw[0] * h[R + j];
+#pragma unroll
+                for (int t = 1; t <= R; ++t) x = __builtin_fmaf(gw[t], h[R + j - t] + h[R + j + t], x);
+                X[j] = x;
+            }
+#pragma unroll
+            for (int sft = -R; sft <= R; ++sft) {
+                const int q = (u + sft + 2 * P) % P;  // constant once unrolled
+#pragma unroll
+                for (int j = 0; j < kSW; ++j)
+                    acc[j][q] = __builtin_fmaf(gw[sft < 0 ? -sft : sft], X[j], acc[j][q]);
+            }
+            constexpr int qd = (u - R + 2 * P) % P;
+            if (yo >= ya) {  // (yo < yb always: yy < ye <= yb + R)
+                float *out = C + ((int64_t)yo * cols + x0) * d + k;
+#pragma unroll
+                for (int j = 0; j < kSW; ++j)
+                    if (x0 + j < cols && k_ok && rq[j] > 0.0f) out[(int64_t)j * d] = acc[j][qd] * rq[j];
+            }
+#pragma unroll
+            for (int j = 0; j < kSW; ++j) acc[j][qd] = 0.0f;
+        }
+    };
+    for (; base < ye; base += P) Unroll<0, P>::run(step);
+    // the map's last R rows have no further input rows: they are complete
+    // now (only when the band reaches the map's end)
+    if (ye == rows) {
+        for (int32_t yo = rows - R > ya ? rows - R : ya; yo < yb; ++yo) {
+            const int q = (yo - ys) % P;
+            float *out = C + ((int64_t)yo * cols + x0) * d + k;
+#pragma unroll
+            for (int j = 0; j < kSW; ++j) {
+                float v = 0.0f;
+#pragma unroll
+                for (int qq = 0; qq < P; ++qq) v = qq == q ? acc[j][qq] : v;
+                if (x0 + j < cols && k_ok) {
+                    const float rd = rden[(int64_t)yo * cols + x0 + j];
+                    if (rd > 0.0f) out[(int64_t)j * d] = v * rd;
+                }
+            }
+        }
+    }
+}
+
 // The same two passes over the counts (one "feature", int32 input first);
 // the second writes 1 / den (0 where den = 0).
 template <bool ALONG_X, typename TIn>
@@ -464,6 +617,30 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
         else                                                                                   \
             hipLaunchKernelGGL((k_som_smooth_blk<RR, false>), gw, dim3(kThreads), 0, st, a.S,   \
                                a.C, a.d, a.rows, a.cols, ntx, items, a.g, a.rden);              \
+        break;
+        switch (R) {
+            VS_SMOOTH(1) VS_SMOOTH(2) VS_SMOOTH(3) VS_SMOOTH(4)
+            VS_SMOOTH(5) VS_SMOOTH(6) VS_SMOOTH(7) VS_SMOOTH(8)
+        }
+#undef VS_SMOOTH
+    } else if (!blocked && R >= 1 && R <= 8) {
+        const int32_t nkc = (a.d + 63) / 64;
+        const int32_t nsg = ((a.cols + kSW - 1) / kSW + 3) / 4;
+        // bands of at least 8 rows, as many as bring the waves to about
+        // kSmoothWaves (more waves keep more loads in flight; each band
+        // re-reads 2R halo rows)
+        const int64_t per_band = (int64_t)nkc * nsg * 4;
+        int64_t nb = (kSmoothWaves + per_band - 1) / per_band;
+        const int64_t nb_max = (a.rows + 7) / 8;
+        nb = nb < 1 ? 1 : (nb > nb_max ? nb_max : nb);
+        const int32_t band = (int32_t)((a.rows + nb - 1) / nb);
+        nb = (a.rows + band - 1) / band;
+        const int64_t items = nb * nkc * nsg;
+        const dim3 gw((unsigned)((items + 7) / 8 * 8));
+#define VS_SMOOTH(RR)                                                                          \
+    case RR:                                                                                   \
+        hipLaunchKernelGGL((k_som_smooth_nm<RR>), gw, dim3(kThreads), 0, st, a.S, a.C, a.d,     \
+                           a.rows, a.cols, nkc, nsg, band, items, a.g, a.rden);                 \
         break;
         switch (R) {
             VS_SMOOTH(1) VS_SMOOTH(2) VS_SMOOTH(3) VS_SMOOTH(4)
