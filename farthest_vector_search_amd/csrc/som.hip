@@ -32,6 +32,8 @@
 // Threads run along the contiguous axis (k, resp. m within a block), so every
 // load and store of a pass is coalesced; the window's other taps are re-reads
 // of lines the neighbouring waves just fetched (L1 / L2 hits).
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "vs_internal.h"
@@ -399,6 +401,10 @@ constexpr int kSW = 8;  // map columns per wave
 #define VS_SOM_SMOOTH_WAVES 2048
 #endif
 constexpr int64_t kSmoothWaves = VS_SOM_SMOOTH_WAVES;  // target wave count of a launch
+// Below this many waves the sweep cannot hide its row-by-row load latency
+// (the 32 x 32 map, 16 waves: 36 us against 28 us for the two passes) and
+// the two-pass kernels run instead.  VS_SOM_SMOOTH=sweep|passes forces one.
+constexpr int64_t kSmoothMinWaves = 256;
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void k_som_smooth_nm(
@@ -605,6 +611,25 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
     hipLaunchKernelGGL((k_som_den_pass<false, float>), gd, dim3(kThreads), 0, st, a.den_t, a.rden,
                        nc, a.rows, a.cols, R, a.g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    // neuron-major sweep: bands of at least 8 rows, as many as bring the
+    // waves to about kSmoothWaves (more waves keep more loads in flight; each
+    // band re-reads 2R halo rows)
+    const int32_t nm_kc = (a.d + 63) / 64;
+    const int32_t nm_sg = ((a.cols + kSW - 1) / kSW + 3) / 4;
+    const int64_t per_band = (int64_t)nm_kc * nm_sg * 4;
+    int64_t nb = (kSmoothWaves + per_band - 1) / per_band;
+    const int64_t nb_max = (a.rows + 7) / 8;
+    nb = nb < 1 ? 1 : (nb > nb_max ? nb_max : nb);
+    const int32_t band = (int32_t)((a.rows + nb - 1) / nb);
+    nb = (a.rows + band - 1) / band;
+    const int64_t nm_items = nb * nm_kc * nm_sg;
+    bool sweep_nm = !blocked && R >= 1 && R <= 8;
+    if (sweep_nm) {
+        const char *env = std::getenv("VS_SOM_SMOOTH");
+        if (env && std::strcmp(env, "passes") == 0) sweep_nm = false;
+        else if (!(env && std::strcmp(env, "sweep") == 0))
+            sweep_nm = nm_items * 4 >= kSmoothMinWaves;
+    }
     if (blocked && R >= 1 && R <= 8) {
         const int32_t ntx = (a.cols + 63) / 64;
         const int64_t items = (int64_t)a.d * ntx;
@@ -623,24 +648,12 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
             VS_SMOOTH(5) VS_SMOOTH(6) VS_SMOOTH(7) VS_SMOOTH(8)
         }
 #undef VS_SMOOTH
-    } else if (!blocked && R >= 1 && R <= 8) {
-        const int32_t nkc = (a.d + 63) / 64;
-        const int32_t nsg = ((a.cols + kSW - 1) / kSW + 3) / 4;
-        // bands of at least 8 rows, as many as bring the waves to about
-        // kSmoothWaves (more waves keep more loads in flight; each band
-        // re-reads 2R halo rows)
-        const int64_t per_band = (int64_t)nkc * nsg * 4;
-        int64_t nb = (kSmoothWaves + per_band - 1) / per_band;
-        const int64_t nb_max = (a.rows + 7) / 8;
-        nb = nb < 1 ? 1 : (nb > nb_max ? nb_max : nb);
-        const int32_t band = (int32_t)((a.rows + nb - 1) / nb);
-        nb = (a.rows + band - 1) / band;
-        const int64_t items = nb * nkc * nsg;
-        const dim3 gw((unsigned)((items + 7) / 8 * 8));
+    } else if (sweep_nm) {
+        const dim3 gw((unsigned)((nm_items + 7) / 8 * 8));
 #define VS_SMOOTH(RR)                                                                          \
     case RR:                                                                                   \
         hipLaunchKernelGGL((k_som_smooth_nm<RR>), gw, dim3(kThreads), 0, st, a.S, a.C, a.d,     \
-                           a.rows, a.cols, nkc, nsg, band, items, a.g, a.rden);                 \
+                           a.rows, a.cols, nm_kc, nm_sg, band, nm_items, a.g, a.rden);          \
         break;
         switch (R) {
             VS_SMOOTH(1) VS_SMOOTH(2) VS_SMOOTH(3) VS_SMOOTH(4)

@@ -8,7 +8,9 @@ window (the oracle's reading).
 Bar, derived from the arithmetic: the GPU sums each neuron's inputs with fp32
 atomics (at most c terms, c = the largest number of inputs sharing a BMU), then
 runs two window passes of at most 2R+1 fp32 fused multiply-adds each over the
-same magnitudes, the same for the denominator, and multiplies by the
+same magnitudes (the one-sweep kernels add the two taps at +-t first and then
+fuse the multiply-add, which puts no more roundings on any term), the same for
+the denominator, and multiplies by the
 denominator's fp32 reciprocal (two roundings).  Every step adds at
 most a unit roundoff u = 2^-24 per term on sum_i h |x_i| / den (the oracle's
 ``mass``), so |w_gpu - w| <= 2 (c + 8R + 12) u mass (factor 2 for second-order
@@ -94,11 +96,20 @@ UPDATE_CASES = [
     (3, 4, 4, 50, 1.0, 0),            # R = 0: per-neuron means
     (16, 16, 256, 2000, 3.0, 9),
     (1, 1, 3, 10, 1.0, 0),            # one neuron
+    (37, 45, 70, 3000, 2.0, 6),       # 5 row bands (the last 5 rows), a partial strip,
+                                      # waves past the map's columns, a partial feature chunk
 ]
 
 
+# "sweep" forces the one-sweep kernel (radii 1..8) on maps too small for it to
+# be chosen, "passes" the two-pass kernels; "auto" is the library's choice
+@pytest.mark.parametrize("smooth", ["auto", "sweep", "passes"])
 @pytest.mark.parametrize("rows,cols,d,n,sigma,R", UPDATE_CASES)
-def test_som_update_dense(rows, cols, d, n, sigma, R):
+def test_som_update_dense(rows, cols, d, n, sigma, R, smooth, monkeypatch):
+    if smooth == "auto":
+        monkeypatch.delenv("VS_SOM_SMOOTH", raising=False)
+    else:
+        monkeypatch.setenv("VS_SOM_SMOOTH", smooth)
     nc = rows * cols
     X, C = dense_inputs(n, rows, cols, d, key=900 + rows * 31 + cols)
     bmu = synth.random_indices(n, nc, key=rows * 100 + cols)
