@@ -281,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     constexpr int P = 2 * R + 1;
     constexpr int W = 64 + 2 * R;
     __shared__ float buf[kThreads / 64][W];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + wave;
     if (item >= n_items) return;
     // strips fastest: the waves of a workgroup sweep neighbouring strips of
@@ -316,6 +317,18 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
         }
     };
 
+    // ALIGNED: uniform row pointers, each advanced by one map row per step
+    // (no per-row 64-bit products), and per-lane offsets inside a row; every
+    // column of the strip is on the map (c_ok), and a halo lane's offset is
+    // taken from its row's own block (the neighbouring blocks of one map row
+    // are adjacent in this layout)
+    const int64_t blk0 = (int64_t)(x0 >> 6) * D64;
+    int64_t hoff = lane;  // lanes without a halo column read their own
+    if (h_ok) hoff = lane < R ? (int64_t)(64 - R + lane) - D64 : D64 + (lane - R);
+    const float *pn = Sk + blk0 + (rows > 1 ? rs : 0);  // row min(yy + 1, rows - 1)
+    const float *pr = rden + x0;                        // row clamp(yy + 1 - R, 0, rows - 1)
+    float *po = Ck + blk0;                              // output row yy - R
+
     float gw[R + 1];
 #pragma unroll
     for (int i = 0; i <= R; ++i) gw[i] = g[i];
@@ -323,7 +336,14 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
 #pragma unroll
     for (int i = 0; i < P; ++i) acc[i] = 0.0f;
 
-    float vc = Sk[at_rc(0, xcl)], vh = Sk[at_rc(0, xhl)];
+    float vc, vh;
+    if constexpr (ALIGNED) {
+        vc = Sk[blk0 + lane];
+        vh = Sk[blk0 + hoff];
+    } else {
+        vc = Sk[at_rc(0, xcl)];
+        vh = Sk[at_rc(0, xhl)];
+    }
     // 1 / denominator of the output row finished after the current input row
     // (row yy - R; none for yy < R)
     float rnext = 0.0f;
@@ -336,7 +356,13 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
             const float cc = c_ok ? vc : 0.0f;
             const float hh = h_ok ? vh : 0.0f;
             const float rd = rnext;
-            {
+            if constexpr (ALIGNED) {
+                vc = pn[lane];
+                vh = pn[hoff];
+                rnext = pr[lane];
+                if (yy + 2 < rows) pn += rs;
+                if (yy + 2 - R >= 1 && yy + 2 - R <= rows - 1) pr += cols;
+            } else {
                 const int32_t yn = yy + 1 < rows ? yy + 1 : rows - 1;
                 vc = Sk[at_rc(yn, xcl)];
                 vh = Sk[at_rc(yn, xhl)];
@@ -360,7 +386,14 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
             }
             constexpr int qd = (u - R + 2 * P) % P;
             const int32_t yd = yy - R;
-            if (yd >= 0 && c_ok && rd > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] * rd;
+            if constexpr (ALIGNED) {
+                if (yd >= 0) {
+                    if (rd > 0.0f) po[lane] = acc[qd] * rd;
+                    po += rs;
+                }
+            } else {
+                if (yd >= 0 && c_ok && rd > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] * rd;
+            }
             acc[qd] = 0.0f;
         }
     };

@@ -154,6 +154,12 @@ def test_som_update_no_inputs_in_window_keeps_codebook():
     (4, 5, 9, 30, 1.0, 6, 0.3),        # window beyond both edges
     (16, 16, 64, 900, 2.0, 16, 0.2),
     (3, 3, 17, 40, 1.0, 0, 0.3),
+    # widths a multiple of 64 (row pointers advanced per step)
+    (10, 128, 20, 300, 1.0, 5, 0.1),   # two strips
+    (70, 64, 8, 400, 2.0, 8, 0.2),     # one strip, many rows
+    (5, 192, 33, 200, 1.0, 3, 0.1),    # three strips
+    (1, 64, 7, 50, 1.0, 2, 0.3),       # one row
+    (2, 128, 5, 40, 1.0, 6, 0.3),      # fewer rows than R
 ])
 def test_som_update_csr(rows, cols, d, n, sigma, R, density):
     nc = rows * cols
