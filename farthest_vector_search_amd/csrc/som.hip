@@ -246,8 +246,12 @@ __global__ __launch_bounds__(kThreads) void k_som_pass_blk(const float *__restri
 }
 
 // Both passes in one sweep (blocked layout, window radius R <= 8 known at
-// compile time).  A wave owns one feature k and a strip of 64 map columns
-// x0 .. x0+63 and walks down the map one row at a time:
+// compile time).  A wave owns kSF consecutive features k0 .. k0+kSF-1 and a
+// strip of 64 map columns x0 .. x0+63 and walks down the map one row at a
+// time; the features' rows of one block are adjacent in memory, so a row's
+// loads and stores cover kSF x 256 contiguous bytes instead of 256 bytes
+// 4 MiB apart (d = 16,384), and they share the row's denominators.  Per
+// feature:
 //   - the row's 64 values plus R halo columns on each side (0 off the map)
 //     go to a per-wave LDS row, from which each lane sums its column's
 //     window along the row: X(y', x) = sum_t g(t) S(y', x + t);
@@ -274,26 +278,39 @@ struct Unroll<E, E> {
     __device__ __forceinline__ static void run(F &) {}
 };
 
+#ifndef VS_SOM_BLK_F
+#define VS_SOM_BLK_F 4
+#endif
+constexpr int kSF = VS_SOM_BLK_F;  // features per wave of the blocked sweep
+
 template <int R, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     const float *__restrict__ S, float *__restrict__ C, int32_t d, int32_t rows, int32_t cols,
     int32_t ntx, int64_t n_items, const float *__restrict__ g, const float *__restrict__ rden) {
     constexpr int P = 2 * R + 1;
     constexpr int W = 64 + 2 * R;
-    __shared__ float buf[kThreads / 64][W];
+    constexpr int F = kSF;
+    __shared__ float buf[kThreads / 64][F][W];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + wave;
     if (item >= n_items) return;
     // strips fastest: the waves of a workgroup sweep neighbouring strips of
-    // one feature together, so each one's halo columns are lines another has
-    // just fetched (ordering features fastest instead measured 23 % slower)
-    const int32_t k = (int32_t)(item / ntx);
-    const int32_t x0 = (int32_t)(item - (int64_t)k * ntx) * 64;
+    // the same F features together, so each one's halo columns are lines
+    // another has just fetched (ordering features fastest instead measured
+    // 23 % slower)
+    const int32_t kg = (int32_t)(item / ntx);
+    const int32_t x0 = (int32_t)(item - (int64_t)kg * ntx) * 64;
+    const int32_t k0 = kg * F;
     const int64_t D64 = 64 * (int64_t)d;
-    const float *Sk = S + (int64_t)k * 64;
-    float *Ck = C + (int64_t)k * 64;
-    float *row = buf[wave];
+    const float *Sk = S + (int64_t)k0 * 64;
+    float *Ck = C + (int64_t)k0 * 64;
+    // feature k0 + f sits 64 f floats after feature k0 in every block;
+    // features past d re-read feature d - 1 and are not stored
+    int32_t fo[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) fo[f] = (k0 + f < d ? f : d - 1 - k0) * 64;
+    const int nf = d - k0 < F ? d - k0 : F;  // features stored
 
     // each lane loads its own column and, lanes < 2R, one halo column:
     // left halo x0-R+lane (slot lane), right halo x0+64+lane-R (slot 64+lane)
@@ -332,17 +349,22 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
     float gw[R + 1];
 #pragma unroll
     for (int i = 0; i <= R; ++i) gw[i] = g[i];
-    float acc[P];
+    float acc[F][P];
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc[i] = 0.0f;
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int i = 0; i < P; ++i) acc[f][i] = 0.0f;
 
-    float vc, vh;
-    if constexpr (ALIGNED) {
-        vc = Sk[blk0 + lane];
-        vh = Sk[blk0 + hoff];
-    } else {
-        vc = Sk[at_rc(0, xcl)];
-        vh = Sk[at_rc(0, xhl)];
+    float vc[F], vh[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        if constexpr (ALIGNED) {
+            vc[f] = Sk[fo[f] + blk0 + lane];
+            vh[f] = Sk[fo[f] + blk0 + hoff];
+        } else {
+            vc[f] = Sk[fo[f] + at_rc(0, xcl)];
+            vh[f] = Sk[fo[f] + at_rc(0, xhl)];
+        }
     }
     // 1 / denominator of the output row finished after the current input row
     // (row yy - R; none for yy < R)
@@ -353,48 +375,78 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
         constexpr int u = decltype(U)::value;
         const int32_t yy = base + u;
         if (yy < rows) {
-            const float cc = c_ok ? vc : 0.0f;
-            const float hh = h_ok ? vh : 0.0f;
+            float cc[F], hh[F];
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                cc[f] = c_ok ? vc[f] : 0.0f;
+                hh[f] = h_ok ? vh[f] : 0.0f;
+            }
             const float rd = rnext;
             if constexpr (ALIGNED) {
-                vc = pn[lane];
-                vh = pn[hoff];
+#pragma unroll
+                for (int f = 0; f < F; ++f) vc[f] = pn[fo[f] + lane];
+#pragma unroll
+                for (int f = 0; f < F; ++f) vh[f] = pn[fo[f] + hoff];
                 rnext = pr[lane];
                 if (yy + 2 < rows) pn += rs;
                 if (yy + 2 - R >= 1 && yy + 2 - R <= rows - 1) pr += cols;
             } else {
                 const int32_t yn = yy + 1 < rows ? yy + 1 : rows - 1;
-                vc = Sk[at_rc(yn, xcl)];
-                vh = Sk[at_rc(yn, xhl)];
+                const int64_t an = at_rc(yn, xcl), hn = at_rc(yn, xhl);
+#pragma unroll
+                for (int f = 0; f < F; ++f) vc[f] = Sk[fo[f] + an];
+#pragma unroll
+                for (int f = 0; f < F; ++f) vh[f] = Sk[fo[f] + hn];
                 int32_t yd1 = yy + 1 - R;
                 yd1 = yd1 < 0 ? 0 : (yd1 >= rows ? rows - 1 : yd1);
                 rnext = rden[(int64_t)yd1 * cols + xcl];
             }
             asm volatile("" ::: "memory");
-            row[R + lane] = cc;
-            if (lane < 2 * R) row[hslot] = hh;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            float X = gw[0] * row[R + lane];
 #pragma unroll
-            for (int t = 1; t <= R; ++t)
-                X = __builtin_fmaf(gw[t], row[R + lane - t] + row[R + lane + t], X);
+            for (int f = 0; f < F; ++f) {
+                buf[wave][f][R + lane] = cc[f];
+                if (lane < 2 * R) buf[wave][f][hslot] = hh[f];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            float X[F];
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const float *row = buf[wave][f];
+                float x = gw[0] * row[R + lane];
+#pragma unroll
+                for (int t = 1; t <= R; ++t)
+                    x = __builtin_fmaf(gw[t], row[R + lane - t] + row[R + lane + t], x);
+                X[f] = x;
+            }
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int sft = -R; sft <= R; ++sft) {
                 const int q = (u + sft + 2 * P) % P;  // constant once unrolled
-                acc[q] = __builtin_fmaf(gw[sft < 0 ? -sft : sft], X, acc[q]);
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    acc[f][q] = __builtin_fmaf(gw[sft < 0 ? -sft : sft], X[f], acc[f][q]);
             }
             constexpr int qd = (u - R + 2 * P) % P;
             const int32_t yd = yy - R;
             if constexpr (ALIGNED) {
                 if (yd >= 0) {
-                    if (rd > 0.0f) po[lane] = acc[qd] * rd;
+                    if (rd > 0.0f) {
+#pragma unroll
+                        for (int f = 0; f < F; ++f)
+                            if (f < nf) po[fo[f] + lane] = acc[f][qd] * rd;
+                    }
                     po += rs;
                 }
             } else {
-                if (yd >= 0 && c_ok && rd > 0.0f) Ck[at_rc(yd, xc)] = acc[qd] * rd;
+                if (yd >= 0 && c_ok && rd > 0.0f) {
+                    const int64_t ao = at_rc(yd, xc);
+#pragma unroll
+                    for (int f = 0; f < F; ++f)
+                        if (f < nf) Ck[fo[f] + ao] = acc[f][qd] * rd;
+                }
             }
-            acc[qd] = 0.0f;
+#pragma unroll
+            for (int f = 0; f < F; ++f) acc[f][qd] = 0.0f;
         }
     };
     for (; base < rows; base += P) Unroll<0, P>::run(step);
@@ -403,11 +455,16 @@ __global__ __launch_bounds__(kThreads) void k_som_smooth_blk(
         const int32_t y = rows - R + j;
         if (y < 0 || !c_ok) continue;
         const int q = y % P;
-        float v = 0.0f;
-#pragma unroll
-        for (int qq = 0; qq < P; ++qq) v = qq == q ? acc[qq] : v;
         const float rd = rden[(int64_t)y * cols + xc];
-        if (rd > 0.0f) Ck[at_rc(y, xc)] = v * rd;
+        if (!(rd > 0.0f)) continue;
+        const int64_t ao = at_rc(y, xc);
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            float v = 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < P; ++qq) v = qq == q ? acc[f][qq] : v;
+            if (f < nf) Ck[fo[f] + ao] = v * rd;
+        }
     }
 }
 
@@ -665,7 +722,7 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
     }
     if (blocked && R >= 1 && R <= 8) {
         const int32_t ntx = (a.cols + 63) / 64;
-        const int64_t items = (int64_t)a.d * ntx;
+        const int64_t items = (int64_t)((a.d + kSF - 1) / kSF) * ntx;
         const dim3 gw((unsigned)((items + 3) / 4));
 #define VS_SMOOTH(RR)                                                                          \
     case RR:                                                                                   \
