@@ -440,6 +440,27 @@ def run_csr_blocked(indptr, indices, values, CT, metric, pad=0):
     return idx.cpu().numpy(), score.cpu().numpy()
 
 
+@pytest.mark.parametrize("metric", [0, 3])
+def test_csr_unsorted_rows(metric, chunk):
+    """Column order inside a row is free (only uniqueness is required): rows
+    whose entries are shuffled meet the oracle's bar, and the blocked layout
+    still agrees with the plain one bit for bit."""
+    indptr, indices, values, CT = csr_case(70, 300, 1000, 0.05, key=77 + metric)
+    (r,) = synth.rng_children(3100 + metric, 1)
+    ix, vv = indices.copy(), values.copy()
+    for i in range(len(indptr) - 1):
+        lo, hi = int(indptr[i]), int(indptr[i + 1])
+        perm = r.permutation(hi - lo)
+        ix[lo:hi] = indices[lo:hi][perm]
+        vv[lo:hi] = values[lo:hi][perm]
+    assert not np.array_equal(ix, indices)
+    csr_parity(indptr, ix, vv, CT, metric)
+    a = run_csr(indptr, ix, vv, CT, metric)
+    b = run_csr_blocked(indptr, ix, vv, CT, metric)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("nc,pad", [(1, 0), (63, 0), (64, 0), (700, 3), (1030, 0), (1028, 64)])
 def test_csr_block_codebook_layout(nc, pad):
     """The blocked copy holds feature k of neuron 64 b + j at (b d + k) 64 + j
