@@ -11,6 +11,14 @@ query that equals a candidate), where a relative bound is meaningless: the
 expanded form |q|^2 + |c|^2 - 2 q.c loses about eps32 * (|q|^2 + |c|^2) to
 cancellation, so the squared-L2 floor is 1e-2 * (|q|^2 + |c*|^2) (score
 tolerance 1e-6 * (|q|^2 + |c*|^2)); cosines of unit rows are O(1), floor 1e-2.
+The floor keeps the 1e-4 relative bound for every s* above it; at s* = 0
+exactly it is tighter than what fp32 guarantees: |q|^2, |c|^2 and q.c are fp32
+sums of d products, each within gamma_d = d u / (1 - d u) (u = 2^-24) of its
+value in any order, so the worst case is 2 gamma_{d+1} (|q|^2 + |c|^2), and
+rows searched against themselves measured up to about 1.1 sqrt(d) u
+(|q|^2 + |c|^2), above 1e-6 (|q|^2 + |c|^2) for some rows at d = 256 and 768.
+Exact self-matches are therefore checked against the worst-case bound
+(``self_match_tol``), not through this rule.
 Exact duplicates are additionally required to return the lowest index (the
 tests that build duplicates check idx directly).
 """
@@ -18,6 +26,18 @@ import numpy as np
 
 REL_SCORE = 1e-4
 REL_GAP = 1e-5
+
+
+U32 = 2.0 ** -24
+
+
+def self_match_tol(C):
+    """fp32 worst case of the expanded form at s* = 0 for rows C searched
+    against themselves: 2 gamma_{d+1} (|c|^2 + |c|^2)."""
+    C64 = C.astype(np.float64)
+    n = C.shape[1] + 1
+    gamma = n * U32 / (1.0 - n * U32)
+    return 2.0 * gamma * 2.0 * np.einsum("ij,ij->i", C64, C64)
 
 
 def l2_floor(Q, C, o_idx):

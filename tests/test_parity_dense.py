@@ -11,7 +11,7 @@ import pytest
 import oracle
 import synth
 from goldens import hand_cases
-from parity import check, l2_floor
+from parity import REL_SCORE, check, l2_floor, self_match_tol
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -259,3 +259,31 @@ def test_workload_5_subset():
                          l2_floor(Qs, w["C"], o_idx),
                          lambda r, c: oracle.pair_values(Qs, w["C"], 0, r, c))
     assert not fails, fails
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["512x512_codebook_l2", "diversity_table_cos"])
+def test_full_size_self_search(which):
+    """A table searched against itself: every row is its own best candidate
+    (squared L2: distance 0 against |c_i - c_j|^2 of about 2d for the other
+    N(0,1) rows; cosine on unit rows: 1 against O(1/sqrt(d))), a property
+    that holds at any size, here at full size with no oracle in the loop:
+    the 262,144 x 256 codebook (32-query kernel, 1,024 x 4,096 tiles) and
+    the 8,359 x 768 unit-row table (16-query kernel, ragged last tiles)."""
+    if which == "512x512_codebook_l2":
+        C, metric = synth.workload(5)["C"], 0
+    else:
+        C, metric = synth.workload(3)["C"], 2
+    Cd = to_dev(C)
+    idx, score = vs.vs_bmu_search(Cd, Cd, metric)
+    torch.cuda.synchronize()
+    idx, score = idx.cpu().numpy(), score.cpu().numpy()
+    n = C.shape[0]
+    assert np.array_equal(idx, np.arange(n, dtype=idx.dtype))
+    if metric == 0:
+        # s* = 0: the fp32 worst case of the expanded form (parity.py)
+        tol = self_match_tol(C)
+        assert (score >= 0).all() and (score <= tol).all(), float((score / tol).max())
+    else:
+        sq = np.einsum("ij,ij->i", C.astype(np.float64), C.astype(np.float64))
+        assert np.allclose(score, sq, rtol=REL_SCORE, atol=0)
