@@ -179,10 +179,33 @@ def _check(rc: int, where: str):
         raise VsError(rc, where)
 
 
+def _out(t, name, dtype, shape, device, want: bool = True):
+    """A caller's output tensor, checked (device, dtype, contiguity, at least
+    the elements the call writes), or a new one; None when not wanted."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device) if want else None
+    _dev(t, name, dtype)
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    n = 1
+    for v in (shape if isinstance(shape, tuple) else (shape,)):
+        n *= max(int(v), 0)
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call writes {n}")
+    return t
+
+
 def _workspace(nbytes: int, device, workspace):
     torch = _torch()
     if workspace is None:
         return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace must be a CUDA (HIP) torch tensor")
+    if workspace.device != torch.device(device):
+        raise ValueError(f"workspace is on {workspace.device}, the inputs on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small")
     return workspace
@@ -203,10 +226,8 @@ def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, worksp
     if C.shape[1] != d:
         raise ValueError("Q and C must have the same number of columns")
     dev = Q.device
-    if idx_out is None:
-        idx_out = torch.empty(nq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nq, dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, nq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
     need = L.vs_bmu_search_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -232,13 +253,13 @@ def vs_bmu_search_unfused(Q, C, metric=VS_L2SQ_MIN, S=None, idx_out=None, score_
     dev = Q.device
     if S is None:
         S = torch.empty((nq, (nc + 63) // 64 * 64), dtype=torch.float32, device=dev)
-    elif S.dtype != torch.float32 or S.dim() != 2 or S.shape[0] < nq or S.shape[1] < nc \
+    elif not isinstance(S, torch.Tensor) or not S.is_cuda or S.device != dev \
+            or S.dtype != torch.float32 or S.dim() != 2 or S.shape[0] < nq or S.shape[1] < nc \
             or S.stride(1) != 1 or S.stride(0) % 4:
-        raise ValueError("S must be a float32 nq x ld_s matrix (ld_s >= nc, ld_s % 4 == 0)")
-    if idx_out is None:
-        idx_out = torch.empty(nq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nq, dtype=torch.float32, device=dev)
+        raise ValueError("S must be a float32 nq x ld_s matrix (ld_s >= nc, ld_s % 4 == 0) "
+                         "on the device of Q")
+    idx_out = _out(idx_out, "idx_out", torch.int32, nq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
     need = L.vs_bmu_search_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -270,10 +291,8 @@ def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=N
         raise ValueError("indices and values differ in length")
     d, nc = CT.shape
     dev = CT.device
-    if idx_out is None:
-        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, max(nq, 0), dev)
+    score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -297,10 +316,7 @@ def vs_csr_block_codebook(CT, out=None):
         raise ValueError("CT must be a float32 CUDA matrix with unit column stride")
     d, nc = CT.shape
     n = L.vs_csr_blocked_bytes(nc, d) // 4
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=CT.device)
-    elif out.numel() < n or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous float32 tensor of at least {n} values")
+    out = _out(out, "out", torch.float32, n, CT.device)
     with torch.cuda.device(CT.device):
         rc = L.vs_csr_block_codebook(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
                                      _stream(CT.device))
@@ -330,10 +346,8 @@ def vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric=VS_L2SQ_MI
     if CB.numel() < nblk * 64 * d:
         raise ValueError("CB is smaller than the blocked layout of nc x d")
     dev = CB.device
-    if idx_out is None:
-        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, max(nq, 0), dev)
+    score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -357,10 +371,7 @@ def vs_csr_block_codebook_f16(CT, out=None):
         raise ValueError("CT must be a float32 CUDA matrix with unit column stride")
     d, nc = CT.shape
     n = L.vs_csr_blocked_f16_bytes(nc, d) // 2
-    if out is None:
-        out = torch.empty(n, dtype=torch.float16, device=CT.device)
-    elif out.numel() < n or out.dtype != torch.float16 or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous float16 tensor of at least {n} values")
+    out = _out(out, "out", torch.float16, n, CT.device)
     with torch.cuda.device(CT.device):
         rc = L.vs_csr_block_codebook_f16(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
                                          _stream(CT.device))
@@ -390,10 +401,8 @@ def vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, metric=VS_L
     if CB16.numel() < nblk * 128 * d:
         raise ValueError("CB16 is smaller than the blocked layout of nc x d")
     dev = CB16.device
-    if idx_out is None:
-        idx_out = torch.empty(max(nq, 0), dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(max(nq, 0), dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, max(nq, 0), dev)
+    score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -421,10 +430,8 @@ def vs_diversity_step(C, last_pick, mask_bits, idx_out=None, score_out=None, wor
     if tuple(mask_bits.shape) != (nseq, W):
         raise ValueError(f"mask_bits must be [{nseq}, {W}]")
     dev = C.device
-    if idx_out is None:
-        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     need = L.vs_diversity_step_workspace(n, d, nseq)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
@@ -450,10 +457,8 @@ def vs_diversity_step_ref(C, Q, mask_bits, idx_out=None, score_out=None, workspa
     if Q.shape[1] != d or tuple(mask_bits.shape) != (nseq, mask_words(n)):
         raise ValueError("Q or mask_bits disagree with C")
     dev = C.device
-    if idx_out is None:
-        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_step_ref(_ptr(C), n, d, _ptr(Q), _ptr(mask_bits), nseq,
@@ -491,9 +496,11 @@ def vs_diversity_gram(C, out=None):
     ldg = (n + 63) // 64 * 64
     if out is None:
         out = torch.empty((n, ldg), dtype=torch.float32, device=C.device)
-    elif out.dtype != torch.float32 or out.dim() != 2 or out.shape[0] != n \
-            or out.shape[1] < n or out.stride(1) != 1 or out.stride(0) % 4:
-        raise ValueError("out must be a float32 n x ldg matrix (ldg >= n, ldg % 4 == 0)")
+    elif not out.is_cuda or out.device != C.device or out.dtype != torch.float32 \
+            or out.dim() != 2 or out.shape[0] != n or out.shape[1] < n or out.stride(1) != 1 \
+            or out.stride(0) % 4:
+        raise ValueError("out must be a float32 n x ldg matrix (ldg >= n, ldg % 4 == 0) "
+                         "on the device of C")
     with torch.cuda.device(C.device):
         rc = L.vs_diversity_gram(_ptr(C), n, d, _ptr(out), out.stride(0), _stream(C.device))
     _check(rc, "vs_diversity_gram")
@@ -519,10 +526,8 @@ def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None
     if tuple(mask_bits.shape) != (nseq, W):
         raise ValueError(f"mask_bits must be [{nseq}, {W}]")
     dev = G.device
-    if idx_out is None:
-        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_step_gram(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(mask_bits),
                                       nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
@@ -551,10 +556,8 @@ def vs_diversity_run(C, seeds, mask_bits, steps: int, picks_out=None, scores_out
     nseq = seeds.numel()
     _mask_arg(mask_bits, nseq, n)
     dev = C.device
-    if picks_out is None:
-        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
-    if scores_out is None and want_scores:
-        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
+    scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_run(_ptr(C), n, d, _ptr(seeds), _ptr(mask_bits), nseq, int(steps),
@@ -576,15 +579,12 @@ def vs_diversity_run_ref(C, seeds, mask_bits, steps: int, Q=None, picks_out=None
     nseq = seeds.numel()
     _mask_arg(mask_bits, nseq, n)
     dev = C.device
-    if Q is None:
-        Q = torch.empty((nseq, d), dtype=torch.float32, device=dev)
+    Q = _out(Q, "Q", torch.float32, (nseq, d), dev)
     _dev(Q, "Q", torch.float32, 2)
     if tuple(Q.shape) != (nseq, d):
         raise ValueError("Q must be (nseq, d)")
-    if picks_out is None:
-        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
-    if scores_out is None and want_scores:
-        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
+    scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_run_ref(_ptr(C), n, d, _ptr(seeds), _ptr(Q), _ptr(mask_bits), nseq,
@@ -604,8 +604,9 @@ def vs_diversity_run_gram(G, seeds, mask_bits, steps: int, R=None, picks_out=Non
         if t is None:
             continue
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
-                or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride")
+                or t.dim() != 2 or t.stride(1) != 1 or t.device != G.device:
+            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride"
+                             " on the device of G")
     _dev(seeds, "seeds", torch.int32, 1)
     n = G.shape[0]
     nseq = seeds.numel()
@@ -613,10 +614,8 @@ def vs_diversity_run_gram(G, seeds, mask_bits, steps: int, R=None, picks_out=Non
         raise ValueError("G must be n x n and R nseq x n")
     _mask_arg(mask_bits, nseq, n)
     dev = G.device
-    if picks_out is None:
-        picks_out = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
-    if scores_out is None and want_scores:
-        scores_out = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+    picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
+    scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_run_gram(_ptr(G), n, G.stride(0), _ptr(seeds), _ptr(R),
                                      0 if R is None else R.stride(0), _ptr(mask_bits), nseq,
@@ -631,8 +630,8 @@ def vs_diversity_gram_sums(G, nseq: int, out=None):
     torch = _torch()
     n = G.shape[0]
     ldr = (n + 63) // 64 * 64
-    if out is None:
-        out = torch.empty((nseq, ldr), dtype=torch.float32, device=G.device)
+    out = _out(out, "out", torch.float32, (nseq, ldr), G.device).view(-1)[:nseq * ldr]
+    out = out.view(nseq, ldr)
     out.zero_()
     return out[:, :n]
 
@@ -646,8 +645,9 @@ def vs_diversity_step_gram_sum(G, last_pick, R, mask_bits, idx_out=None, score_o
     L = lib()
     for name, t in (("G", G), ("R", R)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
-                or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride")
+                or t.dim() != 2 or t.stride(1) != 1 or t.device != G.device:
+            raise ValueError(f"{name} must be a float32 CUDA matrix view with unit column stride"
+                             " on the device of G")
     _dev(last_pick, "last_pick", torch.int32, 1)
     n = G.shape[0]
     nseq = last_pick.numel()
@@ -659,10 +659,8 @@ def vs_diversity_step_gram_sum(G, last_pick, R, mask_bits, idx_out=None, score_o
     if tuple(mask_bits.shape) != (nseq, (n + 31) // 32):
         raise ValueError("mask_bits disagree with G and last_pick")
     dev = G.device
-    if idx_out is None:
-        idx_out = torch.empty(nseq, dtype=torch.int32, device=dev)
-    if score_out is None and want_score:
-        score_out = torch.empty(nseq, dtype=torch.float32, device=dev)
+    idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     with torch.cuda.device(dev):
         rc = L.vs_diversity_step_gram_sum(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(R),
                                           R.stride(0), _ptr(mask_bits), nseq, _ptr(idx_out),
@@ -744,8 +742,7 @@ def vs_som_qe(score, qe_out=None):
     L = lib()
     _dev(score, "score", torch.float32, 1)
     dev = score.device
-    if qe_out is None:
-        qe_out = torch.empty(1, dtype=torch.float64, device=dev)
+    qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     with torch.cuda.device(dev):
         rc = L.vs_som_qe(_ptr(score), score.numel(), _ptr(qe_out), _stream(dev))
     _check(rc, "vs_som_qe")
@@ -766,9 +763,9 @@ def vs_som_epoch(X, C, map_shape, sigma: float, radius: int, bmu_out=None, score
         raise ValueError("X and C must have the same number of columns")
     rows, cols = _map_shape(nc, map_shape)
     dev = C.device
-    bmu_out = torch.empty(n, dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
-    score_out = torch.empty(n, dtype=torch.float32, device=dev) if score_out is None else score_out
-    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    bmu_out = _out(bmu_out, "bmu_out", torch.int32, n, dev)
+    score_out = _out(score_out, "score_out", torch.float32, n, dev)
+    qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_workspace(n, rows, cols, d), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_som_epoch(_ptr(X), n, d, _ptr(C), rows, cols, float(sigma), int(radius),
@@ -791,10 +788,9 @@ def vs_som_epoch_csr(indptr, indices, values, CB, map_shape, d: int, sigma: floa
     if CB.numel() < ((nc + 63) // 64) * 64 * d:
         raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
     dev = CB.device
-    bmu_out = torch.empty(max(n, 0), dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
-    score_out = (torch.empty(max(n, 0), dtype=torch.float32, device=dev) if score_out is None
-                 else score_out)
-    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    bmu_out = _out(bmu_out, "bmu_out", torch.int32, n, dev)
+    score_out = _out(score_out, "score_out", torch.float32, n, dev)
+    qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_som_epoch_csr(_ptr(indptr), _ptr(indices) if nnz else None,
@@ -813,9 +809,7 @@ def vs_csr_blocked_to_f16(CB, nc: int, d: int, out=None):
     _dev(CB, "CB", torch.float32, 1)
     if CB.numel() < ((nc + 63) // 64) * 64 * d:
         raise ValueError("CB is smaller than the blocked layout of nc x d")
-    if out is None:
-        out = torch.empty(L.vs_csr_blocked_f16_bytes(nc, d) // 2, dtype=torch.float16,
-                          device=CB.device)
+    out = _out(out, "out", torch.float16, L.vs_csr_blocked_f16_bytes(nc, d) // 2, CB.device)
     with torch.cuda.device(CB.device):
         rc = L.vs_csr_blocked_to_f16(_ptr(CB), nc, d, _ptr(out), _stream(CB.device))
     _check(rc, "vs_csr_blocked_to_f16")
@@ -836,13 +830,10 @@ def vs_som_epoch_csr_f16(indptr, indices, values, CB, map_shape, d: int, sigma: 
     if CB.numel() < ((nc + 63) // 64) * 64 * d:
         raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
     dev = CB.device
-    if CB16 is None:
-        CB16 = torch.empty(L.vs_csr_blocked_f16_bytes(nc, d) // 2, dtype=torch.float16,
-                           device=dev)
-    bmu_out = torch.empty(max(n, 0), dtype=torch.int32, device=dev) if bmu_out is None else bmu_out
-    score_out = (torch.empty(max(n, 0), dtype=torch.float32, device=dev) if score_out is None
-                 else score_out)
-    qe_out = torch.empty(1, dtype=torch.float64, device=dev) if qe_out is None else qe_out
+    CB16 = _out(CB16, "CB16", torch.float16, L.vs_csr_blocked_f16_bytes(nc, d) // 2, dev)
+    bmu_out = _out(bmu_out, "bmu_out", torch.int32, n, dev)
+    score_out = _out(score_out, "score_out", torch.float32, n, dev)
+    qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
     with torch.cuda.device(dev):
         rc = L.vs_som_epoch_csr_f16(_ptr(indptr), _ptr(indices) if nnz else None,
@@ -863,8 +854,7 @@ def vs_candidate_norms(C, feature_major: bool = False, out=None):
         d, nc = C.shape
     else:
         nc, d = C.shape
-    if out is None:
-        out = torch.empty(nc, dtype=torch.float32, device=C.device)
+    out = _out(out, "out", torch.float32, nc, C.device)
     with torch.cuda.device(C.device):
         rc = L.vs_candidate_norms(_ptr(C), nc, d, int(bool(feature_major)), _ptr(out),
                                   _stream(C.device))

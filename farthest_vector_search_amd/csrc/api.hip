@@ -788,6 +788,7 @@ VS_API int vs_som_update_csr(const int32_t *indptr, const int32_t *indices, cons
     a.indptr = indptr;
     a.indices = indices;
     a.values = values;
+    a.nnz = nnz;
     a.n = n;
     a.d = d;
     a.bmu = bmu;

@@ -7,8 +7,8 @@
 // rows: +-q.c), then per query the best candidate with the lowest index on
 // ties.  Sources (web pages, by title and section):
 //  - "From 80x to 385x: A Best-Matching-Unit Search at the L2 Roof ..."
-//    (summary), section 3: the BMU search, with the argmin fused into the
-//    product so the score block is never materialised;
+//    (summary), section 3: the BMU search; the arg-min there is taken inside
+//    the distance kernel, so no query x neuron distance is ever stored;
 //  - "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache Locality",
 //    "Intended Behavior": walk the candidates in tiles, all workgroups on the
 //    same tile, the running best carried across tiles (never reset); the

@@ -35,8 +35,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // sequence's centroid ranks candidates as C[j] . sum_p C[p] = sum_p G[p][j]
 // does (p over the sequence's rows so far); R[s] keeps that running sum of
 // Gram rows.  A step first adds the reference's row, R[s] += G[pick[s]],
-// then takes the masked arg-min of R[s]; masked columns are neither read nor
-// updated (they are never candidates again).
+// then takes the masked arg-min of R[s].  Masked columns are never candidates
+// again, so their entries of R[s] are left unspecified: a group of four
+// columns is skipped only when all four are masked, otherwise the whole
+// group's sums are read and updated.
 constexpr int kWPS = 4;
 
 template <bool SUM>

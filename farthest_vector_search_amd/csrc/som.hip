@@ -86,11 +86,12 @@ __global__ __launch_bounds__(kThreads) void k_som_scatter_rows(const float *__re
 }
 
 // CSR rows: one wave per input, lanes along its stored entries; entries with
-// a column outside [0, d) are skipped.
+// a column outside [0, d) are skipped, and a row whose span is not inside
+// [0, nnz] pulls nothing (nothing outside the caller's arrays is read).
 __global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
     const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
-    const float *__restrict__ values, int64_t n, int32_t d, const int32_t *__restrict__ bmu,
-    int64_t nc, float *S, int32_t *cnt) {
+    const float *__restrict__ values, int64_t nnz, int64_t n, int32_t d,
+    const int32_t *__restrict__ bmu, int64_t nc, float *S, int32_t *cnt) {
     const int lane = threadIdx.x & 63;
     const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
     for (int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); i < n;
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_som_scatter_csr(
         const int64_t b = bmu[i];
         if (b < 0 || b >= nc) continue;
         const int64_t lo = indptr[i], hi = indptr[i + 1];
+        if (lo < 0 || hi < lo || hi > nnz) continue;
         for (int64_t p = lo + lane; p < hi; p += 64) {
             const int32_t k = indices[p];
             if (k >= 0 && k < d) unsafeAtomicAdd(S + at<true>(b, k, d), values[p]);
@@ -689,7 +691,7 @@ hipError_t launch_som_update(const SomArgs &a, hipStream_t st, int n_cu) {
         const dim3 gs(grid_for(a.n * 64, n_cu));  // one wave per input
         if (blocked)
             hipLaunchKernelGGL(k_som_scatter_csr, gs, dim3(kThreads), 0, st, a.indptr, a.indices,
-                               a.values, a.n, a.d, a.bmu, nc, a.S, a.cnt);
+                               a.values, a.nnz, a.n, a.d, a.bmu, nc, a.S, a.cnt);
         else
             hipLaunchKernelGGL(k_som_scatter_rows, gs, dim3(kThreads), 0, st, a.X, a.n, a.d,
                                a.bmu, nc, a.S, a.cnt);

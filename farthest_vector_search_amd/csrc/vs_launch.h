@@ -88,6 +88,7 @@ struct SomArgs {
     const float *X;                       // dense rows, n x d
     const int32_t *indptr, *indices;      // CSR rows
     const float *values;
+    int64_t nnz;                          // CSR entries the caller's arrays hold
     int64_t n;
     int32_t d;
     const int32_t *bmu;                   // n

@@ -300,7 +300,10 @@ int vs_diversity_gram(const float *C, int64_t n, int32_t d, float *G, int64_t ld
  *                           the unmasked j with the smallest R[s][j] (lowest
  *                           index on ties), sets its bit, and reports
  *                           score_out = R[s][pick].  Columns already masked
- *                           are neither read nor updated.  last_pick outside
+ *                           are never candidates again and their entries of
+ *                           R[s] hold unspecified values (the scan works on
+ *                           groups of four columns and skips a group only
+ *                           when all four are masked).  last_pick outside
  *                           [0, n): -1, mask and R[s] unchanged.  No
  *                           workspace.
  */
@@ -340,7 +343,10 @@ int vs_diversity_step_gram(const float *G, int64_t n, int64_t ldg, const int32_t
  *   vs_som_update      dense rows X (n x d) and bmu int32[n]; C (rows*cols x
  *                      d, neuron-major) is updated in place.
  *   vs_som_update_csr  CSR rows (as vs_bmu_search_csr; entries with a
- *                      column outside [0, d) are skipped); CB is the
+ *                      column outside [0, d) are skipped, and a row whose
+ *                      span indptr[i] .. indptr[i+1] is not inside
+ *                      [0, nnz] pulls nothing, whatever its BMU; nothing
+ *                      outside the arrays is read); CB is the
  *                      64-neuron blocked codebook of vs_csr_block_codebook,
  *                      updated in place.
  *   vs_som_qe          quantisation error: mean over the n inputs of
@@ -399,6 +405,11 @@ int vs_som_epoch_csr_f16(const int32_t *indptr, const int32_t *indices, const fl
  * Squared L2 norms of candidates, float32, fixed summation order (the same
  * values the searches use).  feature_major == 0: C is nc x d (row j);
  * otherwise C is d x nc (column j).  norms_out is float32[nc].
+ * [Issue 9-014, "FP16 storage path": the norm accumulators of the distance
+ * loop stay fp32 whatever the storage type; "From 80x to 385x ...",
+ * section 3: squared-L2 BMU search, the codebook held feature-major.  The
+ * pages compute the norms inside the scan; this call hoists the candidates'
+ * norms out of it so the scan ranks by |c|^2 - 2 q.c.]
  */
 int vs_candidate_norms(const float *C, int64_t nc, int32_t d, int32_t feature_major,
                        float *norms_out, void *stream);

@@ -28,19 +28,30 @@ L2SQ_MIN, L2SQ_MAX, COS_MAX, COS_MIN = 0, 1, 2, 3
 _libs: dict[int, ctypes.CDLL] = {}
 
 
-def lib_path(mutant: int = 0) -> str:
-    name = "liboracle.so" if mutant == 0 else f"liboracle_m{mutant}.so"
+# ORACLE_SANITIZE=1 loads the AddressSanitizer + UndefinedBehaviorSanitizer
+# build instead of the plain one (the process must preload gcc's libasan;
+# see tests/test_oracle_sanitized.py)
+SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def lib_path(mutant: int = 0, sanitize: bool = False) -> str:
+    name = "liboracle" + (f"_m{mutant}" if mutant else "") + ("_san" if sanitize else "") + ".so"
     return os.path.join(_HERE, name)
 
 
-def build(mutant: int = 0, force: bool = True) -> str:
-    """Compile oracle.c with gcc.  ``mutant`` > 0 plants the numbered mistake."""
-    out = lib_path(mutant)
+def build(mutant: int = 0, force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc.  ``mutant`` > 0 plants the numbered mistake;
+    ``sanitize`` builds it with AddressSanitizer and UndefinedBehaviorSanitizer
+    (bounds, use-after-free, signed overflow, misaligned access, ...)."""
+    out = lib_path(mutant, sanitize)
     if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
         return out
     tmp = out + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           f"-DORC_MUTANT={int(mutant)}", _SRC, "-o", tmp, "-lm"]
+           *(SAN_FLAGS if sanitize else []), f"-DORC_MUTANT={int(mutant)}", _SRC, "-o", tmp,
+           "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -49,7 +60,7 @@ def build(mutant: int = 0, force: bool = True) -> str:
 def _load(mutant: int = 0) -> ctypes.CDLL:
     if mutant in _libs:
         return _libs[mutant]
-    path = build(mutant, force=False)
+    path = build(mutant, force=False, sanitize=SANITIZE)
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64

@@ -198,8 +198,15 @@ void orc_pair_values(const float *Q, const float *C, int64_t d, int metric,
                      int64_t npairs, const int64_t *qi, const int64_t *cj,
                      double *value)
 {
-    for (int64_t p = 0; p < npairs; ++p)
+    for (int64_t p = 0; p < npairs; ++p) {
+#if ORC_MUTANT == 17 /* MUTANT 17: query and candidate indices exchanged */
+        value[p] = pair_value(Q + cj[p] * d, C + qi[p] * d, d, metric);
+#elif ORC_MUTANT == 18 /* MUTANT 18: candidate rows one float too short */
+        value[p] = pair_value(Q + qi[p] * d, C + cj[p] * (d > 1 ? d - 1 : d), d, metric);
+#else
         value[p] = pair_value(Q + qi[p] * d, C + cj[p] * d, d, metric);
+#endif
+    }
 }
 
 /* squared norms of rows (feature_major == 0: X is rows x d) or of columns

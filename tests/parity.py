@@ -97,6 +97,9 @@ def check(idx_g, score_g, o_idx, o_val, o_gap, metric, floor, pick_values, legal
             r = near[~good][0]
             fails.append(f"{(~good).sum()} picks outside the gap, e.g. row {r}: gpu {idx_g[r]}")
         n_gap = int(good.sum())
+    # rows whose scale is the floor rather than |s*| (the relative bound
+    # became an absolute one there)
+    floor_bound = int((np.broadcast_to(floor, o_val.shape)[rows] > np.abs(s)).sum())
     stats = dict(rows=int(o_idx.size), same_index=int((~mism).sum()), gap_accepted=n_gap,
-                 empty=int(none.sum()))
+                 empty=int(none.sum()), floor_bound=floor_bound)
     return fails, stats

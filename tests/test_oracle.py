@@ -4,7 +4,9 @@ The oracle is checked against things other than itself:
   * hand-enumerated cases under tests/golden/ (plane geometry, cited);
   * independent library routines: scipy.spatial.distance.cdist and
     sklearn's pairwise_distances_argmin (numpy's argmin documents that the
-    first occurrence wins, which is the lowest-index tie-break);
+    first occurrence wins, which is the lowest-index tie-break); the values
+    of single (query, candidate) pairs, which the parity rule uses to judge
+    near-tie picks, against cdist entries and a hand-worked case;
   * closed forms (a query equal to a candidate, an antipodal unit vector);
   * invariants: split/tiling invariance of the arg-reduction (associativity of
     max, "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache Locality",
@@ -26,7 +28,7 @@ import oracle
 import synth
 from goldens import csr_cases, diversity_centroid, diversity_walk, hand_cases
 
-MUTANTS = list(range(1, 17))
+MUTANTS = list(range(1, 19))
 
 
 def _close(a, b, rel=1e-12, abs_=1e-12):
@@ -179,6 +181,43 @@ def pin_translation(m=0):
         i1, v1, _ = oracle.dense(Q + t, C + t, metric, mutant=m)
         if not (i0 == i1).all() or not (v0 == v1).all():
             bad.append(f"translation metric {metric}")
+    return bad
+
+
+def pin_pair_values(m=0):
+    """orc_pair_values against scipy's cdist entries: every metric, queries
+    and candidates of different counts in both directions, (query, candidate)
+    pairs drawn with repeats and in no order, plus a hand-worked case.  Q and
+    C are two slices of one buffer long enough that a build which reads rows
+    past either slice (indices exchanged, a wrong row stride) stays inside
+    memory and fails on the values instead of faulting."""
+    bad = []
+    rng = np.random.default_rng(1717)
+    for metric in range(4):
+        for nq, nc, d in ((13, 41, 7), (37, 5, 3), (6, 6, 1), (9, 200, 33)):
+            buf = rng.standard_normal((2 * (nq + nc), d)).astype(np.float32)
+            Q, C = buf[:nq], buf[nq:nq + nc]
+            qi = rng.integers(0, nq, 3 * (nq + nc))
+            cj = rng.integers(0, nc, qi.size)
+            qi[:4], cj[:4] = [0, 0, nq - 1, nq - 1], [nc - 1, nc - 1, 0, 0]  # repeats, ends
+            if metric in (0, 1):
+                D = cdist(Q.astype(np.float64), C.astype(np.float64), "sqeuclidean")
+            else:
+                D = 1.0 - cdist(Q.astype(np.float64), C.astype(np.float64), "cosine")
+            got = oracle.pair_values(Q, C, metric, qi, cj, mutant=m)
+            if not np.allclose(got, D[qi, cj], rtol=1e-12, atol=1e-12):
+                bad.append(f"pair values metric {metric} shape {(nq, nc, d)}")
+    # hand case: q0 = (1, 0), q1 = (0, 2); c0 = (3, 4), c1 = (1, 1), c2 = (-2, 0)
+    Q = np.array([[1, 0], [0, 2]], np.float32)
+    C = np.array([[3, 4], [1, 1], [-2, 0]], np.float32)
+    qi = np.array([0, 1, 1, 0, 0])
+    cj = np.array([0, 0, 2, 2, 1])
+    exp_l2 = [4 + 16, 9 + 4, 4 + 4, 9, 1]
+    exp_cos = [3 / 5, 8 / 10, 0.0, -1.0, 1 / math.sqrt(2)]
+    for metric, exp in ((0, exp_l2), (1, exp_l2), (2, exp_cos), (3, exp_cos)):
+        got = oracle.pair_values(Q, C, metric, qi, cj, mutant=m)
+        if not all(_close(g, e, 1e-12, 1e-12) for g, e in zip(got, exp)):
+            bad.append(f"pair values hand case metric {metric}: {list(got)}")
     return bad
 
 
@@ -462,6 +501,7 @@ def pin_centroid_relabel_and_scale(m=0):
 
 
 PINS = [pin_hand_cases, pin_csr_cases, pin_walk, pin_library, pin_sklearn, pin_closed_forms,
+        pin_pair_values,
         pin_split_invariance, pin_permutation, pin_translation, pin_duplicates,
         pin_csr_vs_dense, pin_replay, pin_gram, pin_sqnorms, pin_som_group_mean,
         pin_som_single_input, pin_som_scipy, pin_som_global_mean, pin_som_symmetry,

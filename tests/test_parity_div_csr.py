@@ -579,9 +579,9 @@ def test_csr_bad_rows_skipped(chunk):
 
 
 @pytest.mark.slow
-def test_workload_4_sampled():
+def test_workload_4_seeded_rows():
     """32,768 CSR rows (~164 nnz of 16,384) x 65,536 neurons at full size;
-    256 seeded rows are checked one by one against the oracle."""
+    4,096 seeded rows are checked one by one against the oracle."""
     w = synth.workload(4)
     idx, score = run_csr(w["indptr"], w["indices"], w["values"], w["CT"], 0, pad=64)
     # the blocked layout (the form the benchmark times) gives the same bits
@@ -589,7 +589,7 @@ def test_workload_4_sampled():
     assert np.array_equal(idx, bidx)
     assert np.array_equal(score.view(np.uint32), bscore.view(np.uint32))
     del bidx, bscore
-    sel = synth.sample_queries(w["nq"], 256, key=4)
+    sel = synth.sample_queries(w["nq"], 4096, key=4)
     ptr = w["indptr"]
     sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
     sub_idx = np.concatenate([w["indices"][ptr[i]:ptr[i + 1]] for i in sel])
@@ -608,7 +608,9 @@ def test_workload_4_sampled():
                                         col_sq=col_sq[j:j + 1])[1][0]
                              for i, j in zip(r, c)]))
     assert not fails, fails
+    assert stats["rows"] == 4096 and stats["floor_bound"] == 0, stats
     assert (idx >= 0).all()
+    print("workload 4 parity:", stats)
 
 
 @pytest.mark.slow

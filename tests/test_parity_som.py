@@ -181,6 +181,35 @@ def test_som_update_csr(rows, cols, d, n, sigma, R, density):
     assert not tail.any()
 
 
+def test_som_update_csr_bad_spans_pull_nothing():
+    """Rows whose indptr span is not inside [0, nnz] (lo < 0, hi < lo,
+    hi > nnz) pull nothing even with a valid BMU, and nothing outside the
+    CSR arrays is read; the other rows update as usual (the oracle sees the
+    bad rows with no BMU)."""
+    rows, cols, d, n = 6, 7, 20, 60
+    nc = rows * cols
+    (r,) = synth.rng_children(985, 1)
+    indptr, indices, values = synth.sparse_rows(r, n, d, 0.2)
+    nnz = int(indices.shape[0])
+    CT = synth.uniform01(r, (d, nc))
+    bmu = synth.random_indices(n, nc, key=986)
+    indptr = indptr.copy()
+    indptr[0] = -3                    # row 0: lo < 0
+    indptr[11] = indptr[10] - 1       # row 10: hi < lo (row 11 keeps a valid span)
+    indptr[n] = nnz + 50              # row n - 1: hi > nnz
+    bad = np.array([0, 10, n - 1])
+    bmu[bad] = 5                      # valid BMUs: they would pull neuron 5's window
+    CB = vs.vs_csr_block_codebook(T(CT))
+    vs.vs_som_update_csr(T(indptr), T(indices), T(values), T(bmu), CB, (rows, cols), d, 1.0, 2)
+    w_gpu = unblock(CB.cpu().numpy(), nc, d)
+    C_old = np.ascontiguousarray(CT.T)
+    o_bmu = bmu.copy()
+    o_bmu[bad] = -1
+    w_o, mass, den = oracle.som_update(indptr, indices, values, d, o_bmu, C_old, rows, cols,
+                                       1.0, 2, threads=8)
+    assert not check_update(w_gpu, C_old, w_o, mass, den, o_bmu, rows, cols, 2)
+
+
 # ------------------------------------------------------ quantisation error --
 
 @pytest.mark.parametrize("n", [0, 1, 2, 1023, 1024, 1025, 65536])
