@@ -8,6 +8,7 @@ calls raise.
 
 Functions (same names as the C entry points):
     vs_bmu_search(Q, C, metric)                        -> (idx, score)
+    vs_bmu_search_noalloc(Q, C, metric)                -> (idx, score), no workspace
     vs_bmu_search_unfused(Q, C, metric)                -> (idx, score) via a score block
     vs_bmu_search_csr(indptr, indices, values, CT, metric) -> (idx, score)
     vs_csr_block_codebook(CT)                          -> CB (64-neuron blocked copy)
@@ -36,7 +37,8 @@ STATUS = {0: "VS_OK", 1: "VS_ERR_NULL", 2: "VS_ERR_SHAPE", 3: "VS_ERR_METRIC",
           4: "VS_ERR_WORKSPACE", 5: "VS_ERR_ALIGN", 6: "VS_ERR_INDEX",
           7: "VS_ERR_UNSUPPORTED", 8: "VS_ERR_HIP"}
 
-EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_unfused",
+EXPORTS = ["vs_bmu_search_workspace", "vs_bmu_search", "vs_bmu_search_noalloc",
+           "vs_bmu_search_unfused",
            "vs_bmu_search_csr_workspace",
            "vs_bmu_search_csr", "vs_csr_blocked_bytes", "vs_csr_block_codebook",
            "vs_bmu_search_csr_blocked", "vs_csr_blocked_f16_bytes", "vs_csr_block_codebook_f16",
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.vs_bmu_search_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_workspace.restype = SZ
     L.vs_bmu_search.argtypes = [P, P, I64, I64, I32, I32, P, P, P, SZ, P]
+    L.vs_bmu_search_noalloc.argtypes = [P, P, I64, I64, I32, I32, P, P, P]
     L.vs_bmu_search_unfused.argtypes = [P, P, I64, I64, I32, I32, P, P, P, I64, P, SZ, P]
     L.vs_bmu_search_csr_workspace.argtypes = [I64, I64, I32, I32]
     L.vs_bmu_search_csr_workspace.restype = SZ
@@ -125,7 +128,8 @@ def lib() -> ctypes.CDLL:
     L.vs_status_str.argtypes = [ctypes.c_int]
     L.vs_status_str.restype = ctypes.c_char_p
     L.vs_version.restype = ctypes.c_char_p
-    for name in ("vs_bmu_search", "vs_bmu_search_unfused", "vs_bmu_search_csr",
+    for name in ("vs_bmu_search", "vs_bmu_search_noalloc", "vs_bmu_search_unfused",
+                 "vs_bmu_search_csr",
                  "vs_csr_block_codebook",
                  "vs_bmu_search_csr_blocked", "vs_csr_block_codebook_f16",
                  "vs_bmu_search_csr_blocked_f16", "vs_diversity_step", "vs_diversity_gram",
@@ -234,6 +238,31 @@ def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, worksp
         rc = L.vs_bmu_search(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out), _ptr(score_out),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search")
+    return idx_out, score_out
+
+
+def vs_bmu_search_noalloc(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None,
+                          want_score: bool = True):
+    """vs_bmu_search without a workspace: the library's own device scratch
+    array serves as one (at most 8 MiB of workspace; calls that overlap on
+    one GPU race).  Pass idx_out / score_out to make the call allocate
+    nothing at all."""
+    torch = _torch()
+    L = lib()
+    m = _metric(metric)
+    _dev(Q, "Q", torch.float32, 2)
+    _dev(C, "C", torch.float32, 2)
+    nq, d = Q.shape
+    nc = C.shape[0]
+    if C.shape[1] != d:
+        raise ValueError("Q and C must have the same number of columns")
+    dev = Q.device
+    idx_out = _out(idx_out, "idx_out", torch.int32, nq, dev)
+    score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
+    with torch.cuda.device(dev):
+        rc = L.vs_bmu_search_noalloc(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out),
+                                     _ptr(score_out), _stream(dev))
+    _check(rc, "vs_bmu_search_noalloc")
     return idx_out, score_out
 
 

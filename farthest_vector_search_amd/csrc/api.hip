@@ -181,27 +181,18 @@ VS_API size_t vs_bmu_search_workspace(int64_t nq, int64_t nc, int32_t d, int32_t
     return search_layout(nq, nc, metric).total;
 }
 
-VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
-                         int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
-                         size_t workspace_bytes, void *stream) {
-    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
-    if (nq < 0 || nq > kMaxIndex || nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxDim)
-        return VS_ERR_SHAPE;
-    if (nq == 0) return VS_OK;
-    if (!Q || !C || !idx_out || !workspace) return VS_ERR_NULL;
-    if (!al4(Q) || !al4(C) || !al4(idx_out) || !al4(score_out) || !al256(workspace))
-        return VS_ERR_ALIGN;
+// The dense search's kernel sequence over a workspace already checked to hold
+// search_layout(nq, nc, metric).total bytes (256-byte aligned).
+static int dense_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                        int32_t metric, int32_t *idx_out, float *score_out, char *ws,
+                        hipStream_t st, int n_cu) {
     const Layout L = search_layout(nq, nc, metric);
-    if (workspace_bytes < L.total) return VS_ERR_WORKSPACE;
-    int n_cu = 0;
-    if (const int s = device_ready(&n_cu)) return s;
-
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
     uint64_t *keys = reinterpret_cast<uint64_t *>(ws + L.keys);
     float *qn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.qn) : nullptr;
     float *cn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.cn) : nullptr;
 
+    // every buffer of the workspace is written before it is read: the keys by
+    // a fill kernel (no memset node), the norms by their own kernels
     VS_TRY_HIP(vs::launch_fill_keys(keys, nq, st));
     if (cn) VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, cn, st));
     if (qn && score_out) VS_TRY_HIP(vs::launch_row_sqnorms(Q, nq, d, qn, st));
@@ -221,6 +212,86 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     }
     VS_TRY_HIP(vs::launch_finalize(keys, qn, nq, metric, idx_out, score_out, st));
     return VS_OK;
+}
+
+// Checks shared by the dense search and its no-allocation variant.
+static int dense_check(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                       int32_t metric, const int32_t *idx_out, const float *score_out) {
+    if (metric < 0 || metric > 3) return VS_ERR_METRIC;
+    if (nq < 0 || nq > kMaxIndex || nc < 1 || nc > kMaxIndex || d < 1 || d > kMaxDim)
+        return VS_ERR_SHAPE;
+    if (nq == 0) return VS_OK;
+    if (!Q || !C || !idx_out) return VS_ERR_NULL;
+    if (!al4(Q) || !al4(C) || !al4(idx_out) || !al4(score_out)) return VS_ERR_ALIGN;
+    return VS_OK;
+}
+
+VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                         int32_t metric, int32_t *idx_out, float *score_out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (const int s = dense_check(Q, C, nq, nc, d, metric, idx_out, score_out)) return s;
+    if (nq == 0) return VS_OK;
+    if (!workspace) return VS_ERR_NULL;
+    if (!al256(workspace)) return VS_ERR_ALIGN;
+    if (workspace_bytes < search_layout(nq, nc, metric).total) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    return dense_search(Q, C, nq, nc, d, metric, idx_out, score_out,
+                        static_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream),
+                        n_cu);
+}
+
+// ---- dense search with no allocation ---------------------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the workspace of vs_bmu_search lives in this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (its name on the host is
+// a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and is
+// kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;  // 8 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch[64];  // device address of `scratch` per device (null until taken)
+}  // namespace
+
+static int scratch_ptr(char **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip = (int)e;
+        return VS_ERR_HIP;
+    }
+    if (dev < 0 || dev >= 64) return VS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_hip = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return VS_ERR_HIP;
+        }
+        g_scratch[dev] = p;
+    }
+    *out = static_cast<char *>(g_scratch[dev]);
+    return VS_OK;
+}
+
+VS_API int vs_bmu_search_noalloc(const float *Q, const float *C, int64_t nq, int64_t nc,
+                                 int32_t d, int32_t metric, int32_t *idx_out, float *score_out,
+                                 void *stream) {
+    if (const int s = dense_check(Q, C, nq, nc, d, metric, idx_out, score_out)) return s;
+    if (nq == 0) return VS_OK;
+    if (search_layout(nq, nc, metric).total > kNoAllocScratchBytes) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    char *ws = nullptr;
+    if (const int s = scratch_ptr(&ws)) return s;
+    return dense_search(Q, C, nq, nc, d, metric, idx_out, score_out, ws,
+                        reinterpret_cast<hipStream_t>(stream), n_cu);
 }
 
 // ---- unfused comparator: score block, then a per-row pass -------------------

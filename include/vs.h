@@ -95,6 +95,27 @@ int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_
                   size_t workspace_bytes, void *stream);
 
 /*
+ * vs_bmu_search with no device allocation and no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results (bit for bit) as vs_bmu_search; the workspace is a
+ * file-scope device array of the library, 8 MiB on every GPU the library
+ * runs on, held until the process ends.  Limit: the workspace
+ * vs_bmu_search_workspace(nq, nc, d, metric) would report must be at most
+ * 8,388,608 bytes (for squared L2 about 12 nq + 4 nc bytes, each part
+ * rounded up to 256: e.g. nq = 65,536 with nc up to 1,900,544; for cosine
+ * 8 nq bytes), else VS_ERR_WORKSPACE before anything is enqueued.  No
+ * hipMalloc, hipFree or other allocating call is made; the first call on a
+ * device looks up the array's device address once (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (each call rewrites what it reads before reading it), so calls
+ * that overlap on one GPU -- concurrent streams, or threads -- race and
+ * must be serialised by the caller.
+ */
+int vs_bmu_search_noalloc(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                          int32_t metric, int32_t *idx_out, float *score_out, void *stream);
+
+/*
  * Unfused comparator for the dense search [BMU, section 3 (the unfused
  * GEMM-then-argmin path the fused search is measured against) and section 4]:
  * the same MFMA arithmetic writes the whole score block S[q * ld_s + c] =
