@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark: query x candidate distance pairs per second on one MI355X.
 
-Default workload: the dense best-matching-unit search of a 128x128 SOM map --
-65,536 queries N(0,1) x 16,384 neurons N(0, 0.5), d = 256, squared-L2
-argmin -- with inputs resident in HBM.  One step = one vs_bmu_search call:
-candidate (and query) norms, the fused MFMA scan with its arg-reduction and
-merge, and the finalize kernel.
+Default workload: the dense best-matching-unit search of a 512x512 SOM map --
+65,536 queries x 262,144 neurons, both N(0,1), d = 256, squared-L2 argmin --
+with inputs resident in HBM.  One step = one vs_bmu_search call: candidate
+(and query) norms, the fused MFMA scan with its arg-reduction and merge, and
+the finalize kernel.
 
-Output: one JSON line (rank 0) with the throughput, the roofline of the
-dominant kernel (its algorithmic FLOPs per launch over its average launch
-time, taken with HIP events on the launch stream by the library's timing
-hook) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
-same workload on the host's cores.
+Output: one JSON line with the throughput (whole timed region), the per-step
+median / min / max from HIP events between the steps, the spread over
+independent process replicates, the roofline of the dominant kernel (its
+algorithmic FLOPs per launch over its average launch time, taken with HIP
+events on the launch stream by the library's timing hook), a CPU baseline --
+the fp64 oracle timed on the workload's checked set on the host's cores, plus
+a one-thread rate -- and the parity verdict of the timed run's own output
+against that oracle run (the acceptance rule of tests/parity.py).  The small
+32x32-map workload adds its per-call latency against an empty-kernel floor on
+the same stream, eager and as a captured HIP graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-                    [--no-cpu-baseline] [--traffic-json FILE]
+                    [--replicates R] [--no-cpu-baseline] [--traffic-json FILE]
                     [--som [--som-sigma S --som-radius R]]
 
 --som turns a BMU workload (1, 2, 4, 5) into SOM training: one step = one
@@ -55,8 +60,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (and with it the parity verdict)")
+    ap.add_argument("--replicates", type=int, default=3,
+                    help="independent processes timing the same steps (this one included); "
+                         "their spread is reported.  Runs under a profiler use 1")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--dense-mode", choices=["fused", "unfused"], default="fused",
                     help="dense workloads: 'unfused' writes the whole score block, then "
                          "ranks each row in a second pass (the fusion comparator)")
@@ -164,6 +174,7 @@ def setup(k, torch, vs, a):
         else:
             def step():
                 vs.vs_bmu_search(Q, C, 0, idx_out=idx, score_out=score, workspace=ws)
+        w["gpu_out"] = dict(idx=idx, score=score)
         pairs = w["nq"] * w["nc"]
         flops = 2.0 * w["d"] * pairs
         cfg = dict(workload=w["name"], nq=w["nq"], nc=w["nc"], d=w["d"], metric="l2sq_min")
@@ -182,6 +193,10 @@ def setup(k, torch, vs, a):
         mask0 = torch.from_numpy(m0.view(np.int32)).to(dev)
         mask = mask0.clone()
         picks = torch.empty((steps, nseq), dtype=torch.int32, device=dev)
+        # the timed runs write every pick's score too (one 4-byte store per
+        # sequence and step), so the timed output is the one the oracle checks
+        scores = torch.empty((steps, nseq), dtype=torch.float32, device=dev)
+        w["gpu_out"] = dict(picks=picks, scores=scores, mask=mask, steps=steps)
         ws = torch.empty(vs.lib().vs_diversity_step_workspace(n, d, nseq), dtype=torch.uint8,
                          device=dev)
 
@@ -203,14 +218,14 @@ def setup(k, torch, vs, a):
                     mask.copy_(mask0)
                     G = vs.vs_diversity_gram(C, out=Gbuf)
                     vs.vs_diversity_run_gram(G, seeds, mask, steps, R=Rbuf[:, :n],
-                                             picks_out=picks, want_scores=False)
+                                             picks_out=picks, scores_out=scores)
                 per_col = 12
             else:
                 def step():
                     mask.copy_(mask0)
                     G = vs.vs_diversity_gram(C, out=Gbuf)
                     vs.vs_diversity_run_gram(G, seeds, mask, steps, picks_out=picks,
-                                             want_scores=False)
+                                             scores_out=scores)
                 per_col = 4
             w["run_bytes"] = nseq * (steps * (per_col * live + 4) + 8 * W + 4)
         elif a.div_ref == "centroid":
@@ -221,14 +236,15 @@ def setup(k, torch, vs, a):
             def step():
                 mask.copy_(mask0)
                 vs.vs_diversity_run_ref(C, seeds, mask, steps, Q=Q, picks_out=picks,
-                                        workspace=ws, want_scores=False)
+                                        scores_out=scores, workspace=ws)
         else:
             def step():
                 mask.copy_(mask0)
-                vs.vs_diversity_run(C, seeds, mask, steps, picks_out=picks, workspace=ws,
-                                    want_scores=False)
+                vs.vs_diversity_run(C, seeds, mask, steps, picks_out=picks, scores_out=scores,
+                                    workspace=ws)
         pairs = nseq * n * steps
         flops = 2.0 * d * pairs
+        w["reference"] = a.div_ref
         cfg = dict(workload=w["name"], n=n, d=d, nseq=nseq, steps_per_run=steps,
                    metric="cos_min_masked", mode=a.div_mode, reference=a.div_ref)
         return w, step, pairs, flops, steps, cfg
@@ -271,6 +287,7 @@ def setup(k, torch, vs, a):
             vs.vs_csr_block_codebook(CT, out=CB)
             vs.vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, 0, d=w["d"],
                                          idx_out=idx, score_out=score, workspace=ws)
+    w["gpu_out"] = dict(idx=idx, score=score)
     pairs = nq * nc
     w["nnz"] = int(w["indices"].shape[0])
     flops = 2.0 * w["nnz"] * nc
@@ -464,28 +481,81 @@ def cpu_baseline_som(k, w, target_s):
 
 # ------------------------------------------------------------ cpu leg --
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _verdict(fails, stats, checked_set):
+    out = {"checked": stats["rows"], "set": checked_set, "pass": not fails}
+    out.update({k: stats[k] for k in ("same_index", "gap_accepted", "empty", "floor_bound")})
+    if fails:
+        out["failures"] = fails[:3]
+    return out
+
+
+def _one_thread_rate(run, unit_pairs, first=2, target_s=1.5):
+    """Pairs/s of the single-threaded oracle: time `first` units, then enough
+    units for about target_s seconds; run(m) scans m units."""
+    t0 = time.perf_counter()
+    run(first)
+    per = (time.perf_counter() - t0) / first
+    m = max(first, int(target_s / max(per, 1e-9)))
+    t0 = time.perf_counter()
+    m = run(m)
+    dt = time.perf_counter() - t0
+    return m * unit_pairs / dt, m
+
+
 def cpu_baseline(k, w, target_s):
-    """Oracle (fp64, plain loops, untuned) on a bounded sample, all host
-    threads, each running the single-threaded scan on its own shard."""
+    """Oracle (fp64, plain loops, untuned) on the workload's checked set, all
+    host threads, each running the single-threaded scan on its own shard;
+    the result is also the parity verdict of the timed GPU output.  Returns
+    (cpu_baseline dict, parity dict or None)."""
     import numpy as np
     import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import check, l2_floor
     threads = oracle.default_threads()
+    base = dict(unit="pairs/s", cores=threads, kind="oracle", cpu_model=cpu_model())
     if w["kind"] == "dense":
-        nc = w["nc"]
+        nc, nq = w["nc"], w["nq"]
+        # checked set: every query, or the workload's seeded subset
+        sel = w.get("subset")
+        label = (f"the seeded {len(sel)}-query subset" if sel is not None
+                 else f"all {nq} queries")
+        sel = np.arange(nq) if sel is None else np.asarray(sel)
+        Qs = np.ascontiguousarray(w["Q"][sel])
+        base["one_thread_value"], m1 = _one_thread_rate(
+            lambda m: (oracle.dense(Qs[:m], w["C"], 0, threads=1), min(m, len(sel)))[1], nc)
         t0 = time.perf_counter()
-        oracle.dense(w["Q"][:4], w["C"], 0, threads=1)
-        per_q = (time.perf_counter() - t0) / 4
-        nsample = int(max(threads, min(w["nq"], target_s * threads / max(per_q, 1e-9))))
-        t0 = time.perf_counter()
-        oracle.dense(w["Q"][:nsample], w["C"], 0, threads=threads)
+        o_idx, o_val, o_gap = oracle.dense(Qs, w["C"], 0, threads=threads)
         dt = time.perf_counter() - t0
-        return dict(value=nsample * nc / dt, unit="pairs/s", cores=threads, kind="oracle",
-                    sample=f"first {nsample} of {w['nq']} queries x all {nc} candidates",
-                    seconds=round(dt, 2))
+        base.update(value=len(sel) * nc / dt, seconds=round(dt, 2),
+                    sample=f"{label} x all {nc} candidates (the checked set)",
+                    one_thread_sample=f"{m1} queries x all {nc} candidates, one thread")
+        parity = None
+        if "gpu_out" in w:
+            idx = w["gpu_out"]["idx"].cpu().numpy()[sel]
+            score = w["gpu_out"]["score"].cpu().numpy()[sel]
+            fails, stats = check(idx, score, o_idx, o_val, o_gap, 0, l2_floor(Qs, w["C"], o_idx),
+                                 lambda r, c: oracle.pair_values(Qs, w["C"], 0, r, c))
+            parity = _verdict(fails, stats, label)
+        return base, parity
     if w["kind"] == "diversity":
         n = w["n"]
-        # one diversity step straight from the rows (no Gram cache): a sample
-        # of sequences, each scanning all n rows against its reference
+        # the value: one step straight from the rows (no Gram cache) for a
+        # sample of sequences, each scanning all n rows against its reference
+        base["one_thread_value"], m1 = _one_thread_rate(
+            lambda m: (oracle.div_run(w["C"], w["seeds"][:m], 1), m)[1], n)
         t0 = time.perf_counter()
         oracle.div_run(w["C"], w["seeds"][:2], 1)
         per_seq = (time.perf_counter() - t0) / 2
@@ -497,23 +567,91 @@ def cpu_baseline(k, w, target_s):
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda s: oracle.div_run(w["C"], s, 1), [p for p in parts if len(p)]))
         dt = time.perf_counter() - t0
-        return dict(value=nsample * n / dt, unit="pairs/s", cores=threads, kind="oracle",
+        base.update(value=nsample * n / dt, seconds=round(dt, 2),
                     sample=f"one step of {nsample} of {w['nseq']} sequences x all {n} rows",
-                    seconds=round(dt, 2))
-    # sparse
+                    one_thread_sample=f"one step of {m1} sequences x all {n} rows, one thread")
+        return base, _div_parity(w, threads, check)
+    # sparse: the 4,096 seeded rows
     ptr = w["indptr"]
+    nc = w["nc"]
+    sel = synth_sample(w["nq"], 4096, key=4)
+    sub_ptr = np.concatenate([[0], np.cumsum(ptr[sel + 1] - ptr[sel])]).astype(np.int32)
+    sub_idx = np.concatenate([w["indices"][ptr[i]:ptr[i + 1]] for i in sel])
+    sub_val = np.concatenate([w["values"][ptr[i]:ptr[i + 1]] for i in sel])
     col_sq = oracle.sqnorms(w["CT"], feature_major=True, threads=threads)
+
+    def rows(m):
+        oracle.csr(sub_ptr[:m + 1], sub_idx, sub_val, w["CT"], 0, col_sq=col_sq, threads=1)
+        return m
+    base["one_thread_value"], m1 = _one_thread_rate(rows, nc)
     t0 = time.perf_counter()
-    oracle.csr(ptr[:3], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq, threads=1)
-    per_q = (time.perf_counter() - t0) / 2
-    nsample = int(max(threads, min(w["nq"], target_s * threads / max(per_q, 1e-9))))
-    t0 = time.perf_counter()
-    oracle.csr(ptr[:nsample + 1], w["indices"], w["values"], w["CT"], 0, col_sq=col_sq,
-               threads=threads)
+    o_idx, o_val, o_gap = oracle.csr(sub_ptr, sub_idx, sub_val, w["CT"], 0, col_sq=col_sq,
+                                     threads=threads)
     dt = time.perf_counter() - t0
-    return dict(value=nsample * w["nc"] / dt, unit="pairs/s", cores=threads, kind="oracle",
-                sample=f"first {nsample} of {w['nq']} CSR rows x all {w['nc']} neurons",
-                seconds=round(dt, 2))
+    base.update(value=len(sel) * nc / dt, seconds=round(dt, 2),
+                sample=f"the seeded {len(sel)} of {w['nq']} CSR rows x all {nc} neurons "
+                       "(the checked set)",
+                one_thread_sample=f"{m1} CSR rows x all {nc} neurons, one thread")
+    parity = None
+    if "gpu_out" in w and w.get("value_bytes", 4) == 4:
+        idx = w["gpu_out"]["idx"].cpu().numpy()[sel]
+        score = w["gpu_out"]["score"].cpu().numpy()[sel]
+        qn = np.array([np.sum(sub_val[sub_ptr[i]:sub_ptr[i + 1]].astype(np.float64) ** 2)
+                       for i in range(len(sel))])
+
+        def pick_values(r, c):
+            return np.array([oracle.csr(np.array([0, sub_ptr[i + 1] - sub_ptr[i]], np.int32),
+                                        sub_idx[sub_ptr[i]:sub_ptr[i + 1]],
+                                        sub_val[sub_ptr[i]:sub_ptr[i + 1]],
+                                        np.ascontiguousarray(w["CT"][:, j:j + 1]), 0,
+                                        col_sq=col_sq[j:j + 1])[1][0] for i, j in zip(r, c)])
+        fails, stats = check(idx, score, o_idx, o_val, o_gap, 0, 1e-2 * (qn + 1.0), pick_values)
+        parity = _verdict(fails, stats, f"the seeded {len(sel)} CSR rows")
+    return base, parity
+
+
+def synth_sample(nq, count, key):
+    import synth
+    return synth.sample_queries(nq, count, key=key)
+
+
+def _div_parity(w, threads, check):
+    """Replay of every pick of the timed run (last-pick reading, at most the
+    workload's 64 steps) against the oracle's fp64 cosine Gram matrix, plus
+    the final masks = seed + picks."""
+    import numpy as np
+    import oracle
+    g = w.get("gpu_out")
+    if g is None or w.get("reference", "last") != "last" or g["steps"] > w["steps"]:
+        return None
+    picks = g["picks"].cpu().numpy().T.copy()      # [nseq, steps]
+    scores = g["scores"].cpu().numpy().T.copy()
+    masks = g["mask"].cpu().numpy().view(np.uint32)
+    n, seeds = w["n"], w["seeds"]
+    G = oracle.gram_cos(w["C"], threads=threads)
+    rep = oracle.div_replay(G, seeds, picks, threads=threads)
+    del G
+    live = rep["bidx"] >= 0
+    fails = []
+    if not (rep["pick_ok"][live] == 1).all():
+        fails.append("illegal pick (masked or out of range)")
+    if not (picks[~live] == -1).all():
+        fails.append("pick where nothing was left")
+    flat = lambda a: a.reshape(-1)  # noqa: E731
+    f, stats = check(flat(picks), flat(scores), flat(rep["bidx"]), flat(rep["best"]),
+                     flat(rep["gap"]), 3, 1e-2, lambda r, c: flat(rep["pick_value"])[r],
+                     legal=lambda r, c: flat(rep["pick_ok"])[r] == 1)
+    fails += f
+    exp = np.zeros_like(masks)
+    rows = np.arange(len(seeds))
+    exp[rows, seeds // 32] |= (np.uint32(1) << (seeds % 32).astype(np.uint32))
+    for t in range(picks.shape[1]):
+        p = picks[:, t]
+        ok = p >= 0
+        np.bitwise_or.at(exp, (rows[ok], p[ok] // 32), np.uint32(1) << (p[ok] % 32).astype(np.uint32))
+    if not np.array_equal(exp, masks):
+        fails.append("final masks differ from seed + picks")
+    return _verdict(fails, stats, f"every pick of {len(seeds)} sequences x {picks.shape[1]} steps")
 
 
 def _pmc_avg(db, counter, name_prefix):
@@ -722,6 +860,117 @@ def copy_calibration(a, torch):
                       "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
 
 
+def under_profiler():
+    """True inside rocprofv3 (its tool library is preloaded and its settings
+    are in the environment): no child processes are started there."""
+    return ("rocprof" in os.environ.get("LD_PRELOAD", "")
+            or any(k.startswith("ROCPROF") for k in os.environ))
+
+
+def run_replicates(a, count):
+    """count - 1 further processes run the same timed steps (no oracle leg),
+    one after the other, before this process touches the GPU; returns their
+    JSON lines."""
+    import subprocess
+    argv = [x for x in sys.argv[1:]]
+    out = []
+    for r in range(count - 1):
+        cmd = [sys.executable, os.path.abspath(__file__), *argv, "--replicates", "1",
+               "--no-cpu-baseline", "--child"]
+        log(f"replicate process {r + 1} of {count - 1}")
+        p = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        if p.returncode != 0:
+            sys.stderr.write(p.stderr[-2000:])
+            raise SystemExit(f"replicate process {r + 1} failed (exit {p.returncode})")
+        line = [l for l in p.stdout.splitlines() if l.startswith("{")][-1]
+        out.append(json.loads(line))
+    return out
+
+
+def graph_nodes(g, calls):
+    """Nodes of a captured graph per captured call (hipGraphGetNodes on the
+    graph torch captured), or None where the graph handle is not exposed."""
+    import ctypes
+    try:
+        raw = g.raw_cuda_graph()
+        hip = ctypes.CDLL("libamdhip64.so")
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(ctypes.c_void_p(raw), None, ctypes.byref(n)) != 0:
+            return None
+        return n.value / calls
+    except Exception:  # noqa: BLE001 -- older torch, or a different runtime
+        return None
+
+
+def measure_latency(step, torch, a, w):
+    """Per-call time of the search against the launch floor on the same
+    stream: eager (one Python call per search, as the timed steps) and as a
+    captured HIP graph of `steps` searches replayed as one launch; the floor
+    is an empty kernel (one wave) launched the same ways.  The graph replay's
+    output is checked against the eager output."""
+    import ctypes
+    from farthest_vector_search_amd.build import ROOF_LIB
+    R = ctypes.CDLL(ROOF_LIB)
+    R.vs_roof_empty.restype = ctypes.c_int32
+    R.vs_roof_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p]
+    K = a.steps
+    res = {}
+
+    def per_call_us(fn, reps=5):
+        """Median over reps of (wall time of K back-to-back calls) / K."""
+        vals = []
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            for _ in range(K):
+                fn()
+            torch.cuda.synchronize()
+            vals.append((time.perf_counter() - t0) / K * 1e6)
+        return sorted(vals)[len(vals) // 2]
+
+    def empty():
+        if R.vs_roof_empty(1, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("vs_roof_empty failed")
+
+    res["eager_us_per_call"] = round(per_call_us(step), 2)
+    res["eager_empty_kernel_us"] = round(per_call_us(empty), 2)
+    res["eager_frac"] = round(res["eager_empty_kernel_us"] / res["eager_us_per_call"], 4)
+    # graphs: K searches (or K empty kernels) captured once, replayed
+    ref_idx = w["gpu_out"]["idx"].clone()
+    ref_score = w["gpu_out"]["score"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_search, g_empty = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_search):
+        for _ in range(K):
+            step()
+    with torch.cuda.graph(g_empty):
+        for _ in range(K):
+            empty()
+    torch.cuda.synchronize()
+    ok = True
+    for _ in range(3):  # every replay checked against the eager result
+        w["gpu_out"]["idx"].fill_(-1)
+        g_search.replay()
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(w["gpu_out"]["idx"], ref_idx)
+                   and torch.equal(w["gpu_out"]["score"].view(torch.int32),
+                                   ref_score.view(torch.int32)))
+    res["graph_us_per_call"] = round(per_call_us(g_search.replay) / K, 2)
+    res["graph_empty_kernel_us"] = round(per_call_us(g_empty.replay) / K, 2)
+    res["graph_frac"] = round(res["graph_empty_kernel_us"] / res["graph_us_per_call"], 4)
+    res["graph_replays_match_eager"] = ok
+    res["graph_nodes_per_call"] = graph_nodes(g_search, K)
+    res["note"] = ("frac = empty-kernel time / search time per call on the same stream; "
+                   f"{K} calls per timing, median of 5")
+    return res
+
+
 def main():
     a = parse()
     if a.traffic_from:
@@ -732,6 +981,10 @@ def main():
               "(queries split across GPUs with no exchange would be the way). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    replicas = []
+    n_rep = 1 if (a.child or a.roof or a.copy_bytes > 0 or under_profiler()) else max(1, a.replicates)
+    if n_rep > 1:
+        replicas = run_replicates(a, n_rep)
     import torch
     import farthest_vector_search_amd as vs
     if not torch.cuda.is_available():
@@ -760,15 +1013,19 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {a.steps} steps")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     with vs.KernelTimer(max_launches=a.steps * launches_per_step + 8) as kt:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(a.steps):
+        evs[0].record()
+        for i in range(a.steps):
             step()
+            evs[i + 1].record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / a.steps
     value = pairs * a.steps / dt
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
     # roofline of the dominant kernel: algorithmic work of the timed steps over
     # the summed durations of its launches (= per-launch work / mean launch time)
     launches = max(kt.launches, 1)
@@ -816,18 +1073,34 @@ def main():
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": cfg, "roofline": roof,
+        # HIP events between consecutive steps on the launch stream
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4),
+                    "min": round(per_step[0], 4), "max": round(per_step[-1], 4)},
     }
+    if replicas:
+        vals = [r["value"] for r in replicas] + [value]
+        med = sorted(vals)[len(vals) // 2]
+        spread = (max(vals) - min(vals)) / med * 100.0
+        out["replicates"] = {"processes": len(vals), "values": vals,
+                             "ms_per_step": [r["ms_per_step"] for r in replicas] + [out["ms_per_step"]],
+                             "spread_pct": round(spread, 3), "spread_within_1_5_pct": spread <= 1.5}
+    if a.workload == 1 and not a.som and a.dense_mode == "fused":
+        log("latency against the empty-kernel floor")
+        out["latency"] = measure_latency(step, torch, a, w)
     if a.som:
         qe_final = float(w["som_qe"].cpu()[0])
         log("epoch phases")
         out["som_epoch"] = som_phase_times(w, torch)
         out["som_epoch"]["qe_last_epoch"] = qe_final
     if not a.no_cpu_baseline:
-        log("cpu baseline (oracle on a bounded sample)")
-        out["cpu_baseline"] = (cpu_baseline_som(a.workload, w, a.cpu_seconds) if a.som else
-                               cpu_baseline(a.workload, w, a.cpu_seconds))
+        log("cpu baseline (the oracle on the checked set) and parity of the timed output")
+        if a.som:
+            out["cpu_baseline"] = cpu_baseline_som(a.workload, w, a.cpu_seconds)
+        else:
+            out["cpu_baseline"], parity = cpu_baseline(a.workload, w, a.cpu_seconds)
+            if parity is not None:
+                out["parity"] = parity
     print(json.dumps(out), flush=True)
-
 
 if __name__ == "__main__":
     main()

@@ -191,11 +191,9 @@ static int dense_search(const float *Q, const float *C, int64_t nq, int64_t nc, 
     float *qn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.qn) : nullptr;
     float *cn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.cn) : nullptr;
 
-    // every buffer of the workspace is written before it is read: the keys by
-    // a fill kernel (no memset node), the norms by their own kernels
-    VS_TRY_HIP(vs::launch_fill_keys(keys, nq, st));
-    if (cn) VS_TRY_HIP(vs::launch_row_sqnorms(C, nc, d, cn, st));
-    if (qn && score_out) VS_TRY_HIP(vs::launch_row_sqnorms(Q, nq, d, qn, st));
+    // every buffer of the workspace is written before it is read, in one
+    // prologue launch: keys reset by a kernel (no memset node), the norms
+    VS_TRY_HIP(vs::launch_dense_prep(C, nc, cn, Q, nq, score_out ? qn : nullptr, d, keys, st));
 
     vs::DenseArgs a{};
     a.Q = Q;

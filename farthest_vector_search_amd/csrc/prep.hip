@@ -21,14 +21,9 @@ __global__ __launch_bounds__(256) void k_fill_keys(uint64_t *keys, int64_t n) {
 // One wave per row.  Lane l owns the 4-element groups starting at 4l + 256i
 // and accumulates them in index order; the 64 lane sums are then combined by
 // a fixed butterfly.  The vector and scalar variants read the same elements
-// in the same order.
+// in the same order.  Every row norm of the library comes from this routine.
 template <bool VEC>
-__global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X, int64_t rows,
-                                                    int32_t d, float *__restrict__ out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const float *x = X + row * (int64_t)d;
+__device__ __forceinline__ float row_sqnorm(const float *__restrict__ x, int32_t d, int lane) {
     float acc = 0.0f;
     for (int32_t k = 4 * lane; k < d; k += 256) {
         if constexpr (VEC) {
@@ -47,7 +42,47 @@ __global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X
         }
     }
     for (int s = 32; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
+    return acc;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_row_sqnorms(const float *__restrict__ X, int64_t rows,
+                                                    int32_t d, float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float acc = row_sqnorm<VEC>(X + row * (int64_t)d, d, lane);
     if (lane == 0) out[row] = acc;
+}
+
+// Everything the dense search needs before its scan, in one launch: the
+// candidates' squared norms (workgroups [0, bc)), the queries' (next bq
+// workgroups; skipped when qn is null) and the packed keys reset to "no
+// candidate" (the last bk workgroups).  Same per-row routine, so the norms
+// equal k_row_sqnorms' bit for bit.
+template <bool VECC, bool VECQ>
+__global__ __launch_bounds__(256) void k_dense_prep(const float *__restrict__ C, int64_t nc,
+                                                   float *__restrict__ cn,
+                                                   const float *__restrict__ Q, int64_t nq,
+                                                   float *__restrict__ qn, int32_t d,
+                                                   uint64_t *__restrict__ keys, int64_t bc,
+                                                   int64_t bq) {
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.x;
+    if (b < bc) {
+        const int64_t row = b * 4 + (threadIdx.x >> 6);
+        if (row >= nc) return;
+        const float acc = row_sqnorm<VECC>(C + row * (int64_t)d, d, lane);
+        if (lane == 0) cn[row] = acc;
+    } else if (b < bc + bq) {
+        const int64_t row = (b - bc) * 4 + (threadIdx.x >> 6);
+        if (row >= nq) return;
+        const float acc = row_sqnorm<VECQ>(Q + row * (int64_t)d, d, lane);
+        if (lane == 0) qn[row] = acc;
+    } else {
+        const int64_t i = (b - bc - bq) * 256 + threadIdx.x;
+        if (i < nq) keys[i] = kNoKey;
+    }
 }
 
 // Feature-major X: column j's squared norm, feature k of column j at
@@ -153,6 +188,32 @@ hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *ou
     else
         hipLaunchKernelGGL(k_row_sqnorms<false>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, X,
                            rows, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_prep(const float *C, int64_t nc, float *cn, const float *Q, int64_t nq,
+                             float *qn, int32_t d, uint64_t *keys, hipStream_t st) {
+    if (nq <= 0) return hipSuccess;
+    const int64_t bc = cn ? blocks_for(nc, 4) : 0;
+    const int64_t bq = qn ? blocks_for(nq, 4) : 0;
+    const int64_t bk = blocks_for(nq, 256);
+    const dim3 grid((unsigned)(bc + bq + bk)), block(256);
+    auto vec = [d](const float *X) {
+        return (d % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    };
+    const bool vc = cn && vec(C), vq = qn && vec(Q);
+    if (vc && vq)
+        hipLaunchKernelGGL((k_dense_prep<true, true>), grid, block, 0, st, C, nc, cn, Q, nq, qn, d,
+                           keys, bc, bq);
+    else if (vc)
+        hipLaunchKernelGGL((k_dense_prep<true, false>), grid, block, 0, st, C, nc, cn, Q, nq, qn,
+                           d, keys, bc, bq);
+    else if (vq)
+        hipLaunchKernelGGL((k_dense_prep<false, true>), grid, block, 0, st, C, nc, cn, Q, nq, qn,
+                           d, keys, bc, bq);
+    else
+        hipLaunchKernelGGL((k_dense_prep<false, false>), grid, block, 0, st, C, nc, cn, Q, nq, qn,
+                           d, keys, bc, bq);
     return hipGetLastError();
 }
 

@@ -189,3 +189,15 @@ VS_API int32_t vs_roof_gather(const float *G, int64_t nrows, int64_t n, int64_t 
                        rows, nseq, steps, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+// The launch floor: a kernel with no work, one workgroup of one wave.
+__global__ __launch_bounds__(64) void k_empty() {}
+
+// Launches k_empty `count` times on `stream` (one launch per call of the
+// caller's own loop when count = 1).  Returns 0, or -1 on a launch error.
+VS_API int32_t vs_roof_empty(int32_t count, void *stream) {
+    if (count < 1) return -1;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < count; ++i) hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}

@@ -13,6 +13,10 @@ struct CsrArgs;
 // Launchers (return hipError_t of the launch).  The dominant kernel of each
 // entry point is bracketed by the library's timing events when recording.
 hipError_t launch_fill_keys(uint64_t *keys, int64_t n, hipStream_t st);
+// Dense search prologue in one launch: candidate norms (cn may be null),
+// query norms (qn may be null) and the nq packed keys reset.
+hipError_t launch_dense_prep(const float *C, int64_t nc, float *cn, const float *Q, int64_t nq,
+                             float *qn, int32_t d, uint64_t *keys, hipStream_t st);
 hipError_t launch_row_sqnorms(const float *X, int64_t rows, int32_t d, float *out,
                               hipStream_t st);
 // feature k of column j at X[(j / 64) * cs + k * ld + j % 64]
