@@ -262,11 +262,51 @@ void k_bmu_qreg(const DenseArgs a) {
                 acc[cb] = f32x16{};
             }
         };
-        if ((int64_t)base + kBC <= nc) scan(std::false_type{});  // uniform
-        else scan(std::true_type{});
-        if (tb < best) {
-            best = tb;
-            bidx = base + 4 * h + tr;
+        if ((int64_t)base + kBC <= nc) {  // uniform: a full tile
+            // Rank in place, take the tile's minimum with a min tree, and look
+            // for its lowest row only where it beats the running best (late in
+            // a sweep a tile rarely improves any of a wave's queries).  Same
+            // result as the scan: the lowest row holding the minimum, taken
+            // only when strictly below the best.
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (metric_is_l2(M)) cn4 = cnr[4 * cb + (i >> 2)];
+                    acc[cb][i] = rank_value<M>(acc[cb][i], cn4[i & 3]);
+                }
+            }
+            float m[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                m[j] = __builtin_fminf(__builtin_fminf(acc[j >> 2][4 * (j & 3)], acc[j >> 2][4 * (j & 3) + 1]),
+                                       __builtin_fminf(acc[j >> 2][4 * (j & 3) + 2], acc[j >> 2][4 * (j & 3) + 3]));
+            const float tmin = __builtin_fminf(
+                __builtin_fminf(__builtin_fminf(m[0], m[1]), __builtin_fminf(m[2], m[3])),
+                __builtin_fminf(__builtin_fminf(m[4], m[5]), __builtin_fminf(m[6], m[7])));
+            if (tmin < best) {
+                // rows r = cb * 32 + 8 * r4 + e hold acc[cb][4 * r4 + e]: the
+                // lowest row with the minimum, found from the highest down
+#pragma unroll
+                for (int cb = 1; cb >= 0; --cb) {
+#pragma unroll
+                    for (int i = 15; i >= 0; --i) {
+                        const int r = cb * 32 + 8 * (i >> 2) + (i & 3);
+                        tr = acc[cb][i] == tmin ? r : tr;
+                    }
+                }
+                best = tmin;
+                bidx = base + 4 * h + tr;
+            }
+            acc[0] = f32x16{};
+            acc[1] = f32x16{};
+        } else {
+            scan(std::true_type{});
+            if (tb < best) {
+                best = tb;
+                bidx = base + 4 * h + tr;
+            }
         }
     };
     auto flush = [&](int64_t qtile) {
