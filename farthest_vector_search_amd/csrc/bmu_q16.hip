@@ -269,6 +269,36 @@ void k_bmu_q16(const DenseArgs a) {
         const int32_t lim = left < 64 ? (int32_t)left : 64;
         uint32_t mg = 0;
         if constexpr (MASKED) mg = mw >> (4 * g);
+        if (nc - base >= kBC) {  // uniform: a full tile
+            // Rank in place (masked rows rank as +inf), take the minimum with
+            // a min tree, and look for its lowest row only where it beats the
+            // running best: the same (value, lowest row) as the scan below.
+            float v[8];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (metric_is_l2(M))
+                    cn4 = *reinterpret_cast<const f32x4 *>(&sN[par][16 * b + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = rank_value<M>(acc[b][r], cn4[r]);
+                    if constexpr (MASKED) x = ((mg >> (16 * b + r)) & 1u) ? __builtin_inff() : x;
+                    v[4 * b + r] = x;
+                }
+                acc[b] = f32x4{};
+            }
+            const float tmin = __builtin_fminf(
+                __builtin_fminf(__builtin_fminf(v[0], v[1]), __builtin_fminf(v[2], v[3])),
+                __builtin_fminf(__builtin_fminf(v[4], v[5]), __builtin_fminf(v[6], v[7])));
+            if (tmin < best) {
+                int32_t tr = 0;
+#pragma unroll
+                for (int j = 7; j >= 0; --j) tr = v[j] == tmin ? 16 * (j >> 2) + (j & 3) : tr;
+                best = tmin;
+                bidx = base + 4 * g + tr;
+            }
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             f32x4 cn4 = {0.0f, 0.0f, 0.0f, 0.0f};
