@@ -12,7 +12,6 @@ import subprocess
 import sys
 
 import numpy as np
-import pytest
 
 import oracle
 import synth
@@ -86,7 +85,7 @@ def test_dense_leg_uses_the_seeded_subset():
 def test_diversity_replay_leg():
     """The diversity leg replays every pick against the Gram matrix and
     checks the final masks (16 sequences of the 8,359 x 768 table, 8 steps);
-    a repeated pick and a wrong mask each fail it."""
+    a final mask with one bit more or less fails it."""
     from parity import check
     w = synth.workload(3)
     seeds = w["seeds"][:16]
