@@ -507,6 +507,37 @@ VS_API size_t vs_diversity_step_workspace(int64_t n, int32_t d, int64_t nseq) {
     return up256((size_t)nseq * 8);
 }
 
+// The kernels of one diversity step (references gathered as C[last_pick[s]],
+// or the rows of Q when Q is not null) on arguments already checked: the key
+// reset (fill_keys; a run skips it after its first step, whose finalize
+// left every key reset), the masked scan, the finalize (reset_keys: leave
+// the keys reset for the run's next step).
+static int diversity_step_enqueue(const float *C, int64_t n, int32_t d, const int32_t *last_pick,
+                                  const float *Q, uint32_t *mask_bits, int64_t nseq,
+                                  int32_t *idx_out, float *score_out, void *workspace,
+                                  hipStream_t st, int n_cu, bool fill_keys, bool reset_keys) {
+    uint64_t *keys = static_cast<uint64_t *>(workspace);
+    const int64_t W = (n + 31) / 32;
+    if (fill_keys) VS_TRY_HIP(vs::launch_fill_keys(keys, nseq, st));
+    vs::DenseArgs a{};
+    a.Q = Q;
+    a.C = C;
+    a.pick = last_pick;
+    a.mask = mask_bits;
+    a.keys = keys;
+    a.nq = nseq;
+    a.nc = n;
+    a.d = d;
+    a.mask_words = W;
+    const int mode = Q ? vs::kQRowsMasked : vs::kQGatherMasked;
+    const bool q16 = div_use_q16(d, C) && (!Q || vs::q16_supports(d, C, Q));
+    if (q16) VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, mode, st, n_cu));
+    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, mode, st, n_cu));
+    VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st,
+                                       reset_keys));
+    return VS_OK;
+}
+
 VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t *last_pick,
                              uint32_t *mask_bits, int64_t nseq, int32_t *idx_out,
                              float *score_out, void *workspace, size_t workspace_bytes,
@@ -522,24 +553,9 @@ VS_API int vs_diversity_step(const float *C, int64_t n, int32_t d, const int32_t
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
 
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    uint64_t *keys = static_cast<uint64_t *>(workspace);
-    const int64_t W = (n + 31) / 32;
-    VS_TRY_HIP(vs::launch_fill_keys(keys, nseq, st));
-    vs::DenseArgs a{};
-    a.C = C;
-    a.pick = last_pick;
-    a.mask = mask_bits;
-    a.keys = keys;
-    a.nq = nseq;
-    a.nc = n;
-    a.d = d;
-    a.mask_words = W;
-    if (div_use_q16(d, C))
-        VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, vs::kQGatherMasked, st, n_cu));
-    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, vs::kQGatherMasked, st, n_cu));
-    VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
-    return VS_OK;
+    return diversity_step_enqueue(C, n, d, last_pick, nullptr, mask_bits, nseq, idx_out,
+                                  score_out, workspace, reinterpret_cast<hipStream_t>(stream),
+                                  n_cu, true, false);
 }
 
 // A whole run: `steps` steps chained on the stream, step t's references being
@@ -552,13 +568,21 @@ VS_API int vs_diversity_run(const float *C, int64_t n, int32_t d, const int32_t 
         steps < 0)
         return VS_ERR_SHAPE;
     if (nseq == 0 || steps == 0) return VS_OK;
-    if (!seeds || !picks_out) return VS_ERR_NULL;
+    // every check of the steps below, before anything is enqueued
+    if (!C || !seeds || !picks_out || !mask_bits || !workspace) return VS_ERR_NULL;
+    if (!al4(C) || !al4(seeds) || !al4(mask_bits) || !al4(picks_out) || !al4(scores_out) ||
+        !al256(workspace))
+        return VS_ERR_ALIGN;
+    if (workspace_bytes < vs_diversity_step_workspace(n, d, nseq)) return VS_ERR_WORKSPACE;
+    int n_cu = 0;
+    if (const int s = device_ready(&n_cu)) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     for (int32_t t = 0; t < steps; ++t) {
         const int32_t *last = t == 0 ? seeds : picks_out + (int64_t)(t - 1) * nseq;
         float *sc = scores_out ? scores_out + (int64_t)t * nseq : nullptr;
-        if (const int s = vs_diversity_step(C, n, d, last, mask_bits, nseq,
-                                            picks_out + (int64_t)t * nseq, sc, workspace,
-                                            workspace_bytes, stream))
+        if (const int s = diversity_step_enqueue(C, n, d, last, nullptr, mask_bits, nseq,
+                                                 picks_out + (int64_t)t * nseq, sc, workspace,
+                                                 st, n_cu, t == 0, t + 1 < steps))
             return s;
     }
     return VS_OK;
@@ -581,24 +605,9 @@ VS_API int vs_diversity_step_ref(const float *C, int64_t n, int32_t d, const flo
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
 
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    uint64_t *keys = static_cast<uint64_t *>(workspace);
-    const int64_t W = (n + 31) / 32;
-    VS_TRY_HIP(vs::launch_fill_keys(keys, nseq, st));
-    vs::DenseArgs a{};
-    a.Q = Q;
-    a.C = C;
-    a.mask = mask_bits;
-    a.keys = keys;
-    a.nq = nseq;
-    a.nc = n;
-    a.d = d;
-    a.mask_words = W;
-    if (div_use_q16(d, C) && vs::q16_supports(d, C, Q))
-        VS_TRY_HIP(vs::launch_dense_q16(a, VS_COS_MIN, vs::kQRowsMasked, st, n_cu));
-    else VS_TRY_HIP(vs::launch_dense(a, VS_COS_MIN, vs::kQRowsMasked, st, n_cu));
-    VS_TRY_HIP(vs::launch_finalize_div(keys, nseq, mask_bits, W, idx_out, score_out, st));
-    return VS_OK;
+    return diversity_step_enqueue(C, n, d, nullptr, Q, mask_bits, nseq, idx_out, score_out,
+                                  workspace, reinterpret_cast<hipStream_t>(stream), n_cu, true,
+                                  false);
 }
 
 VS_API int vs_diversity_accumulate(const float *C, int64_t n, int32_t d, const int32_t *pick,
@@ -638,8 +647,8 @@ VS_API int vs_diversity_run_ref(const float *C, int64_t n, int32_t d, const int3
     for (int32_t t = 0; t < steps; ++t) {
         int32_t *idx = picks_out + (int64_t)t * nseq;
         float *sc = scores_out ? scores_out + (int64_t)t * nseq : nullptr;
-        if (const int s = vs_diversity_step_ref(C, n, d, Q, mask_bits, nseq, idx, sc, workspace,
-                                                workspace_bytes, stream))
+        if (const int s = diversity_step_enqueue(C, n, d, nullptr, Q, mask_bits, nseq, idx, sc,
+                                                 workspace, st, n_cu, t == 0, t + 1 < steps))
             return s;
         VS_TRY_HIP(vs::launch_div_accumulate(C, n, d, idx, Q, nseq, st));
     }

@@ -40,14 +40,17 @@ __global__ __launch_bounds__(256) void k_finalize(const uint64_t *__restrict__ k
     }
 }
 
-__global__ __launch_bounds__(256) void k_finalize_div(const uint64_t *__restrict__ keys,
+// reset != 0: the key is set back to "no candidate" once read, so the next
+// step of a run needs no separate reset launch.
+__global__ __launch_bounds__(256) void k_finalize_div(uint64_t *__restrict__ keys,
                                                      int64_t nseq, uint32_t *__restrict__ mask,
                                                      int64_t mask_words,
                                                      int32_t *__restrict__ idx_out,
-                                                     float *__restrict__ score_out) {
+                                                     float *__restrict__ score_out, int reset) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= nseq) return;
     const uint64_t k = keys[s];
+    if (reset && k != kNoKey) keys[s] = kNoKey;
     if (k == kNoKey) {
         idx_out[s] = -1;
         if (score_out) score_out[s] = __builtin_nanf("");
@@ -73,12 +76,12 @@ hipError_t launch_finalize(const uint64_t *keys, const float *qn, int64_t nq, in
     return hipGetLastError();
 }
 
-hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mask,
+hipError_t launch_finalize_div(uint64_t *keys, int64_t nseq, uint32_t *mask,
                                int64_t mask_words, int32_t *idx_out, float *score_out,
-                               hipStream_t st) {
+                               hipStream_t st, bool reset) {
     if (nseq <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_finalize_div, dim3((unsigned)((nseq + 255) / 256)), dim3(256), 0, st,
-                       keys, nseq, mask, mask_words, idx_out, score_out);
+                       keys, nseq, mask, mask_words, idx_out, score_out, reset ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -80,9 +80,11 @@ hipError_t launch_csr(const CsrArgs &a, int metric, hipStream_t st, int n_cu, ui
 hipError_t launch_csr_f16(const CsrArgs &a, int metric, hipStream_t st, int n_cu, uint64_t *part);
 hipError_t launch_finalize(const uint64_t *keys, const float *qn, int64_t nq, int metric,
                            int32_t *idx_out, float *score_out, hipStream_t st);
-hipError_t launch_finalize_div(const uint64_t *keys, int64_t nseq, uint32_t *mask,
+// reset: set every key back to "no candidate" once read (the next step of a
+// run then needs no reset launch)
+hipError_t launch_finalize_div(uint64_t *keys, int64_t nseq, uint32_t *mask,
                                int64_t mask_words, int32_t *idx_out, float *score_out,
-                               hipStream_t st);
+                               hipStream_t st, bool reset);
 
 // Batch SOM update (som.hip).  The codebook and the S / T buffers are
 // neuron-major (m * d + k) for dense rows, blocked feature-major
