@@ -945,10 +945,17 @@ def measure_latency(step, torch, a, w):
         step()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g_search, g_empty = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    try:  # keep the captured graph so that its nodes can be counted
+        g_search, kept = torch.cuda.CUDAGraph(keep_graph=True), True
+    except TypeError:
+        g_search, kept = torch.cuda.CUDAGraph(), False
+    g_empty = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_search):
         for _ in range(K):
             step()
+    res["graph_nodes_per_call"] = graph_nodes(g_search, K) if kept else None
+    if kept:
+        g_search.instantiate()
     with torch.cuda.graph(g_empty):
         for _ in range(K):
             empty()
@@ -965,7 +972,6 @@ def measure_latency(step, torch, a, w):
     res["graph_empty_kernel_us"] = round(per_call_us(g_empty.replay) / K, 2)
     res["graph_frac"] = round(res["graph_empty_kernel_us"] / res["graph_us_per_call"], 4)
     res["graph_replays_match_eager"] = ok
-    res["graph_nodes_per_call"] = graph_nodes(g_search, K)
     res["note"] = ("frac = empty-kernel time / search time per call on the same stream; "
                    f"{K} calls per timing, median of 5")
     return res

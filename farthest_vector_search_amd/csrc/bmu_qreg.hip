@@ -42,8 +42,7 @@ namespace {
 #define VS_QREG_PRIO 0
 #endif
 
-constexpr int kQW = 8;          // waves per workgroup
-constexpr int kBQ = 32 * kQW;   // queries per tile
+constexpr int kQW = 8;          // waves per workgroup (4 for searches too small to fill the chip)
 constexpr int kBC = 64;         // candidates per tile
 constexpr int kBK = VS_QREG_BK; // features per LDS slab (64 or 128)
 constexpr int kCPS = kBK / 8;   // 8-feature chunks per slab
@@ -76,14 +75,15 @@ __device__ __forceinline__ f32x4 ld4(const float *p, int32_t k, int32_t d) {
 // ranking (the score block of the unfused comparator).
 constexpr int kStoreDots = 4;
 
-template <int M, bool VEC, int NSLAB>
-__global__ __launch_bounds__(64 * kQW) __attribute__((amdgpu_waves_per_eu(2)))
+template <int M, bool VEC, int NSLAB, int QW>
+__global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bmu_qreg(const DenseArgs a) {
-    constexpr int NT = 64 * kQW;
+    constexpr int kBQ = 32 * QW;  // queries per tile
+    constexpr int NT = 64 * QW;
     constexpr int NCH = NSLAB * kCPS;
     constexpr int RPP = NT / kPieces;  // loader rows per pass (register path)
     constexpr int AP = kBC / RPP;      // loader pieces per thread (register path)
-    constexpr int RPW = kBC / kQW;     // slab rows owned by each wave (DMA path)
+    constexpr int RPW = kBC / QW;      // slab rows owned by each wave (DMA path)
     constexpr int RPI = 64 / kPieces;  // rows per DMA instruction (1 KiB)
     static_assert(kBC % RPP == 0 && RPW % RPI == 0, "loader shape");
 
@@ -433,48 +433,70 @@ void k_bmu_qreg(const DenseArgs a) {
     }
 }
 
-template <int M, int NSLAB>
+template <int M, int NSLAB, int QW>
 static void dispatch_q(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) {
     if (vec)
-        hipLaunchKernelGGL((k_bmu_qreg<M, true, NSLAB>), grid, dim3(64 * kQW), 0, st, a);
+        hipLaunchKernelGGL((k_bmu_qreg<M, true, NSLAB, QW>), grid, dim3(64 * QW), 0, st, a);
     else
-        hipLaunchKernelGGL((k_bmu_qreg<M, false, NSLAB>), grid, dim3(64 * kQW), 0, st, a);
+        hipLaunchKernelGGL((k_bmu_qreg<M, false, NSLAB, QW>), grid, dim3(64 * QW), 0, st, a);
 }
 
-template <int M>
+template <int M, int QW>
 static void dispatch_slabs(const DenseArgs &a, bool vec, dim3 grid, hipStream_t st) {
     const int nslab = (a.d + kBK - 1) / kBK;
     if constexpr (kMaxSlabs == 4) {
         switch (nslab) {
-        case 1: dispatch_q<M, 1>(a, vec, grid, st); break;
-        case 2: dispatch_q<M, 2>(a, vec, grid, st); break;
-        case 3: dispatch_q<M, 3>(a, vec, grid, st); break;
-        default: dispatch_q<M, 4>(a, vec, grid, st); break;
+        case 1: dispatch_q<M, 1, QW>(a, vec, grid, st); break;
+        case 2: dispatch_q<M, 2, QW>(a, vec, grid, st); break;
+        case 3: dispatch_q<M, 3, QW>(a, vec, grid, st); break;
+        default: dispatch_q<M, 4, QW>(a, vec, grid, st); break;
         }
     } else {
-        if (nslab == 1) dispatch_q<M, 1>(a, vec, grid, st);
-        else dispatch_q<M, 2>(a, vec, grid, st);
+        if (nslab == 1) dispatch_q<M, 1, QW>(a, vec, grid, st);
+        else dispatch_q<M, 2, QW>(a, vec, grid, st);
     }
+}
+
+// Items of (32 QW queries) x 64 candidates; at most 8 waves per CU of work
+// split into contiguous runs, one per workgroup.
+static DenseArgs qreg_split(const DenseArgs &a0, int qw, int n_cu) {
+    DenseArgs a = a0;
+    const int64_t nqt = (a.nq + 32 * qw - 1) / (32 * qw);
+    a.n_ctiles = (a.nc + kBC - 1) / kBC;
+    a.n_items = nqt * a.n_ctiles;
+    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256) * (kQW / qw);
+    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    return a;
 }
 
 bool qreg_supports(int32_t d) { return d >= 1 && d <= 256; }
 
 hipError_t launch_dense_qreg(const DenseArgs &a0, int metric, hipStream_t st, int n_cu) {
-    DenseArgs a = a0;
-    const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
-    a.n_ctiles = (a.nc + kBC - 1) / kBC;
-    a.n_items = nqt * a.n_ctiles;
-    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256);  // one 8-wave workgroup per CU
-    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    // A search with fewer 8-wave items than CUs (e.g. 256 queries x 1,024
+    // candidates: 16 items) runs 4-wave workgroups instead: twice the items,
+    // one wave per SIMD, so each item's MFMA chain takes half as long.  The
+    // per-pair arithmetic is the same, so are the results, bit for bit.
+    DenseArgs a = qreg_split(a0, kQW, n_cu);
+    const bool small = a.n_items < (int64_t)(n_cu > 0 ? n_cu : 256);
+    if (small) a = qreg_split(a0, kQW / 2, n_cu);
     const bool vec = (a.d % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(a.Q) & 15) == 0);
     const dim3 grid((unsigned)a.grid);
     timing_before(st, "k_bmu_qreg");
-    switch (metric) {
-    case L2SQ_MIN: dispatch_slabs<L2SQ_MIN>(a, vec, grid, st); break;
-    case L2SQ_MAX: dispatch_slabs<L2SQ_MAX>(a, vec, grid, st); break;
-    case COS_MAX: dispatch_slabs<COS_MAX>(a, vec, grid, st); break;
-    default: dispatch_slabs<COS_MIN>(a, vec, grid, st); break;
+    if (small) {
+        switch (metric) {
+        case L2SQ_MIN: dispatch_slabs<L2SQ_MIN, kQW / 2>(a, vec, grid, st); break;
+        case L2SQ_MAX: dispatch_slabs<L2SQ_MAX, kQW / 2>(a, vec, grid, st); break;
+        case COS_MAX: dispatch_slabs<COS_MAX, kQW / 2>(a, vec, grid, st); break;
+        default: dispatch_slabs<COS_MIN, kQW / 2>(a, vec, grid, st); break;
+        }
+    } else {
+        switch (metric) {
+        case L2SQ_MIN: dispatch_slabs<L2SQ_MIN, kQW>(a, vec, grid, st); break;
+        case L2SQ_MAX: dispatch_slabs<L2SQ_MAX, kQW>(a, vec, grid, st); break;
+        case COS_MAX: dispatch_slabs<COS_MAX, kQW>(a, vec, grid, st); break;
+        default: dispatch_slabs<COS_MIN, kQW>(a, vec, grid, st); break;
+        }
     }
     const hipError_t err = hipGetLastError();
     timing_after(st);
@@ -485,16 +507,11 @@ hipError_t launch_dense_qreg(const DenseArgs &a0, int metric, hipStream_t st, in
 // (ld_s % 4 == 0, S 16-byte aligned) by the arithmetic of the scan above, so
 // each value equals, bit for bit, the dot product that scan ranks.
 hipError_t launch_dense_qreg_store(const DenseArgs &a0, hipStream_t st, int n_cu) {
-    DenseArgs a = a0;
-    const int64_t nqt = (a.nq + kBQ - 1) / kBQ;
-    a.n_ctiles = (a.nc + kBC - 1) / kBC;
-    a.n_items = nqt * a.n_ctiles;
-    const int64_t cap = (int64_t)(n_cu > 0 ? n_cu : 256);
-    a.grid = (int32_t)(a.n_items < cap ? a.n_items : cap);
+    const DenseArgs a = qreg_split(a0, kQW, n_cu);
     const bool vec = (a.d % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(a.Q) & 15) == 0);
     timing_before(st, "k_bmu_qreg<store>");
-    dispatch_slabs<kStoreDots>(a, vec, dim3((unsigned)a.grid), st);
+    dispatch_slabs<kStoreDots, kQW>(a, vec, dim3((unsigned)a.grid), st);
     const hipError_t err = hipGetLastError();
     timing_after(st);
     return err;

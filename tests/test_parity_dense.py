@@ -248,6 +248,19 @@ def test_kernels_agree_bitwise(monkeypatch):
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
+@pytest.mark.parametrize("d", [64, 200, 256])
+def test_small_and_large_searches_agree_bitwise(d):
+    """A search too small to fill the chip runs 4-wave workgroups, a large
+    one 8-wave workgroups; each pair's arithmetic is the same, so a query's
+    result does not depend on which: the first 256 queries searched alone
+    (16-32 items) equal their rows of the 32,768-query search bit for bit."""
+    Q, C = synth.dense_case(32768, 1024, d, "normal", key=300 + d)
+    big = run_dense(Q, C, 0)
+    small = run_dense(np.ascontiguousarray(Q[:256]), C, 0)
+    assert np.array_equal(big[0][:256], small[0])
+    assert np.array_equal(big[1][:256].view(np.uint32), small[1].view(np.uint32))
+
+
 def test_workload_1_all_queries():
     w = synth.workload(1)
     stats = assert_parity(w["Q"], w["C"], w["metric"])
