@@ -136,3 +136,46 @@ def test_noalloc_at_its_size_limit():
     torch.cuda.synchronize()
     assert torch.equal(idx, ridx)
     assert torch.equal(score.view(torch.int32), rscore.view(torch.int32))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("entry", ["workspace", "noalloc"])
+def test_search_replays_from_a_captured_graph(entry):
+    """The search captured into a HIP graph (three kernels, no memset node):
+    every replay, with eager work and synchronisations between replays and
+    different query contents each time, equals the eager search of the same
+    contents bit for bit."""
+    Qn, Cn = synth.dense_case(600, 3000, 64, "normal", key=21)
+    Q = torch.from_numpy(Qn).to(_dev())
+    C = torch.from_numpy(Cn).to(_dev())
+    idx = torch.empty(600, dtype=torch.int32, device=_dev())
+    score = torch.empty(600, dtype=torch.float32, device=_dev())
+    L = vs.lib()
+    ws = torch.empty(L.vs_bmu_search_workspace(600, 3000, 64, 0), dtype=torch.uint8, device=_dev())
+
+    def call():
+        if entry == "noalloc":
+            _noalloc(Q, C, 0, idx, score)
+        else:
+            vs.vs_bmu_search(Q, C, 0, idx_out=idx, score_out=score, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # first call on the device outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Q.copy_(torch.from_numpy(Qn * np.float32(1 + rep)).to(_dev()))
+        g.replay()
+        torch.cuda.synchronize()
+        got_i, got_s = idx.clone(), score.clone()
+        idx.fill_(-5)
+        call()  # eager, same contents
+        torch.cuda.synchronize()
+        assert torch.equal(got_i, idx), rep
+        assert torch.equal(got_s.view(torch.int32), score.view(torch.int32)), rep
