@@ -209,6 +209,29 @@ def test_empty_query_set():
     assert idx.numel() == 0
 
 
+@pytest.mark.parametrize("env,d,expect", [
+    (None, 64, "k_bmu_qreg"), (None, 300, "k_bmu_q16"), (None, 770, "k_bmu_mfma"),
+    ("qreg", 64, "k_bmu_qreg"), ("q16", 64, "k_bmu_q16"), ("tiled", 64, "k_bmu_mfma"),
+    ("q16", 770, "k_bmu_mfma"),   # q16 does not apply to d % 4 != 0: the next kernel takes it
+])
+def test_kernel_choice_reaches_the_launch(env, d, expect, monkeypatch):
+    """The kernel-choice override (VS_DENSE_KERNEL) and the choice by d reach
+    the launch: the library's timing hook names the kernel that ran, and
+    every choice meets the oracle bar."""
+    if env is None:
+        monkeypatch.delenv("VS_DENSE_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("VS_DENSE_KERNEL", env)
+    Q, C = synth.dense_case(300, 500, d, "normal", key=500 + d)
+    with vs.KernelTimer(8) as kt:
+        idx, score = run_dense(Q, C, 0)
+    assert kt.launches == 1 and kt.name.startswith(expect), (kt.name, kt.launches)
+    o_idx, o_val, o_gap = oracle.dense(Q, C, 0, threads=8)
+    fails, _ = check(idx, score, o_idx, o_val, o_gap, 0, l2_floor(Q, C, o_idx),
+                     lambda r, c: oracle.pair_values(Q, C, 0, r, c))
+    assert not fails, fails
+
+
 def test_binding_refuses_bad_outputs():
     """Caller-supplied outputs and workspaces are checked before any kernel
     runs: too short, wrong dtype, not contiguous, on the host."""

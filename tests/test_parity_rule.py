@@ -165,3 +165,53 @@ def test_floor_bound_rows_are_counted():
     fails, stats = check(idx, score, o_idx, o_val, o_gap, 0, l2_floor(Q, C, o_idx),
                          lambda r, c: oracle.pair_values(Q, C, 0, r, c))
     assert fails == [] and stats["floor_bound"] == 1
+
+
+# ---- the parity tests would catch a kernel with a classic mistake ----------
+# A kernel that makes one of these mistakes returns what the oracle built
+# with the same planted mistake returns; on inputs shaped like the GPU parity
+# cases (a ragged last tile, exact duplicates, masks), the acceptance rule
+# against the correct oracle must reject that answer.
+
+def _mutant_answer_fails(Q, C, metric, mutant, mask=None):
+    o_idx, o_val, o_gap = oracle.dense(Q, C, metric, mask=mask)
+    m_idx, m_val, _ = oracle.dense(Q, C, metric, mask=mask, mutant=mutant)
+    score = np.where(m_idx >= 0, m_val, np.nan).astype(np.float32)
+    floor = l2_floor(Q, C, o_idx) if metric in (0, 1) else 1e-2
+
+    def legal(r, c):
+        ok = (c >= 0) & (c < C.shape[0])
+        if mask is not None:
+            ok[ok] &= ((mask[r[ok], c[ok] // 32] >> (c[ok] % 32).astype(np.uint32)) & 1) == 0
+        return ok
+    fails, _ = check(m_idx, score, o_idx, o_val, o_gap, metric, floor,
+                     lambda r, c: oracle.pair_values(Q, C, metric, r, c), legal)
+    return bool(fails)
+
+
+@pytest.mark.parametrize("mutant,what", [(2, "last candidate dropped"), (3, "MAX ranked as MIN"),
+                                         (4, "last coordinate dropped")])
+def test_rule_rejects_mutant_kernels(mutant, what):
+    # 130 queries x 97 candidates (ragged against 32/64-row tiles), the last
+    # candidate planted as the best match of the first query; d = 33
+    Q, C = synth.dense_case(130, 97, 33, "normal", key=70 + mutant)
+    C[96] = Q[0] * np.float32(1.0001)
+    metric = 1 if mutant == 3 else 0
+    assert _mutant_answer_fails(Q, C, metric, mutant), what
+
+
+def test_rule_rejects_highest_index_ties_through_the_duplicate_check():
+    """Ties broken toward the highest index pass the gap rule (the values are
+    equal) but not the direct lowest-index check of the duplicate tests."""
+    Q, C = synth.dense_case(40, 60, 8, "normal", key=77)
+    C[50] = C[7]
+    Q[3] = C[7] + np.float32(0.01)
+    o_idx, _, _ = oracle.dense(Q, C, 0)
+    m_idx, _, _ = oracle.dense(Q, C, 0, mutant=1)
+    assert o_idx[3] == 7 and m_idx[3] == 50
+
+
+def test_rule_rejects_an_ignored_mask():
+    Q, C = synth.dense_case(50, 90, 12, "normal", key=78)
+    mask = synth.random_mask(50, 90, 0.5, key=79)
+    assert _mutant_answer_fails(Q, C, 0, 5, mask=mask)
