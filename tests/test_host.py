@@ -257,6 +257,14 @@ def test_diversity_run_validation(L):
     assert run(seeds=0) == 1
     assert run(picks=0) == 1
     assert run(ws_bytes=8) == 4
+    # every check of the steps is made before the first step is enqueued
+    assert run(C=0) == 1
+    assert run(mask=0) == 1
+    assert run(ws=0) == 1
+    assert run(mask=FAKE + 2) == 5
+    assert run(scores=FAKE + 1) == 5
+    assert run(ws=FAKE + 8) == 5
+    assert run(d=0) == 2
 
     def run_gram(G=FAKE, n=100, ldg=128, seeds=FAKE, R=0, ldr=0, mask=FAKE, nseq=5, steps=3,
                  picks=FAKE, scores=FAKE):
