@@ -136,16 +136,25 @@ KERNEL_SOURCES = {"k_bmu_qreg": "bmu_qreg.hip", "k_bmu_q16": "bmu_q16.hip",
                   "k_bmu_mfma": "bmu_mfma.hip", "k_bmu_csr": "bmu_csr.hip"}
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks or empty lines."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash(kernel):
-    """Hash of the kernel's source file and the shared header: a recorded
-    traffic figure is reported only while both are unchanged."""
+    """Hash of the code (comments left out) of the kernel's source file and
+    the shared header: a recorded traffic figure is reported only while
+    both are unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "farthest_vector_search_amd", "csrc")
     for name in (KERNEL_SOURCES[kernel], "vs_internal.h"):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -273,11 +273,11 @@ __global__ __launch_bounds__(256) void k_bmu_csr(const CsrArgs a, uint64_t *__re
 // r consumes the LUs of batch r - 1 slot by slot and refills each slot with
 // the matching LU of batch r, so N loads stay in flight across batch and
 // query boundaries instead of draining at each batch.
-//  - At the start of a rotation the batch's (k, v) (brought into LDS by DMA
-//    during the previous rotation) become row-address records; then the
-//    (k, v) of the next batch are staged.  No register load of the stream is
-//    ever waited for by the compiler, and every step issues exactly one
-//    codebook load, so the wait for a slot is vmcnt(N - 1).
+//  - At the start of a rotation the batch's (k, v) (loaded into registers,
+//    one non-zero per lane, at the start of the previous rotation, so N + 1
+//    loads have been issued behind them) become row-address records in LDS;
+//    then the (k, v) of the next batch are loaded.  Every step issues
+//    exactly one codebook load, so the wait for a slot is vmcnt(N - 1).
 //  - A query is finalised after the rotation that consumed its last batch;
 //    the (group, query) result is merged with a 64-bit atomicMin (nothing
 //    returned, nothing waited for).

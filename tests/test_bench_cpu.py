@@ -120,3 +120,14 @@ def test_replicates_off_under_a_profiler(monkeypatch):
     for k in [k for k in os.environ if k.startswith("ROCPROF")]:
         monkeypatch.delenv(k)
     assert not bench.under_profiler()
+
+
+def test_traffic_hash_follows_code_not_comments():
+    """A recorded traffic figure stays valid across comment edits and is
+    dropped when the kernel's code changes."""
+    code = "int f(int x) {\n    return x + 1;  // one more\n}\n"
+    assert bench._code_only(code) == bench._code_only(
+        "/* header\n   text */\nint f(int x) {\n    // note\n    return x + 1;\n}\n\n")
+    assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
+    for k in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_hash(k)) == 16
