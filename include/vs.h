@@ -11,8 +11,8 @@
  *        Measured Against a Symmetrically Tuned Baseline" (summary),
  *        section 3 "Background: the design being tuned": the best-matching
  *        unit of each article is its closest neuron; sparse articles against
- *        a feature-major codebook, the arg-reduction fused into the product
- *        so the score block never reaches memory.
+ *        a feature-major codebook; the arg-reduction runs inside the
+ *        contraction, and no matrix of scores is ever written out.
  *  [DIV] "Issue 9-014: Tile Diversity Shader Inner Loop For L2 Cache
  *        Locality", "Current Behavior" and "Intended Behavior": per sequence,
  *        the unmasked candidate most different from the reference vector,

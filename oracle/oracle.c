@@ -381,8 +381,9 @@ void orc_div_replay(const double *G, int64_t n, int64_t nseq, int T,
 /* ------------------------------------------------------ SOM batch update -- */
 /*
  * One batch update of a self-organizing map around the BMU search.  "From
- * 80x to 385x ...", section 3 (workload): each article's closest neuron is
- * found first, then that neuron and its neighbours on the map are updated.
+ * 80x to 385x ...", section 3 (workload): the search for every article's
+ * BMU comes first; the update of the BMU and of the neurons around it on
+ * the map follows.
  * The pages name no update rule; the readings taken here (all listed in the
  * design notes) are the batch map of the SOM literature:
  *  - the map is rows x cols, planar (no wrap-around); neuron m sits at grid
