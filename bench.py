@@ -133,6 +133,7 @@ def load_traffic(path, kernel, workload):
 
 
 KERNEL_SOURCES = {"k_bmu_qreg": "bmu_qreg.hip", "k_bmu_q16": "bmu_q16.hip",
+                  "k_small_scan": "bmu_small.hip",
                   "k_bmu_mfma": "bmu_mfma.hip", "k_bmu_csr": "bmu_csr.hip"}
 
 
@@ -676,7 +677,7 @@ def _pmc_avg(db, counter, name_prefix):
     return sum(vals) / len(vals), len(vals)
 
 
-DOMINANT = {1: "k_bmu_qreg", 2: "k_bmu_qreg", 3: "k_bmu_q16", 4: "k_bmu_csr", 5: "k_bmu_qreg"}
+DOMINANT = {1: "k_small_scan", 2: "k_bmu_qreg", 3: "k_bmu_q16", 4: "k_bmu_csr", 5: "k_bmu_qreg"}
 
 
 def record_traffic(a):

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libvs.so")
 ROOF_LIB = os.path.join(HERE, "libvs_roofs.so")  # measurement kernels, not the search ABI
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "prep.hip", "bmu_mfma.hip", "bmu_qreg.hip", "bmu_q16.hip", "bmu_csr.hip", "finalize.hip",
+SOURCES = ["api.hip", "prep.hip", "bmu_mfma.hip", "bmu_qreg.hip", "bmu_q16.hip", "bmu_small.hip", "bmu_csr.hip", "finalize.hip",
            "div_gram.hip", "div_ref.hip", "som.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

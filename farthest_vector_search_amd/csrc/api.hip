@@ -78,16 +78,34 @@ Layout search_layout(int64_t nq, int64_t nc, int32_t metric) {
     return L;
 }
 
-// Dense kernel choice: 32 queries per wave in registers for d <= 256, 16 per
-// wave for d <= 768 (d % 4 == 0, 16-byte aligned rows), the LDS-tiled kernel
-// otherwise.  VS_DENSE_KERNEL=qreg|q16|tiled forces one where it applies
-// (all give results within the same bound; qreg and tiled are bit-identical).
-enum class DenseKernel { QREG, Q16, TILED };
-DenseKernel dense_kernel(int32_t d, const float *C, const float *Q) {
+// The dense search's workspace: search_layout, or for a problem the small
+// search may take, at least its partial keys and query norms (from offset 0;
+// the small search uses nothing else).
+Layout dense_layout(int64_t nq, int64_t nc, int32_t d, int32_t metric) {
+    Layout L = search_layout(nq, nc, metric);
+    if (vs::small_shape(nq, nc, d)) {
+        const size_t small = vs::small_workspace(nq, nc);
+        L.total = L.total > small ? L.total : small;
+    }
+    return L;
+}
+
+// Dense kernel choice: the two-launch small search for problems far too
+// small to fill the chip (nq <= 1,024, nc <= 2,048, d <= 256, d % 4 == 0,
+// 16-byte aligned rows); otherwise 32 queries per wave in registers for
+// d <= 256, 16 per wave for d <= 768 (d % 4 == 0, 16-byte aligned rows), the
+// LDS-tiled kernel otherwise.  VS_DENSE_KERNEL=small|qreg|q16|tiled forces
+// one where it applies (all give results within the same bound; small, qreg
+// and tiled are bit-identical).
+enum class DenseKernel { SMALL, QREG, Q16, TILED };
+DenseKernel dense_kernel(int64_t nq, int64_t nc, int32_t d, const float *C, const float *Q) {
     const char *env = std::getenv("VS_DENSE_KERNEL");
+    const bool forced = env && env[0] != '\0';
     const bool q32 = vs::qreg_supports(d), q16 = vs::q16_supports(d, C, Q);
-    if (env && std::strcmp(env, "tiled") == 0) return DenseKernel::TILED;
-    if (env && std::strcmp(env, "q16") == 0 && q16) return DenseKernel::Q16;
+    const bool small = vs::small_supports(nq, nc, d, Q, C);
+    if (small && (!forced || std::strcmp(env, "small") == 0)) return DenseKernel::SMALL;
+    if (forced && std::strcmp(env, "tiled") == 0) return DenseKernel::TILED;
+    if (forced && std::strcmp(env, "q16") == 0 && q16) return DenseKernel::Q16;
     if (q32) return DenseKernel::QREG;
     return q16 ? DenseKernel::Q16 : DenseKernel::TILED;
 }
@@ -176,16 +194,21 @@ VS_API const char *vs_timing_kernel_name(void) { return g_timing.name; }
 // ---- dense search --------------------------------------------------------
 
 VS_API size_t vs_bmu_search_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric) {
-    (void)d;
     if (nq < 0 || nc < 0 || metric < 0 || metric > 3) return 0;
-    return search_layout(nq, nc, metric).total;
+    return dense_layout(nq, nc, d, metric).total;
 }
 
 // The dense search's kernel sequence over a workspace already checked to hold
-// search_layout(nq, nc, metric).total bytes (256-byte aligned).
+// dense_layout(nq, nc, d, metric).total bytes (256-byte aligned).
 static int dense_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
                         int32_t metric, int32_t *idx_out, float *score_out, char *ws,
                         hipStream_t st, int n_cu) {
+    const DenseKernel kernel = dense_kernel(nq, nc, d, C, Q);
+    if (kernel == DenseKernel::SMALL) {
+        VS_TRY_HIP(vs::launch_dense_small(Q, C, nq, nc, d, metric, reinterpret_cast<uint64_t *>(ws),
+                                          idx_out, score_out, st));
+        return VS_OK;
+    }
     const Layout L = search_layout(nq, nc, metric);
     uint64_t *keys = reinterpret_cast<uint64_t *>(ws + L.keys);
     float *qn = vs::metric_is_l2(metric) ? reinterpret_cast<float *>(ws + L.qn) : nullptr;
@@ -203,7 +226,7 @@ static int dense_search(const float *Q, const float *C, int64_t nq, int64_t nc, 
     a.nq = nq;
     a.nc = nc;
     a.d = d;
-    switch (dense_kernel(d, C, Q)) {
+    switch (kernel) {
     case DenseKernel::QREG: VS_TRY_HIP(vs::launch_dense_qreg(a, metric, st, n_cu)); break;
     case DenseKernel::Q16: VS_TRY_HIP(vs::launch_dense_q16(a, metric, vs::kQRows, st, n_cu)); break;
     default: VS_TRY_HIP(vs::launch_dense(a, metric, vs::kQRows, st, n_cu)); break;
@@ -231,7 +254,7 @@ VS_API int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc,
     if (nq == 0) return VS_OK;
     if (!workspace) return VS_ERR_NULL;
     if (!al256(workspace)) return VS_ERR_ALIGN;
-    if (workspace_bytes < search_layout(nq, nc, metric).total) return VS_ERR_WORKSPACE;
+    if (workspace_bytes < dense_layout(nq, nc, d, metric).total) return VS_ERR_WORKSPACE;
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
     return dense_search(Q, C, nq, nc, d, metric, idx_out, score_out,
@@ -283,7 +306,7 @@ VS_API int vs_bmu_search_noalloc(const float *Q, const float *C, int64_t nq, int
                                  void *stream) {
     if (const int s = dense_check(Q, C, nq, nc, d, metric, idx_out, score_out)) return s;
     if (nq == 0) return VS_OK;
-    if (search_layout(nq, nc, metric).total > kNoAllocScratchBytes) return VS_ERR_WORKSPACE;
+    if (dense_layout(nq, nc, d, metric).total > kNoAllocScratchBytes) return VS_ERR_WORKSPACE;
     int n_cu = 0;
     if (const int s = device_ready(&n_cu)) return s;
     char *ws = nullptr;
@@ -891,7 +914,7 @@ VS_API int vs_som_qe(const float *score, int64_t n, double *qe_out, void *stream
 VS_API size_t vs_som_epoch_workspace(int64_t n, int32_t map_rows, int32_t map_cols, int32_t d) {
     const size_t u = vs_som_update_workspace(map_rows, map_cols, d);
     if (!u || n < 0) return 0;
-    return up256(search_layout(n, (int64_t)map_rows * map_cols, vs::L2SQ_MIN).total) + u;
+    return up256(dense_layout(n, (int64_t)map_rows * map_cols, d, vs::L2SQ_MIN).total) + u;
 }
 
 VS_API int vs_som_epoch(const float *X, int64_t n, int32_t d, float *C, int32_t map_rows,
@@ -906,7 +929,7 @@ VS_API int vs_som_epoch(const float *X, int64_t n, int32_t d, float *C, int32_t 
     const size_t need = vs_som_epoch_workspace(n, map_rows, map_cols, d);
     if (workspace_bytes < need) return VS_ERR_WORKSPACE;
     const int64_t nc = (int64_t)map_rows * map_cols;
-    const size_t ws1 = up256(search_layout(n, nc, vs::L2SQ_MIN).total);
+    const size_t ws1 = up256(dense_layout(n, nc, d, vs::L2SQ_MIN).total);
     char *ws = static_cast<char *>(workspace);
     if (const int s = vs_bmu_search(X, C, n, nc, d, vs::L2SQ_MIN, bmu_out, score_out, ws, ws1,
                                     stream))

@@ -192,6 +192,10 @@ void k_bmu_q16(const DenseArgs a) {
             src[u] = a.C + c * d + 4 * piece;
         }
     };
+    // Every slab holds at least one feature below d (the kernel is launched
+    // with NSLAB = ceil(d / kBK)), so each wave issues exactly kDPW loads per
+    // slab, each with at least the lanes of piece 0 active: the slab
+    // pipeline's waits count on that.
     auto load_slab = [&](int slab, int buf) {
         int32_t dl = d;  // opaque, as in load_queries
         asm volatile("" : "+s"(dl));
@@ -212,14 +216,16 @@ void k_bmu_q16(const DenseArgs a) {
         }
     };
     // waves 0 and 1: the mask words (query tile qtile, candidate tile ct) of
-    // the tile's 128 queries; a query past nq gets a zero word
+    // the tile's 128 queries.  Every lane loads (a query past nq reads query
+    // nq - 1's word, which nothing uses: such a query's result is never
+    // published), so each of these waves issues exactly one load.
     auto load_mask = [&](int32_t qtile, int32_t ct, int par) {
         if constexpr (MASKED) {
             if (wave < kBQ / 64) {
-                const int64_t q = (int64_t)qtile * kBQ + wave * 64 + lane;
-                if (q < nq) dma4(reinterpret_cast<const float *>(a.mask + q * a.mask_words + ct),
-                                 reinterpret_cast<float *>(&sM[par][wave * 64]));
-                else sM[par][wave * 64 + lane] = 0u;
+                int64_t q = (int64_t)qtile * kBQ + wave * 64 + lane;
+                q = q < nq ? q : nq - 1;
+                dma4(reinterpret_cast<const float *>(a.mask + q * a.mask_words + ct),
+                     reinterpret_cast<float *>(&sM[par][wave * 64]));
             }
         }
     };
@@ -447,15 +453,20 @@ static void dispatch_slabs(const DenseArgs &a, dim3 grid, hipStream_t st) {
         default: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 6>), grid, dim3(64 * kW), 0, st, a); break;
         }
     } else {
-        // 64-feature slabs: slab counts rounded up to an even number above 4
+        // 64-feature slabs, the exact count: no slab lies wholly past d (the
+        // slab pipeline counts kDPW loads per slab)
         switch (nslab) {
         case 1: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 1>), grid, dim3(64 * kW), 0, st, a); break;
         case 2: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 2>), grid, dim3(64 * kW), 0, st, a); break;
         case 3: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 3>), grid, dim3(64 * kW), 0, st, a); break;
         case 4: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 4>), grid, dim3(64 * kW), 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 6>), grid, dim3(64 * kW), 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 8>), grid, dim3(64 * kW), 0, st, a); break;
-        case 9: case 10: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 10>), grid, dim3(64 * kW), 0, st, a); break;
+        case 5: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 5>), grid, dim3(64 * kW), 0, st, a); break;
+        case 6: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 6>), grid, dim3(64 * kW), 0, st, a); break;
+        case 7: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 7>), grid, dim3(64 * kW), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 8>), grid, dim3(64 * kW), 0, st, a); break;
+        case 9: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 9>), grid, dim3(64 * kW), 0, st, a); break;
+        case 10: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 10>), grid, dim3(64 * kW), 0, st, a); break;
+        case 11: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 11>), grid, dim3(64 * kW), 0, st, a); break;
         default: hipLaunchKernelGGL((k_bmu_q16<M, MODE, 12>), grid, dim3(64 * kW), 0, st, a); break;
         }
     }

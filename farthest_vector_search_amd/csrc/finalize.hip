@@ -9,6 +9,7 @@
 // Shader Inner Loop For L2 Cache Locality", "Current Behavior": the mask
 // grows as picks accumulate).
 #include "vs_internal.h"
+#include "vs_score.h"
 
 namespace vs {
 
@@ -19,25 +20,8 @@ __global__ __launch_bounds__(256) void k_finalize(const uint64_t *__restrict__ k
                                                  float *__restrict__ score_out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nq) return;
-    const uint64_t k = keys[i];
-    if (k == kNoKey) {
-        idx_out[i] = -1;
-        if (score_out) score_out[i] = __builtin_nanf("");
-        return;
-    }
-    idx_out[i] = (int32_t)(uint32_t)(k & 0xffffffffu);
-    if (score_out) {
-        const float e = float_of_ord((uint32_t)(k >> 32));
-        const float key = metric_is_max(M) ? -e : e;
-        float s;
-        if constexpr (metric_is_l2(M)) {
-            s = qn[i] + key;
-            s = s > 0.0f ? s : 0.0f;
-        } else {
-            s = key;
-        }
-        score_out[i] = s;
-    }
+    const float qni = (metric_is_l2(M) && score_out) ? qn[i] : 0.0f;
+    write_result<M>(keys[i], qni, idx_out + i, score_out ? score_out + i : nullptr);
 }
 
 // reset != 0: the key is set back to "no candidate" once read, so the next

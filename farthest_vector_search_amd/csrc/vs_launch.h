@@ -40,6 +40,20 @@ hipError_t launch_dense_qreg(const DenseArgs &a, int metric, hipStream_t st, int
 // 16-queries-per-wave variant (d <= 768, d % 4 == 0, 16-byte aligned rows);
 // also runs the gathered, masked diversity step.
 bool q16_supports(int32_t d, const float *C, const float *Q);
+// Dense search of a small problem in two launches (bmu_small.hip): nq <=
+// kSmallMaxQueries, nc <= kSmallMaxCandidates, d <= 256; small_supports adds
+// d % 4 == 0 and 16-byte aligned rows.  Its workspace (small_workspace bytes
+// at part): small_part_keys packed keys (nq * ceil(nc / 32), rounded up to
+// 32), then nq query norms; every entry is written before it is read.
+constexpr int64_t kSmallMaxQueries = 1024;
+constexpr int64_t kSmallMaxCandidates = 2048;
+int64_t small_part_keys(int64_t nq, int64_t nc);
+size_t small_workspace(int64_t nq, int64_t nc);
+bool small_shape(int64_t nq, int64_t nc, int32_t d);
+bool small_supports(int64_t nq, int64_t nc, int32_t d, const float *Q, const float *C);
+hipError_t launch_dense_small(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
+                              int metric, uint64_t *part, int32_t *idx_out, float *score_out,
+                              hipStream_t st);
 hipError_t launch_dense_q16(const DenseArgs &a, int metric, int qmode, hipStream_t st,
                             int n_cu);
 // every dot product Q[q] . C[c] into a.S (same arithmetic as the scans)

@@ -88,6 +88,13 @@ typedef enum {
  *   score_out  float32[nq] (may be NULL): squared distance of the winner
  *              (|q|^2 + |c|^2 - 2 q.c, clamped at 0) for L2SQ_*, q.c for COS_*.
  * nq == 0 is a no-op.  nc must be in [1, 2^31-1], d in [1, 2^20].
+ * Workspace (vs_bmu_search_workspace): 8 nq bytes of packed keys, plus for
+ * L2SQ_* 4 nq + 4 nc bytes of squared norms, each part rounded up to 256;
+ * a search small enough for the two-launch small path (nq <= 1,024,
+ * nc <= 2,048, d <= 256) needs instead, if that is more, its partial keys
+ * (8 nq ceil(nc / 32) bytes, rounded up to 256) and 4 nq bytes of query
+ * norms (rounded up to 256).  Its contents on entry do not
+ * matter: every call writes what it reads.
  */
 size_t vs_bmu_search_workspace(int64_t nq, int64_t nc, int32_t d, int32_t metric);
 int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_t d,
@@ -104,7 +111,8 @@ int vs_bmu_search(const float *Q, const float *C, int64_t nq, int64_t nc, int32_
  * vs_bmu_search_workspace(nq, nc, d, metric) would report must be at most
  * 8,388,608 bytes (for squared L2 about 12 nq + 4 nc bytes, each part
  * rounded up to 256: e.g. nq = 65,536 with nc up to 1,900,544; for cosine
- * 8 nq bytes), else VS_ERR_WORKSPACE before anything is enqueued.  No
+ * 8 nq bytes; every small-path search fits), else VS_ERR_WORKSPACE before
+ * anything is enqueued.  No
  * hipMalloc, hipFree or other allocating call is made; the first call on a
  * device looks up the array's device address once (hipGetSymbolAddress).
  * Every call on one GPU shares that GPU's array and leaves its contents

@@ -112,8 +112,13 @@ def test_unfused_validation(L):
 
 def test_workspace_sizes(L):
     # keys (8 B per query) always; squared L2 adds query and candidate norms
-    assert L.vs_bmu_search_workspace(1000, 500, 64, 2) == 8192
-    assert L.vs_bmu_search_workspace(1000, 500, 64, 0) == 8192 + 4096 + 2048
+    # keys[nq] u64 | qn[nq] f32 | cn[nc] f32, each 256-byte aligned
+    assert L.vs_bmu_search_workspace(1000, 2100, 64, 2) == 8192
+    assert L.vs_bmu_search_workspace(1000, 2100, 64, 0) == 8192 + 4096 + 8448
+    # a search the small path may take: nq * ceil(nc / 32) keys + nq norms
+    assert L.vs_bmu_search_workspace(1000, 500, 64, 2) == 1000 * 16 * 8 + 4096
+    assert L.vs_bmu_search_workspace(1000, 500, 64, 0) == 1000 * 16 * 8 + 4096
+    assert L.vs_bmu_search_workspace(1000, 500, 300, 0) == 8192 + 4096 + 2048  # d > 256
     assert L.vs_diversity_step_workspace(8359, 768, 3584) == 28672
     assert L.vs_bmu_search_workspace(-1, 5, 4, 0) == 0
 

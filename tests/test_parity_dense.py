@@ -23,12 +23,14 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.fixture(params=["qreg", "q16", "tiled"])
+@pytest.fixture(params=["small", "qreg", "q16", "tiled"])
 def kernel(request, monkeypatch):
-    """Run the test with each dense kernel: 32 queries per wave in registers
-    (d <= 256), 16 per wave (d <= 768, d % 4 == 0, aligned rows), the
-    LDS-tiled kernel (any d); a kernel that does not apply to a case hands it
-    to the next one.  All must satisfy the same bar."""
+    """Run the test with each dense kernel: the two-launch small search
+    (nq <= 1,024, nc <= 2,048, d <= 256, d % 4 == 0, aligned rows), 32
+    queries per wave in registers (d <= 256), 16 per wave (d <= 768,
+    d % 4 == 0, aligned rows), the LDS-tiled kernel (any d); a kernel that
+    does not apply to a case hands it to the next one.  All must satisfy the
+    same bar."""
     monkeypatch.setenv("VS_DENSE_KERNEL", request.param)
     return request.param
 
@@ -209,20 +211,23 @@ def test_empty_query_set():
     assert idx.numel() == 0
 
 
-@pytest.mark.parametrize("env,d,expect", [
-    (None, 64, "k_bmu_qreg"), (None, 300, "k_bmu_q16"), (None, 770, "k_bmu_mfma"),
-    ("qreg", 64, "k_bmu_qreg"), ("q16", 64, "k_bmu_q16"), ("tiled", 64, "k_bmu_mfma"),
-    ("q16", 770, "k_bmu_mfma"),   # q16 does not apply to d % 4 != 0: the next kernel takes it
+@pytest.mark.parametrize("env,nq,d,expect", [
+    (None, 300, 64, "k_small_scan"), (None, 1500, 64, "k_bmu_qreg"),
+    (None, 300, 300, "k_bmu_q16"), (None, 300, 770, "k_bmu_mfma"),
+    ("small", 300, 64, "k_small_scan"), ("qreg", 300, 64, "k_bmu_qreg"),
+    ("q16", 300, 64, "k_bmu_q16"), ("tiled", 300, 64, "k_bmu_mfma"),
+    ("small", 300, 62, "k_bmu_qreg"),  # small needs d % 4 == 0: the next kernel takes it
+    ("q16", 300, 770, "k_bmu_mfma"),   # q16 does not apply to d % 4 != 0: the next kernel takes it
 ])
-def test_kernel_choice_reaches_the_launch(env, d, expect, monkeypatch):
-    """The kernel-choice override (VS_DENSE_KERNEL) and the choice by d reach
-    the launch: the library's timing hook names the kernel that ran, and
-    every choice meets the oracle bar."""
+def test_kernel_choice_reaches_the_launch(env, nq, d, expect, monkeypatch):
+    """The kernel-choice override (VS_DENSE_KERNEL) and the choice by size
+    and d reach the launch: the library's timing hook names the kernel that
+    ran, and every choice meets the oracle bar."""
     if env is None:
         monkeypatch.delenv("VS_DENSE_KERNEL", raising=False)
     else:
         monkeypatch.setenv("VS_DENSE_KERNEL", env)
-    Q, C = synth.dense_case(300, 500, d, "normal", key=500 + d)
+    Q, C = synth.dense_case(nq, 500, d, "normal", key=500 + d)
     with vs.KernelTimer(8) as kt:
         idx, score = run_dense(Q, C, 0)
     assert kt.launches == 1 and kt.name.startswith(expect), (kt.name, kt.launches)
@@ -259,6 +264,51 @@ def test_binding_refuses_bad_outputs():
 
 # ------------------------------------------------------------ workloads --
 
+@pytest.mark.parametrize("metric", [0, 1, 2, 3])
+@pytest.mark.parametrize("nq,nc,d", [(1, 1, 4), (33, 65, 12), (256, 1024, 64),
+                                      (700, 2000, 200), (1024, 2048, 256)])
+def test_small_search_agrees_bitwise(nq, nc, d, metric, monkeypatch):
+    """The two-launch small search runs the same MFMA sequence, norms and
+    ranking as the register-query kernel and the LDS-tiled kernel: all three
+    return the same bits (and meet the oracle bar)."""
+    dist = "unit" if metric in (2, 3) else "normal"
+    Q, C = synth.dense_case(nq, nc, d, dist, key=40 + d + metric)
+    outs = []
+    for k in ("small", "qreg", "tiled"):
+        monkeypatch.setenv("VS_DENSE_KERNEL", k)
+        with vs.KernelTimer(8) as kt:
+            outs.append(run_dense(Q, C, metric))
+        assert kt.name.startswith({"small": "k_small_scan", "qreg": "k_bmu_qreg",
+                                   "tiled": "k_bmu_mfma"}[k]), kt.name
+    for o in outs[1:]:
+        assert np.array_equal(outs[0][0], o[0])
+        assert np.array_equal(outs[0][1].view(np.uint32), o[1].view(np.uint32))
+    o_idx, o_val, o_gap = oracle.dense(Q, C, metric, threads=8)
+    floor = l2_floor(Q, C, o_idx) if metric in (0, 1) else 1e-2
+    fails, _ = check(outs[0][0], outs[0][1], o_idx, o_val, o_gap, metric, floor,
+                     lambda r, c: oracle.pair_values(Q, C, metric, r, c))
+    assert not fails, fails
+
+
+@pytest.mark.parametrize("d", [260, 400, 520, 700])
+def test_q16_rounded_slab_counts(d, monkeypatch):
+    """Widths whose slab count the 16-query kernel rounds up to an even
+    number (5 -> 6, 7 -> 8, 9 -> 10, 11 -> 12 slabs of 64 features), so the
+    last slab lies wholly past d and issues no load: the pipeline's waits
+    count only the loads issued, and every run gives the same bits and meets
+    the oracle bar."""
+    monkeypatch.setenv("VS_DENSE_KERNEL", "q16")
+    Q, C = synth.dense_case(2048, 3000, d, "unit", key=60 + d)
+    runs = [run_dense(Q, C, 2) for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(runs[0][0], r[0])
+        assert np.array_equal(runs[0][1].view(np.uint32), r[1].view(np.uint32))
+    o_idx, o_val, o_gap = oracle.dense(Q, C, 2, threads=16)
+    fails, _ = check(runs[0][0], runs[0][1], o_idx, o_val, o_gap, 2, 1e-2,
+                     lambda r, c: oracle.pair_values(Q, C, 2, r, c))
+    assert not fails, fails
+
+
 def test_kernels_agree_bitwise(monkeypatch):
     """Both dense kernels run the same per-pair arithmetic in the same order,
     so their outputs are identical bit for bit."""
@@ -273,10 +323,11 @@ def test_kernels_agree_bitwise(monkeypatch):
 
 @pytest.mark.parametrize("d", [64, 200, 256])
 def test_small_and_large_searches_agree_bitwise(d):
-    """A search too small to fill the chip runs 4-wave workgroups, a large
-    one 8-wave workgroups; each pair's arithmetic is the same, so a query's
-    result does not depend on which: the first 256 queries searched alone
-    (16-32 items) equal their rows of the 32,768-query search bit for bit."""
+    """A small search (256 queries: the two-launch small search) and a large
+    one (32,768 queries: 8-wave workgroups of the register-query kernel) run
+    the same arithmetic for each pair, so a query's result does not depend
+    on the batch it comes in: the first 256 queries searched alone equal
+    their rows of the 32,768-query search bit for bit."""
     Q, C = synth.dense_case(32768, 1024, d, "normal", key=300 + d)
     big = run_dense(Q, C, 0)
     small = run_dense(np.ascontiguousarray(Q[:256]), C, 0)

@@ -92,7 +92,7 @@ def test_noalloc_matches_workspace_search(metric):
     """Two calls in a row on the shared array, the second smaller, each
     compared bit for bit with vs_bmu_search and with the oracle."""
     dist = "unit" if metric in (2, 3) else "normal"
-    shapes = [(3000, 5000, 64, 11), (300, 700, 33, 12)]
+    shapes = [(3000, 5000, 64, 11), (300, 700, 33, 12), (256, 1024, 64, 13)]
     for nq, nc, d, key in shapes:
         print(f"noalloc metric {metric} nq {nq} nc {nc} d {d}", flush=True)
         Qn, Cn = synth.dense_case(nq, nc, d, dist, key=key)
@@ -140,18 +140,19 @@ def test_noalloc_at_its_size_limit():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("entry", ["workspace", "noalloc"])
-def test_search_replays_from_a_captured_graph(entry):
-    """The search captured into a HIP graph (three kernels, no memset node):
-    every replay, with eager work and synchronisations between replays and
-    different query contents each time, equals the eager search of the same
-    contents bit for bit."""
-    Qn, Cn = synth.dense_case(600, 3000, 64, "normal", key=21)
+@pytest.mark.parametrize("nq,nc", [(600, 3000), (256, 1024)])
+def test_search_replays_from_a_captured_graph(entry, nq, nc):
+    """The search captured into a HIP graph (three kernels, two for a small
+    search; no memset node): every replay, with eager work and
+    synchronisations between replays and different query contents each
+    time, equals the eager search of the same contents bit for bit."""
+    Qn, Cn = synth.dense_case(nq, nc, 64, "normal", key=21)
     Q = torch.from_numpy(Qn).to(_dev())
     C = torch.from_numpy(Cn).to(_dev())
-    idx = torch.empty(600, dtype=torch.int32, device=_dev())
-    score = torch.empty(600, dtype=torch.float32, device=_dev())
+    idx = torch.empty(nq, dtype=torch.int32, device=_dev())
+    score = torch.empty(nq, dtype=torch.float32, device=_dev())
     L = vs.lib()
-    ws = torch.empty(L.vs_bmu_search_workspace(600, 3000, 64, 0), dtype=torch.uint8, device=_dev())
+    ws = torch.empty(L.vs_bmu_search_workspace(nq, nc, 64, 0), dtype=torch.uint8, device=_dev())
 
     def call():
         if entry == "noalloc":
