@@ -266,6 +266,7 @@ def test_binding_refuses_bad_outputs():
 
 @pytest.mark.parametrize("metric", [0, 1, 2, 3])
 @pytest.mark.parametrize("nq,nc,d", [(1, 1, 4), (33, 65, 12), (256, 1024, 64),
+                                      (300, 1000, 128), (500, 1500, 160),
                                       (700, 2000, 200), (1024, 2048, 256)])
 def test_small_search_agrees_bitwise(nq, nc, d, metric, monkeypatch):
     """The two-launch small search runs the same MFMA sequence, norms and
