@@ -939,8 +939,11 @@ def measure_latency(step, torch, a, w):
             vals.append((time.perf_counter() - t0) / K * 1e6)
         return sorted(vals)[len(vals) // 2]
 
-    def empty():
-        if R.vs_roof_empty(1, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+    import farthest_vector_search_amd as vs
+    dev = torch.device("cuda", torch.cuda.current_device())
+
+    def empty():  # the stream handle taken the way the binding takes it
+        if R.vs_roof_empty(1, vs._stream(dev)) != 0:
             raise RuntimeError("vs_roof_empty failed")
 
     res["eager_us_per_call"] = round(per_call_us(step), 2)

@@ -24,6 +24,7 @@ Metrics: VS_L2SQ_MIN, VS_L2SQ_MAX, VS_COS_MAX, VS_COS_MIN.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -171,11 +172,35 @@ def _dev(t, name, dtype, ndim=None):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = None
 
 
 def _stream(device):
-    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+    """The raw handle of torch's current stream on `device` (the call's
+    stream).  torch's own raw-handle accessor where present: the public
+    Stream object costs a few microseconds per call."""
+    global _raw_stream
+    torch = _torch()
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    i = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream:
+        return _raw_stream(i)
+    return torch.cuda.current_stream(i).cuda_stream
+
+
+_same_device = contextlib.nullcontext()
+
+
+def _on(device):
+    """Make `device` current for the call (a no-op when it already is)."""
+    torch = _torch()
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _same_device
+    return torch.cuda.device(device)
 
 
 def _check(rc: int, where: str):
@@ -234,7 +259,7 @@ def vs_bmu_search(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None, worksp
     score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
     need = L.vs_bmu_search_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out), _ptr(score_out),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_bmu_search")
@@ -259,7 +284,7 @@ def vs_bmu_search_noalloc(Q, C, metric=VS_L2SQ_MIN, idx_out=None, score_out=None
     dev = Q.device
     idx_out = _out(idx_out, "idx_out", torch.int32, nq, dev)
     score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search_noalloc(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out),
                                      _ptr(score_out), _stream(dev))
     _check(rc, "vs_bmu_search_noalloc")
@@ -291,7 +316,7 @@ def vs_bmu_search_unfused(Q, C, metric=VS_L2SQ_MIN, S=None, idx_out=None, score_
     score_out = _out(score_out, "score_out", torch.float32, nq, dev, want_score)
     need = L.vs_bmu_search_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search_unfused(_ptr(Q), _ptr(C), nq, nc, d, m, _ptr(idx_out),
                                      _ptr(score_out), _ptr(S), S.stride(0), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(dev))
@@ -324,7 +349,7 @@ def vs_bmu_search_csr(indptr, indices, values, CT, metric=VS_L2SQ_MIN, idx_out=N
     score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search_csr(_ptr(indptr), _ptr(indices) if nnz else None,
                                  _ptr(values) if nnz else None, nq, nnz, _ptr(CT), nc,
                                  CT.stride(0), d, m,
@@ -346,7 +371,7 @@ def vs_csr_block_codebook(CT, out=None):
     d, nc = CT.shape
     n = L.vs_csr_blocked_bytes(nc, d) // 4
     out = _out(out, "out", torch.float32, n, CT.device)
-    with torch.cuda.device(CT.device):
+    with _on(CT.device):
         rc = L.vs_csr_block_codebook(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
                                      _stream(CT.device))
     _check(rc, "vs_csr_block_codebook")
@@ -379,7 +404,7 @@ def vs_bmu_search_csr_blocked(indptr, indices, values, CB, nc, metric=VS_L2SQ_MI
     score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search_csr_blocked(_ptr(indptr), _ptr(indices) if nnz else None,
                                          _ptr(values) if nnz else None, nq, nnz, _ptr(CB), nc,
                                          d, m, _ptr(idx_out), _ptr(score_out), _ptr(ws),
@@ -401,7 +426,7 @@ def vs_csr_block_codebook_f16(CT, out=None):
     d, nc = CT.shape
     n = L.vs_csr_blocked_f16_bytes(nc, d) // 2
     out = _out(out, "out", torch.float16, n, CT.device)
-    with torch.cuda.device(CT.device):
+    with _on(CT.device):
         rc = L.vs_csr_block_codebook_f16(_ptr(CT), nc, CT.stride(0), d, _ptr(out),
                                          _stream(CT.device))
     _check(rc, "vs_csr_block_codebook_f16")
@@ -434,7 +459,7 @@ def vs_bmu_search_csr_blocked_f16(indptr, indices, values, CB16, nc, metric=VS_L
     score_out = _out(score_out, "score_out", torch.float32, max(nq, 0), dev, want_score)
     need = L.vs_bmu_search_csr_workspace(nq, nc, d, m)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_bmu_search_csr_blocked_f16(_ptr(indptr), _ptr(indices) if nnz else None,
                                              _ptr(values) if nnz else None, nq, nnz, _ptr(CB16),
                                              nc, d, m, _ptr(idx_out), _ptr(score_out), _ptr(ws),
@@ -463,7 +488,7 @@ def vs_diversity_step(C, last_pick, mask_bits, idx_out=None, score_out=None, wor
     score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     need = L.vs_diversity_step_workspace(n, d, nseq)
     ws = _workspace(need, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_step(_ptr(C), n, d, _ptr(last_pick), _ptr(mask_bits), nseq,
                                  _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev))
@@ -489,7 +514,7 @@ def vs_diversity_step_ref(C, Q, mask_bits, idx_out=None, score_out=None, workspa
     idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
     score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_step_ref(_ptr(C), n, d, _ptr(Q), _ptr(mask_bits), nseq,
                                      _ptr(idx_out), _ptr(score_out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(dev))
@@ -507,7 +532,7 @@ def vs_diversity_accumulate(C, pick, Q):
     n, d = C.shape
     if Q.shape != (pick.numel(), d):
         raise ValueError("Q must be (len(pick), d)")
-    with torch.cuda.device(C.device):
+    with _on(C.device):
         rc = L.vs_diversity_accumulate(_ptr(C), n, d, _ptr(pick), _ptr(Q), pick.numel(),
                                        _stream(C.device))
     _check(rc, "vs_diversity_accumulate")
@@ -530,7 +555,7 @@ def vs_diversity_gram(C, out=None):
             or out.stride(0) % 4:
         raise ValueError("out must be a float32 n x ldg matrix (ldg >= n, ldg % 4 == 0) "
                          "on the device of C")
-    with torch.cuda.device(C.device):
+    with _on(C.device):
         rc = L.vs_diversity_gram(_ptr(C), n, d, _ptr(out), out.stride(0), _stream(C.device))
     _check(rc, "vs_diversity_gram")
     return out[:, :n]
@@ -557,7 +582,7 @@ def vs_diversity_step_gram(G, last_pick, mask_bits, idx_out=None, score_out=None
     dev = G.device
     idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
     score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_step_gram(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(mask_bits),
                                       nseq, _ptr(idx_out), _ptr(score_out), _stream(dev))
     _check(rc, "vs_diversity_step_gram")
@@ -588,7 +613,7 @@ def vs_diversity_run(C, seeds, mask_bits, steps: int, picks_out=None, scores_out
     picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
     scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_run(_ptr(C), n, d, _ptr(seeds), _ptr(mask_bits), nseq, int(steps),
                                 _ptr(picks_out), _ptr(scores_out), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(dev))
@@ -615,7 +640,7 @@ def vs_diversity_run_ref(C, seeds, mask_bits, steps: int, Q=None, picks_out=None
     picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
     scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
     ws = _workspace(L.vs_diversity_step_workspace(n, d, nseq), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_run_ref(_ptr(C), n, d, _ptr(seeds), _ptr(Q), _ptr(mask_bits), nseq,
                                     int(steps), _ptr(picks_out), _ptr(scores_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(dev))
@@ -645,7 +670,7 @@ def vs_diversity_run_gram(G, seeds, mask_bits, steps: int, R=None, picks_out=Non
     dev = G.device
     picks_out = _out(picks_out, "picks_out", torch.int32, (steps, nseq), dev)
     scores_out = _out(scores_out, "scores_out", torch.float32, (steps, nseq), dev, want_scores)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_run_gram(_ptr(G), n, G.stride(0), _ptr(seeds), _ptr(R),
                                      0 if R is None else R.stride(0), _ptr(mask_bits), nseq,
                                      int(steps), _ptr(picks_out), _ptr(scores_out), _stream(dev))
@@ -690,7 +715,7 @@ def vs_diversity_step_gram_sum(G, last_pick, R, mask_bits, idx_out=None, score_o
     dev = G.device
     idx_out = _out(idx_out, "idx_out", torch.int32, nseq, dev)
     score_out = _out(score_out, "score_out", torch.float32, nseq, dev, want_score)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_diversity_step_gram_sum(_ptr(G), n, G.stride(0), _ptr(last_pick), _ptr(R),
                                           R.stride(0), _ptr(mask_bits), nseq, _ptr(idx_out),
                                           _ptr(score_out), _stream(dev))
@@ -732,7 +757,7 @@ def vs_som_update(X, bmu, C, map_shape, sigma: float, radius: int, workspace=Non
     rows, cols = _map_shape(nc, map_shape)
     dev = C.device
     ws = _workspace(L.vs_som_update_workspace(rows, cols, d), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_update(_ptr(X), n, d, _ptr(bmu), _ptr(C), rows, cols, float(sigma),
                              int(radius), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "vs_som_update")
@@ -756,7 +781,7 @@ def vs_som_update_csr(indptr, indices, values, bmu, CB, map_shape, d: int, sigma
         raise ValueError("CB is smaller than the blocked layout of rows*cols x d")
     dev = CB.device
     ws = _workspace(L.vs_som_update_workspace(rows, cols, d), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_update_csr(_ptr(indptr), _ptr(indices) if nnz else None,
                                  _ptr(values) if nnz else None, n, nnz, _ptr(bmu), _ptr(CB),
                                  rows, cols, d, float(sigma), int(radius), _ptr(ws),
@@ -772,7 +797,7 @@ def vs_som_qe(score, qe_out=None):
     _dev(score, "score", torch.float32, 1)
     dev = score.device
     qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_qe(_ptr(score), score.numel(), _ptr(qe_out), _stream(dev))
     _check(rc, "vs_som_qe")
     return qe_out
@@ -796,7 +821,7 @@ def vs_som_epoch(X, C, map_shape, sigma: float, radius: int, bmu_out=None, score
     score_out = _out(score_out, "score_out", torch.float32, n, dev)
     qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_workspace(n, rows, cols, d), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_epoch(_ptr(X), n, d, _ptr(C), rows, cols, float(sigma), int(radius),
                             _ptr(bmu_out), _ptr(score_out), _ptr(qe_out), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(dev))
@@ -821,7 +846,7 @@ def vs_som_epoch_csr(indptr, indices, values, CB, map_shape, d: int, sigma: floa
     score_out = _out(score_out, "score_out", torch.float32, n, dev)
     qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_epoch_csr(_ptr(indptr), _ptr(indices) if nnz else None,
                                 _ptr(values) if nnz else None, n, nnz, _ptr(CB), rows, cols, d,
                                 float(sigma), int(radius), _ptr(bmu_out), _ptr(score_out),
@@ -839,7 +864,7 @@ def vs_csr_blocked_to_f16(CB, nc: int, d: int, out=None):
     if CB.numel() < ((nc + 63) // 64) * 64 * d:
         raise ValueError("CB is smaller than the blocked layout of nc x d")
     out = _out(out, "out", torch.float16, L.vs_csr_blocked_f16_bytes(nc, d) // 2, CB.device)
-    with torch.cuda.device(CB.device):
+    with _on(CB.device):
         rc = L.vs_csr_blocked_to_f16(_ptr(CB), nc, d, _ptr(out), _stream(CB.device))
     _check(rc, "vs_csr_blocked_to_f16")
     return out
@@ -864,7 +889,7 @@ def vs_som_epoch_csr_f16(indptr, indices, values, CB, map_shape, d: int, sigma: 
     score_out = _out(score_out, "score_out", torch.float32, n, dev)
     qe_out = _out(qe_out, "qe_out", torch.float64, 1, dev)
     ws = _workspace(L.vs_som_epoch_csr_workspace(n, rows, cols, d), dev, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = L.vs_som_epoch_csr_f16(_ptr(indptr), _ptr(indices) if nnz else None,
                                     _ptr(values) if nnz else None, n, nnz, _ptr(CB), _ptr(CB16),
                                     rows, cols, d, float(sigma), int(radius), _ptr(bmu_out),
@@ -884,7 +909,7 @@ def vs_candidate_norms(C, feature_major: bool = False, out=None):
     else:
         nc, d = C.shape
     out = _out(out, "out", torch.float32, nc, C.device)
-    with torch.cuda.device(C.device):
+    with _on(C.device):
         rc = L.vs_candidate_norms(_ptr(C), nc, d, int(bool(feature_major)), _ptr(out),
                                   _stream(C.device))
     _check(rc, "vs_candidate_norms")
