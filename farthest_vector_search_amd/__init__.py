@@ -193,12 +193,16 @@ def _stream(device):
 
 
 _same_device = contextlib.nullcontext()
+_get_device = None
 
 
 def _on(device):
     """Make `device` current for the call (a no-op when it already is)."""
+    global _get_device
     torch = _torch()
-    if device.index is None or device.index == torch.cuda.current_device():
+    if _get_device is None:
+        _get_device = getattr(torch._C, "_cuda_getDevice", torch.cuda.current_device)
+    if device.index is None or device.index == _get_device():
         return _same_device
     return torch.cuda.device(device)
 
@@ -215,7 +219,7 @@ def _out(t, name, dtype, shape, device, want: bool = True):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device) if want else None
     _dev(t, name, dtype)
-    if t.device != torch.device(device):
+    if t.device != (device if isinstance(device, torch.device) else torch.device(device)):
         raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
     n = 1
     for v in (shape if isinstance(shape, tuple) else (shape,)):
@@ -231,7 +235,7 @@ def _workspace(nbytes: int, device, workspace):
         return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
         raise TypeError("workspace must be a CUDA (HIP) torch tensor")
-    if workspace.device != torch.device(device):
+    if workspace.device != (device if isinstance(device, torch.device) else torch.device(device)):
         raise ValueError(f"workspace is on {workspace.device}, the inputs on {device}")
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
