@@ -4,8 +4,12 @@ Shapes, feature counts, metrics and value distributions are drawn from a
 seeded generator, so each case is fixed and reproducible; every result is
 held to the same bar as the hand-picked tests (tests/parity.py): the dense
 and sparse searches against the oracle's exact scan, diversity chains
-against the oracle's step-by-step replay.
+against the oracle's step-by-step replay.  The case counts (24, 12, 8) can
+be raised for a longer sweep with VS_RANDOM_DENSE, VS_RANDOM_CSR and
+VS_RANDOM_DIVERSITY.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -22,7 +26,7 @@ def _draws(key, count):
     return r, count
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(int(os.environ.get("VS_RANDOM_DENSE", "24"))))
 def test_random_dense(case):
     r, _ = _draws(case, 1)
     nq = int(r.integers(1, 300))
@@ -34,7 +38,7 @@ def test_random_dense(case):
     assert_parity(Q, C, metric)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(int(os.environ.get("VS_RANDOM_CSR", "12"))))
 def test_random_csr(case):
     r, _ = _draws(100 + case, 1)
     nq = int(r.integers(1, 120))
@@ -55,7 +59,7 @@ def test_random_csr(case):
     csr_parity(indptr, indices, values, CT, metric)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(int(os.environ.get("VS_RANDOM_DIVERSITY", "8"))))
 def test_random_diversity_chain(case):
     r, _ = _draws(200 + case, 1)
     n = int(r.integers(20, 1500))
